@@ -1,0 +1,13 @@
+"""CPU oracle for jagged exact-softmax attention (test infrastructure only).
+
+Plain, slow, fp64 numpy code that states what the GPU path must compute. Only
+the tests, the smoke check and the benchmark's CPU-baseline leg may import it;
+the product path (the C-ABI library and its Python binding) never does, and
+shares no code with it.
+
+Modules:
+  attention  forward / backward of exact softmax attention per sequence
+  plan       the longest-first work list and the offsets scan, as integers
+"""
+from .attention import forward, backward, valid_pairs  # noqa: F401
+from .plan import build_plan, q_tile_cost, kv_tile_cost, exclusive_scan, COST_KEY_CAP  # noqa: F401

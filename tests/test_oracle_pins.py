@@ -1,0 +1,254 @@
+"""Pins for the fp64 oracle, independent of the oracle's own code.
+
+* a library routine: torch's scaled_dot_product_attention in float64 on padded
+  dense tensors with an additive mask, and torch autograd through it for the
+  gradients (the oracle's backward is hand-derived, so this checks the
+  derivation);
+* closed forms: one key, zero queries (uniform softmax), causal zero queries;
+* invariants: key/value permutation, linearity in V, independence of
+  sequences and heads, gradient sums;
+* central finite differences of sum(dO * O) in fp64;
+* a bias-direction case built so that only i - j = -1 gets a large bias.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from variable_length_attention_jfa_amd import inputs as gen
+
+R = gen.BIAS_RADIUS
+
+
+def _rand_batch(rng, B, H, D, lq_range, lk_range=None, bias=False):
+    lq = rng.integers(lq_range[0], lq_range[1] + 1, size=B)
+    lk = lq.copy() if lk_range is None else rng.integers(lk_range[0], lk_range[1] + 1, size=B)
+    qo, ko = gen.offsets_from_lengths(lq), gen.offsets_from_lengths(lk)
+    q = rng.standard_normal((int(qo[-1]), H, D))
+    k = rng.standard_normal((int(ko[-1]), H, D))
+    v = rng.standard_normal((int(ko[-1]), H, D))
+    do = rng.standard_normal((int(qo[-1]), H, D))
+    bt = rng.standard_normal((H, 2 * R + 1)) * 0.5 if bias else None
+    return qo, ko, q, k, v, do, bt
+
+
+def _sdpa_padded(qo, ko, q, k, v, do, bt, causal):
+    """Padded-dense masked attention through torch (fp64), plus autograd grads."""
+    B = len(qo) - 1
+    H, D = q.shape[1], q.shape[2]
+    lq, lk = np.diff(qo), np.diff(ko)
+    Mq, Mk = max(int(lq.max()), 1), max(int(lk.max()), 1)
+    Qp = torch.zeros(B, H, Mq, D, dtype=torch.float64)
+    Kp = torch.zeros(B, H, Mk, D, dtype=torch.float64)
+    Vp = torch.zeros(B, H, Mk, D, dtype=torch.float64)
+    dOp = torch.zeros(B, H, Mq, D, dtype=torch.float64)
+    mask = torch.full((B, H, Mq, Mk), -math.inf, dtype=torch.float64)
+    for b in range(B):
+        a, e, c, f = int(qo[b]), int(qo[b + 1]), int(ko[b]), int(ko[b + 1])
+        Qp[b, :, :e - a] = torch.from_numpy(q[a:e]).transpose(0, 1)
+        Kp[b, :, :f - c] = torch.from_numpy(k[c:f]).transpose(0, 1)
+        Vp[b, :, :f - c] = torch.from_numpy(v[c:f]).transpose(0, 1)
+        dOp[b, :, :e - a] = torch.from_numpy(do[a:e]).transpose(0, 1)
+        for i in range(Mq):
+            for j in range(Mk):
+                ok = j < f - c and (not causal or j <= i)
+                if i >= e - a:
+                    ok = j == 0  # padded query rows: any finite row, discarded later
+                if ok:
+                    val = 0.0 if bt is None else bt[:, min(max(i - j, -R), R) + R]
+                    mask[b, :, i, j] = torch.as_tensor(val, dtype=torch.float64)
+    Qp.requires_grad_(True)
+    Kp.requires_grad_(True)
+    Vp.requires_grad_(True)
+    O = F.scaled_dot_product_attention(Qp, Kp, Vp, attn_mask=mask)
+    (O * dOp).sum().backward()
+    scores = (Qp.detach() @ Kp.detach().transpose(-1, -2)) / math.sqrt(D) + mask
+    lse = torch.logsumexp(scores, dim=-1)
+    out = np.zeros(q.shape)
+    lse_j = np.zeros(q.shape[:2])
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(B):
+        a, e, c, f = int(qo[b]), int(qo[b + 1]), int(ko[b]), int(ko[b + 1])
+        out[a:e] = O[b, :, :e - a].detach().transpose(0, 1).numpy()
+        lse_j[a:e] = lse[b, :, :e - a].transpose(0, 1).numpy()
+        dq[a:e] = Qp.grad[b, :, :e - a].transpose(0, 1).numpy()
+        dk[c:f] = Kp.grad[b, :, :f - c].transpose(0, 1).numpy()
+        dv[c:f] = Vp.grad[b, :, :f - c].transpose(0, 1).numpy()
+    return out, lse_j, dq, dk, dv
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bias", [False, True])
+@pytest.mark.parametrize("asym", [False, True])
+def test_oracle_matches_padded_dense_sdpa(causal, bias, asym):
+    rng = np.random.default_rng(11 + 2 * causal + 4 * bias + 8 * asym)
+    qo, ko, q, k, v, do, bt = _rand_batch(rng, 4, 2, 8, (1, 13), (1, 17) if asym else None, bias)
+    out, lse = oracle.forward(q, k, v, qo, ko, bt, causal, row_block=5)
+    dq, dk, dv = oracle.backward(q, k, v, do, qo, ko, bt, causal, row_block=5)
+    r_out, r_lse, r_dq, r_dk, r_dv = _sdpa_padded(qo, ko, q, k, v, do, bt, causal)
+    np.testing.assert_allclose(out, r_out, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse, r_lse, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dq, r_dq, atol=1e-11, rtol=0)
+    np.testing.assert_allclose(dk, r_dk, atol=1e-11, rtol=0)
+    np.testing.assert_allclose(dv, r_dv, atol=1e-11, rtol=0)
+
+
+def test_single_key_gives_its_value():
+    rng = np.random.default_rng(3)
+    qo, ko, q, k, v, do, bt = _rand_batch(rng, 3, 2, 16, (1, 9), (1, 1), bias=True)
+    out, lse = oracle.forward(q, k, v, qo, ko, bt, False)
+    dq, dk, dv = oracle.backward(q, k, v, do, qo, ko, bt, False)
+    for b in range(3):
+        for h in range(2):
+            rows = slice(qo[b], qo[b + 1])
+            kv = ko[b]
+            np.testing.assert_allclose(out[rows, h], np.broadcast_to(v[kv, h], out[rows, h].shape), atol=1e-14)
+            i = np.arange(qo[b + 1] - qo[b])
+            s = q[rows, h] @ k[kv, h] / 4.0 + bt[h][np.clip(i, -R, R) + R]
+            np.testing.assert_allclose(lse[rows, h], s, atol=1e-13)
+            np.testing.assert_allclose(dq[rows, h], 0.0, atol=1e-14)
+            np.testing.assert_allclose(dk[kv, h], 0.0, atol=1e-13)
+            np.testing.assert_allclose(dv[kv, h], do[rows, h].sum(axis=0), atol=1e-13)
+
+
+def test_zero_queries_give_mean_of_values():
+    rng = np.random.default_rng(4)
+    qo, ko, q, k, v, do, _ = _rand_batch(rng, 3, 2, 8, (1, 20), (1, 30))
+    q[:] = 0.0
+    out, lse = oracle.forward(q, k, v, qo, ko, None, False)
+    for b in range(3):
+        rows = slice(qo[b], qo[b + 1])
+        for h in range(2):
+            np.testing.assert_allclose(out[rows, h], np.broadcast_to(v[ko[b]:ko[b + 1], h].mean(0), out[rows, h].shape), atol=1e-14)
+            np.testing.assert_allclose(lse[rows, h], math.log(ko[b + 1] - ko[b]), atol=1e-14)
+
+
+def test_causal_zero_queries_give_prefix_means():
+    rng = np.random.default_rng(5)
+    qo, ko, q, k, v, do, _ = _rand_batch(rng, 3, 1, 8, (1, 25))
+    q[:] = 0.0
+    out, lse = oracle.forward(q, k, v, qo, ko, None, True, row_block=7)
+    for b in range(3):
+        L = qo[b + 1] - qo[b]
+        V = v[ko[b]:ko[b + 1], 0]
+        for i in range(L):
+            np.testing.assert_allclose(out[qo[b] + i, 0], V[:i + 1].mean(0), atol=1e-14)
+            assert abs(lse[qo[b] + i, 0] - math.log(i + 1)) < 1e-14
+
+
+def test_empty_sequences():
+    q = np.ones((3, 1, 4))
+    k = np.ones((2, 1, 4))
+    v = np.ones((2, 1, 4))
+    qo = np.array([0, 2, 2, 3])   # b=1 has no queries
+    ko = np.array([0, 0, 1, 2])   # b=0 has no keys
+    out, lse = oracle.forward(q, k, v, qo, ko)
+    assert np.all(out[0:2] == 0) and np.all(np.isneginf(lse[0:2]))
+    np.testing.assert_allclose(out[2, 0], v[1, 0])
+    dq, dk, dv = oracle.backward(q, k, v, np.ones_like(q), qo, ko)
+    assert np.all(dq[0:2] == 0)
+    assert np.all(dk[0] == 0) and np.all(dv[0] == 0)  # keys of b=1 have no queries
+
+
+def test_bias_direction():
+    """Only beta[i - j = -1] is large: each query attends to the next key."""
+    Lq, Lk, D = 3, 5, 4
+    q = np.zeros((Lq, 1, D))
+    k = np.zeros((Lk, 1, D))
+    v = np.arange(Lk * D, dtype=np.float64).reshape(Lk, 1, D)
+    bt = np.zeros((1, 2 * R + 1))
+    bt[0, -1 + R] = 60.0
+    out, _ = oracle.forward(q, k, v, [0, Lq], [0, Lk], bt, False)
+    for i in range(Lq):
+        np.testing.assert_allclose(out[i, 0], v[i + 1, 0], atol=1e-20)
+    # clipping: distances beyond the radius share the end entries
+    bt = np.zeros((1, 2 * R + 1))
+    bt[0, 0] = 50.0  # i - j <= -R
+    out, _ = oracle.forward(np.zeros((1, 1, D)), np.zeros((R + 3, 1, D)),
+                            np.arange((R + 3) * D, dtype=np.float64).reshape(R + 3, 1, D), [0, 1], [0, R + 3], bt)
+    np.testing.assert_allclose(out[0, 0], v_mean := np.arange((R + 3) * D, dtype=np.float64).reshape(R + 3, D)[R:].mean(0), atol=1e-12)
+
+
+def test_permutation_linearity_independence():
+    rng = np.random.default_rng(6)
+    qo, ko, q, k, v, do, _ = _rand_batch(rng, 3, 3, 8, (2, 15), (2, 19))
+    out, lse = oracle.forward(q, k, v, qo, ko)
+    # joint permutation of keys and values inside each sequence
+    perm = np.concatenate([ko[b] + rng.permutation(ko[b + 1] - ko[b]) for b in range(3)])
+    out_p, lse_p = oracle.forward(q, k[perm], v[perm], qo, ko)
+    np.testing.assert_allclose(out_p, out, atol=1e-13)
+    np.testing.assert_allclose(lse_p, lse, atol=1e-13)
+    # linear in V, shift-equivariant
+    v2 = rng.standard_normal(v.shape)
+    out2, _ = oracle.forward(q, k, v2, qo, ko)
+    out12, _ = oracle.forward(q, k, 2.0 * v - 3.0 * v2, qo, ko)
+    np.testing.assert_allclose(out12, 2.0 * out - 3.0 * out2, atol=1e-12)
+    c = rng.standard_normal(8)
+    out_s, _ = oracle.forward(q, k, v + c, qo, ko)
+    np.testing.assert_allclose(out_s, out + c, atol=1e-12)
+    # a sequence alone gives the same rows as inside the batch; heads too
+    b = 1
+    o1, l1 = oracle.forward(q[qo[b]:qo[b + 1], 1:2], k[ko[b]:ko[b + 1], 1:2], v[ko[b]:ko[b + 1], 1:2],
+                            [0, qo[b + 1] - qo[b]], [0, ko[b + 1] - ko[b]])
+    np.testing.assert_array_equal(o1[:, 0], out[qo[b]:qo[b + 1], 1])
+    np.testing.assert_array_equal(l1[:, 0], lse[qo[b]:qo[b + 1], 1])
+
+
+@pytest.mark.parametrize("causal,bias", [(False, False), (True, False), (False, True), (True, True)])
+def test_gradient_sums(causal, bias):
+    rng = np.random.default_rng(7)
+    qo, ko, q, k, v, do, bt = _rand_batch(rng, 3, 2, 8, (1, 21), None if causal else (1, 23), bias)
+    dq, dk, dv = oracle.backward(q, k, v, do, qo, ko, bt, causal, row_block=6)
+    for b in range(3):
+        for h in range(2):
+            ks = slice(ko[b], ko[b + 1])
+            rows = slice(qo[b], qo[b + 1])
+            np.testing.assert_allclose(dk[ks, h].sum(0), 0.0, atol=1e-12)
+            np.testing.assert_allclose(dv[ks, h].sum(0), do[rows, h].sum(0), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,bias", [(False, True), (True, False)])
+def test_finite_differences(causal, bias):
+    rng = np.random.default_rng(8)
+    qo, ko, q, k, v, do, bt = _rand_batch(rng, 2, 2, 4, (2, 6), None if causal else (2, 7), bias)
+    dq, dk, dv = oracle.backward(q, k, v, do, qo, ko, bt, causal)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.forward(q_, k_, v_, qo, ko, bt, causal)
+        return float((o * do).sum())
+
+    eps = 1e-6
+    for name, arr, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = {"q": q, "k": k, "v": v}
+            args_p[name], args_m[name] = plus, minus
+            fd = (loss(args_p["q"], args_p["k"], args_p["v"]) - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * eps)
+            assert abs(fd - g[idx]) <= 1e-7 * max(1.0, abs(g[idx])), (name, idx, fd, g[idx])
+
+
+def test_valid_pairs_brute_force():
+    rng = np.random.default_rng(9)
+    for causal in (False, True):
+        lq = rng.integers(0, 40, size=7)
+        lk = rng.integers(0, 40, size=7)
+        qo, ko = gen.offsets_from_lengths(lq), gen.offsets_from_lengths(lk)
+        brute = sum(1 for b in range(7) for i in range(lq[b]) for j in range(lk[b]) if (not causal or j <= i))
+        assert oracle.valid_pairs(qo, ko, causal) == brute
+
+
+def test_pairs_subset_matches_full():
+    rng = np.random.default_rng(10)
+    qo, ko, q, k, v, do, bt = _rand_batch(rng, 4, 2, 8, (1, 30), None, True)
+    full = oracle.backward(q, k, v, do, qo, ko, bt, True)
+    sub = oracle.backward(q, k, v, do, qo, ko, bt, True, pairs=[(2, 1)])
+    for a, s in zip(full, sub):
+        np.testing.assert_array_equal(a[qo[2]:qo[3], 1] if a.shape[0] == q.shape[0] else a[ko[2]:ko[3], 1],
+                                      s[qo[2]:qo[3], 1] if s.shape[0] == q.shape[0] else s[ko[2]:ko[3], 1])
