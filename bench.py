@@ -1,0 +1,232 @@
+"""Benchmark: jagged attention forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--all] [--no-cpu-baseline]
+
+One step is the whole hot path over one synthetic batch already resident in
+HBM: jfa_fwd (work-list build + forward kernel) then jfa_bwd (two work lists,
+delta, dK/dV pass, dQ pass). Throughput counts valid (query, key) pairs only:
+forward 4*D*H*pairs flops, backward 10*D*H*pairs flops (pairs = sum Lq*Lk, or
+sum_i min(i+1, Lk) with the causal mask).
+
+Prints one JSON line. `value` is fwd+bwd TFLOP/s of the default workload
+(B=64 sequences, lengths uniform in [1, 1024], H=8, D=64, bf16). The
+`roofline` entry is for the kernel with the largest share of the step,
+timed with HIP events around each of its launches on its own stream over the
+timed steps; `cpu_baseline` times the fp64 CPU oracle on a bounded sample of
+the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0
+
+
+def valid_pairs(q_lengths, kv_lengths, causal):
+    total = 0
+    for lq, lk in zip(q_lengths.tolist(), kv_lengths.tolist()):
+        if causal:
+            m = min(lq, lk)
+            total += m * (m + 1) // 2 + (lq - m) * lk
+        else:
+            total += lq * lk
+    return total
+
+
+# Algorithmic flops per valid pair per head, as multiples of D, for each kernel:
+# forward QK^T + PV; dK/dV pass recomputes QK^T and dO V^T and forms dV, dK;
+# dQ pass recomputes QK^T and dO V^T and forms dQ.
+KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "dkdv": 8, "dq": 6}
+
+
+def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None):
+    wl = gen.WORKLOADS[idx]
+    batch = gen.make_batch(wl, seed=seed)
+    dev = torch.device("cuda")
+
+    def t(vals, bits):
+        if bits is not None:
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(vals).to(dev)
+
+    q, k, v = t(batch.q, batch.q_bits), t(batch.k, batch.k_bits), t(batch.v, batch.v_bits)
+    do = t(batch.dout, batch.dout_bits)
+    qo = torch.from_numpy(batch.q_offsets).to(dev)
+    ko = torch.from_numpy(batch.kv_offsets).to(dev)
+    bias = None if batch.bias is None else torch.from_numpy(batch.bias).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((batch.total_q, wl.H), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step():
+        jfa.forward(q, k, v, qo, ko, bias, wl.causal, out=out, lse=lse)
+        jfa.backward(q, k, v, out, lse, do, qo, ko, bias, wl.causal, dq=dq, dk=dk, dv=dv)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    jfa.timing_collect()  # drop anything recorded before
+    jfa.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    jfa.timing_enable(False)
+    kt = jfa.timing_collect()
+
+    pairs = valid_pairs(batch.q_lengths, batch.kv_lengths, wl.causal)
+    fwd_flops = 4.0 * wl.D * wl.H * pairs
+    bwd_flops = 10.0 * wl.D * wl.H * pairs
+    ms_step = (t1 - t0) * 1e3 / steps
+    per = {k_: (ms / max(n, 1), n) for k_, (ms, n) in kt.items()}
+    # the plan kind covers one launch in forward and one in backward per step
+    plan_ms = kt["plan"][0] / max(kt["plan"][1], 1)
+    fwd_ms = kt["forward"][0] / steps + plan_ms
+    bwd_ms = (kt["delta"][0] + kt["dkdv"][0] + kt["dq"][0]) / steps + plan_ms
+    res = {
+        "workload": wl.name, "B": wl.B, "H": wl.H, "D": wl.D, "dtype": wl.dtype, "causal": wl.causal,
+        "bias": wl.bias, "seed": wl.seed if seed is None else seed, "total_q": batch.total_q,
+        "total_kv": batch.total_kv, "valid_pairs_per_head": pairs,
+        "ms_per_step": ms_step,
+        "tflops_step": (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12,
+        "fwd_ms_kernels": fwd_ms, "bwd_ms_kernels": bwd_ms,
+        "fwd_tflops": fwd_flops / (fwd_ms * 1e-3) / 1e12,
+        "bwd_tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12,
+        "kernel_avg_ms": {k_: per[k_][0] for k_ in per if per[k_][1] > 0},
+    }
+    peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
+    res["fwd_pct_peak"] = 100.0 * res["fwd_tflops"] / peak
+    res["bwd_pct_peak"] = 100.0 * res["bwd_tflops"] / peak
+    # dominant kernel
+    share = {k_: kt[k_][0] for k_ in ("forward", "dkdv", "dq")}
+    dom = max(share, key=share.get)
+    avg_ms = kt[dom][0] / kt[dom][1]
+    alg = KERNEL_FLOPS_PER_PAIR_D[dom] * wl.D * wl.H * pairs
+    achieved = alg / (avg_ms * 1e-3) / 1e12
+    res["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                       "frac": achieved / peak, "traffic": None,
+                       "avg_launch_ms": avg_ms, "algorithmic_flops_per_launch": alg}
+    res["_batch"] = batch
+    return res
+
+
+def cpu_baseline(batch, budget_s=15.0):
+    """fp64 oracle (fwd + bwd) on (b, h) pairs in a fixed order until the budget is spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    wl = batch.wl
+    B, H = len(batch.q_lengths), wl.H
+    order = [(b, h) for h in range(H) for b in range(B)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(order)
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    for b, h in order:
+        oracle.backward(batch.q, batch.k, batch.v, batch.dout, batch.q_offsets, batch.kv_offsets, batch.bias,
+                        wl.causal, pairs=[(b, h)])  # runs the forward internally
+        lq, lk = int(batch.q_lengths[b]), int(batch.kv_lengths[b])
+        p = valid_pairs(np.array([lq]), np.array([lk]), wl.causal)
+        flops += 14.0 * wl.D * p  # 4*D forward + 10*D backward per pair
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 numpy oracle forward+backward on {done} of {B * H} (b, h) slices of the same "
+                      f"workload ({flops / 1e9:.1f} valid-pair GFLOP in {el:.1f} s)"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="workload number 1..5 (default 2)")
+    ap.add_argument("--also", type=str, default="3", help="comma list of extra workloads reported alongside")
+    ap.add_argument("--all", action="store_true", help="also report workloads 1..5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(multi-GPU runs are not part of this benchmark)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from variable_length_attention_jfa_amd import inputs as gen
+    from variable_length_attention_jfa_amd import jfa
+    jfa.lib()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+
+    main_res = run_workload(args.workload, args.steps, args.warmup, torch, jfa, gen)
+    print(f"[bench] workload {args.workload}: {main_res['tflops_step']:.1f} TFLOP/s fwd+bwd, "
+          f"fwd {main_res['fwd_tflops']:.1f} bwd {main_res['bwd_tflops']:.1f}", file=sys.stderr, flush=True)
+    extra_ids = list(range(1, 6)) if args.all else [int(x) for x in args.also.split(",") if x.strip()]
+    extras = []
+    for i in extra_ids:
+        if i == args.workload:
+            continue
+        r = run_workload(i, max(3, args.steps // 2), 2, torch, jfa, gen)
+        r.pop("_batch")
+        print(f"[bench] workload {i}: fwd {r['fwd_tflops']:.1f} ({r['fwd_pct_peak']:.1f}%) "
+              f"bwd {r['bwd_tflops']:.1f} ({r['bwd_pct_peak']:.1f}%)", file=sys.stderr, flush=True)
+        extras.append(r)
+        torch.cuda.empty_cache()
+
+    batch = main_res.pop("_batch")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(batch, args.cpu_budget)
+
+    wl = batch.wl
+    line = {
+        "metric": "jagged attn fwd/bwd TFLOPS (valid tokens) bf16 + % MFMA peak, 1 MI355X",
+        "value": main_res["tflops_step"],
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: B={wl.B}, lengths U[{wl.q_len.lo},{wl.q_len.hi}], H={wl.H}, "
+                               f"D={wl.D}, {wl.dtype}, causal={wl.causal}, bias={wl.bias}",
+                   "B": wl.B, "H": wl.H, "D": wl.D, "seed": main_res["seed"], "total_tokens": main_res["total_q"],
+                   "valid_pairs_per_head": main_res["valid_pairs_per_head"]},
+        "pct_mfma_peak": 100.0 * main_res["tflops_step"] / PEAK_BF16_TFLOPS,
+        "fwd_tflops": main_res["fwd_tflops"], "fwd_pct_peak": main_res["fwd_pct_peak"],
+        "bwd_tflops": main_res["bwd_tflops"], "bwd_pct_peak": main_res["bwd_pct_peak"],
+        "kernel_avg_ms": main_res["kernel_avg_ms"],
+        "roofline": main_res["roofline"],
+        "cpu_baseline": cpu,
+        "other_workloads": extras,
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

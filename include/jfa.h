@@ -1,0 +1,151 @@
+/*
+ * jfa.h -- C ABI of libjfa.so: jagged exact-softmax attention on AMD MI355X
+ * (gfx950), forward and backward.
+ *
+ * The operation ("Jagged Flash Attention (JFA)", sysdesign-wiki, section
+ * "Definition"; tiling and online softmax as in "TLX-Optimized Jagged Flash
+ * Attention: Approaching FA4-Level Performance on Blackwell", section "Why
+ * Jagged Flash Attention Deserves Attention"): B variable-length sequences are
+ * packed back to back with no padding and addressed by prefix-sum offsets.
+ * Query and key/value lengths may differ per sequence. For sequence b, head h,
+ * local query row i and key row j:
+ *
+ *   S_ij   = (Q_i . K_j) / sqrt(D) + bias[h][clamp(i - j, -128, 128) + 128]
+ *   causal : key j is visible to query i iff j <= i (top-left alignment)
+ *   O_i    = sum_j softmax_j(S_ij) V_j,   lse_i = ln sum_j exp(S_ij)
+ *   a sequence with no keys gives O_i = 0 and lse_i = -inf.
+ *
+ * Layouts (all row-major, D contiguous, device memory):
+ *   q, out, dout, dq      [total_q,  H, D]   element type T
+ *   k, v, dk, dv          [total_kv, H, D]   element type T
+ *   lse                   [total_q,  H]      fp32, natural log
+ *   q_offsets, kv_offsets [B + 1]            int32, offsets[0] = 0,
+ *                                            non-decreasing, offsets[B] = total
+ *   bias                  [H, 257]           fp32, or NULL for no bias
+ * T is bf16 for jfa_fwd / jfa_bwd and fp32 for jfa_fwd_f32 / jfa_bwd_f32.
+ * Accumulation is fp32 in every variant. D must be 32, 64 or 128.
+ * Each sequence's slice of one tensor (length * H * D * sizeof(T)) must be
+ * below 4 GiB. kv_offsets may alias q_offsets.
+ *
+ * Ownership: the caller owns every buffer. The library allocates no device
+ * memory; scratch space is the caller's `workspace` (size from the
+ * *_workspace_bytes queries, 256-byte aligned). All calls are asynchronous on
+ * `stream` (a hipStream_t, NULL = default stream): no host synchronisation
+ * and no device-to-host reads. Concurrent calls must use distinct
+ * workspaces.
+ *
+ * Errors: every call returns a jfa_status. Invalid arguments are detected on
+ * the host before anything is launched (nothing is written then);
+ * jfa_last_error() gives a thread-local description of the last failure.
+ * Device-side faults surface at the caller's next synchronisation. Offsets
+ * that break the preconditions above are not detected; if they make the work
+ * list larger than the workspace, no output is written and the list header's
+ * status word is set to 1.
+ */
+#ifndef JFA_H
+#define JFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JFA_OK = 0,
+  JFA_ERR_INVALID_ARGUMENT = 1,
+  JFA_ERR_WORKSPACE = 2,
+  JFA_ERR_UNSUPPORTED = 3,
+  JFA_ERR_HIP = 4
+} jfa_status;
+
+#define JFA_BIAS_RADIUS 128 /* bias table is [H][2 * JFA_BIAS_RADIUS + 1] */
+#define JFA_MAX_BATCH 8192  /* largest B accepted by one call */
+
+/* Kernel ids for jfa_tile_config / jfa_build_plan. */
+#define JFA_KERNEL_FWD 0       /* forward: tiles of query rows            */
+#define JFA_KERNEL_BWD_DKDV 1  /* backward dK/dV pass: tiles of keys       */
+#define JFA_KERNEL_BWD_DQ 2    /* backward dQ pass: tiles of query rows    */
+
+/* Element types for jfa_tile_config / jfa_build_plan. */
+#define JFA_DTYPE_BF16 0
+#define JFA_DTYPE_F32 1
+
+/* Bytes of workspace jfa_fwd / jfa_fwd_f32 need. total_q, total_kv are the
+ * row counts of q and k. Returns 0 for invalid sizes. */
+size_t jfa_fwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, int D, int causal);
+
+/* Bytes of workspace jfa_bwd / jfa_bwd_f32 need. */
+size_t jfa_bwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, int D, int causal);
+
+/* Forward pass (bf16 q/k/v/out). Writes out and lse for every valid row;
+ * rows are never written outside their sequence. The softmax scale is
+ * 1/sqrt(D). Jagged edges are handled by zero-filled loads and a subtraction
+ * of the extra exponent terms ("Jagged Flash Attention (JFA)", section "Four
+ * generations", item 1); work is scheduled longest-first over persistent
+ * workgroups (same section, item 3). */
+jfa_status jfa_fwd(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                   const int32_t* kv_offsets, int B, int H, int D, int64_t total_q, int64_t total_kv,
+                   const float* bias, int causal, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Backward pass (bf16). Takes the forward's out and lse and the upstream
+ * gradient dout; writes dq, dk, dv (same layout and type as q, k, v). dK/dV
+ * and dQ are computed in two passes with no atomics ("Jagged Flash Attention
+ * (JFA)", section "Four generations", item 2). No gradient for the bias. */
+jfa_status jfa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                   const void* dout, const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H,
+                   int D, int64_t total_q, int64_t total_kv, const float* bias, int causal, void* dq,
+                   void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* fp32 twins: identical parameters, every tensor of element type fp32. */
+jfa_status jfa_fwd_f32(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                       const int32_t* kv_offsets, int B, int H, int D, int64_t total_q, int64_t total_kv,
+                       const float* bias, int causal, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream);
+jfa_status jfa_bwd_f32(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                       const void* dout, const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H,
+                       int D, int64_t total_q, int64_t total_kv, const float* bias, int causal, void* dq,
+                       void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* offsets[0] = 0, offsets[b+1] = offsets[b] + lengths[b] for b < B (device
+ * int32 arrays, lengths [B], offsets [B+1]); the prefix-sum addressing of
+ * jagged tensors ("Jagged Flash Attention (JFA)", section "Definition"). */
+jfa_status jfa_offsets_from_lengths(const int32_t* lengths, int B, int32_t* offsets, void* stream);
+
+/* Tile shape of a kernel: *tile_m query rows and *tile_n keys. For
+ * JFA_KERNEL_FWD and JFA_KERNEL_BWD_DQ an item is one tile of tile_m query
+ * rows and its cost counts tile_n-key blocks; for JFA_KERNEL_BWD_DKDV an item
+ * is one tile of tile_n keys and its cost counts tile_m-row query blocks. */
+jfa_status jfa_tile_config(int kernel, int D, int dtype, int* tile_m, int* tile_n);
+
+/* Builds the longest-first work list the given kernel runs on, into
+ * `workspace`: a 64-byte header (int32 count, ticket, status, ...) followed
+ * by `count` items of four int32 (b, h, tile, cost). Order: cost descending
+ * (costs of 1023 and more tie), then b, h, tile ascending. Exposed so that the
+ * list can be checked against an independent builder. */
+jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D, int dtype,
+                          int causal, int kernel, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes jfa_build_plan needs for that kernel. */
+size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, int D, int dtype, int kernel);
+
+/* Launch timing, for benchmarks and profiling. While enabled, every kernel
+ * launch of this library is bracketed by two HIP events recorded on its
+ * stream (a few microseconds of host overhead per launch). */
+#define JFA_TIMING_KINDS 6 /* 0 plan, 1 forward, 2 delta, 3 dK/dV, 4 dQ, 5 offsets scan */
+jfa_status jfa_timing_enable(int enable);
+
+/* Waits for every recorded launch, writes the summed kernel milliseconds and
+ * the launch count per kind (arrays of n_kinds entries), and forgets them. */
+jfa_status jfa_timing_collect(double* total_ms, int64_t* launches, int n_kinds);
+
+const char* jfa_status_string(jfa_status status);
+const char* jfa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JFA_H */

@@ -1,0 +1,204 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle.
+
+Sizes here let the oracle finish in seconds while still spanning several
+tiles and a ragged tail; full-size workloads are in test_gpu_full.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import BF16_TOL, compare_backward, compare_forward, raw_forward_error, to_device, tol_for
+from variable_length_attention_jfa_amd import inputs as gen
+from variable_length_attention_jfa_amd import jfa
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(batch, with_bwd=True):
+    d = to_device(batch)
+    out, lse = jfa.forward(d["q"], d["k"], d["v"], d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal)
+    grads = None
+    if with_bwd:
+        grads = jfa.backward(d["q"], d["k"], d["v"], out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], d["bias"],
+                             batch.wl.causal)
+    torch.cuda.synchronize()
+    return out, lse, grads
+
+
+def _check(batch, with_bwd=True, label=""):
+    print(f"[case] {label} B={len(batch.q_lengths)} H={batch.wl.H} D={batch.wl.D} dtype={batch.wl.dtype} "
+          f"causal={batch.wl.causal} bias={batch.wl.bias} Tq={batch.total_q} Tk={batch.total_kv}", flush=True)
+    tol = tol_for(batch)
+    out, lse, grads = _run(batch, with_bwd)
+    e_o, e_l, o_ref, _ = compare_forward(batch, out, lse)
+    raw = raw_forward_error(batch, out, o_ref)
+    print(f"   fwd max|dO| beyond output rounding={e_o:.3e} (raw {raw:.3e}) max|dlse|={e_l:.3e}", flush=True)
+    assert e_o <= tol["out"], f"forward error {e_o}"
+    assert e_l <= tol["lse"], f"lse error {e_l}"
+    if with_bwd:
+        r = compare_backward(batch, *grads)
+        print(f"   bwd relL2 dq={r[0]:.3e} dk={r[1]:.3e} dv={r[2]:.3e}", flush=True)
+        assert max(r) <= tol["grad"], f"gradient errors {r}"
+
+
+# Reduced copies of the five workloads: same H, D, dtype, mask and bias.
+SMALL = {
+    1: gen.WORKLOADS[1],
+    2: gen.small_workload(gen.WORKLOADS[2], B=6, lo=1, hi=700, seed=21),
+    3: gen.small_workload(gen.WORKLOADS[3], B=5, lo=1, hi=600, seed=31),
+    4: gen.small_workload(gen.WORKLOADS[4], B=5, lo=1, hi=64, kv=(64, 900), seed=41),
+    5: gen.small_workload(gen.WORKLOADS[5], B=3, lo=16, hi=1100, seed=51),
+}
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_small_workload_parity(cfg):
+    _check(gen.make_batch(SMALL[cfg]), label=f"small cfg{cfg}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("causal,bias,asym", [(False, False, False), (True, False, False), (False, True, True),
+                                              (True, True, True)])
+def test_feature_grid(dtype, D, causal, bias, asym):
+    base = gen.Workload("grid", 4, 2, D, dtype, causal, bias, gen.LengthDist("uniform", 1, 300),
+                        gen.LengthDist("uniform", 1, 330) if asym else None, seed=100 + D)
+    _check(gen.make_batch(base), label=f"grid {dtype} D={D} causal={causal} bias={bias} asym={asym}")
+
+
+@pytest.mark.parametrize("lengths", [
+    ([0, 5, 0, 7], None),                     # empty query sequences
+    ([3, 4, 2], [0, 6, 0]),                   # no keys for some sequences
+    ([1, 1, 1], None),                        # single tokens
+    ([63, 64, 65, 127, 128, 129], None),      # tile edges (64-key blocks, 128-row tiles)
+    ([2048], None),                           # one long sequence
+    ([200, 70], [5, 300]),                    # Lq > Lk and Lq < Lk
+])
+@pytest.mark.parametrize("causal,bias", [(False, False), (True, False), (False, True), (True, True)])
+def test_edge_lengths(lengths, causal, bias):
+    ql, kl = lengths
+    wl = gen.Workload("edge", len(ql), 2, 64, "bf16", causal, bias, gen.LengthDist("fixed", 1, 1), seed=5)
+    _check(gen.make_batch(wl, q_lengths=ql, kv_lengths=kl), label=f"edge {ql} {kl} causal={causal} bias={bias}")
+
+
+def test_single_head_d128_long_causal():
+    wl = gen.Workload("h1", 2, 1, 128, "bf16", True, False, gen.LengthDist("fixed", 1, 1), seed=9)
+    _check(gen.make_batch(wl, q_lengths=[1500, 3000]), label="H=1 long causal")
+
+
+def test_many_short_sequences():
+    wl = gen.Workload("many", 4096, 1, 64, "bf16", False, False, gen.LengthDist("uniform", 1, 8), seed=10)
+    _check(gen.make_batch(wl), label="B=4096 short")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_deterministic_bitwise(cfg):
+    batch = gen.make_batch(SMALL[cfg])
+    a = _run(batch)
+    b = _run(batch)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])
+    for x, y in zip(a[2], b[2]):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_outputs_outside_sequences_untouched():
+    """Canary rows after T in every output must keep their sentinel values."""
+    batch = gen.make_batch(SMALL[3])
+    d = to_device(batch)
+    Tq, Tk, H, D = batch.total_q, batch.total_kv, batch.wl.H, batch.wl.D
+    pad = 200
+    out_buf = torch.full((Tq + pad, H, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse_buf = torch.full((Tq + pad, H), 7.0, dtype=torch.float32, device="cuda")
+    dq_buf = torch.full((Tq + pad, H, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    dk_buf = torch.full((Tk + pad, H, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    dv_buf = torch.full((Tk + pad, H, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    out, lse = jfa.forward(d["q"], d["k"], d["v"], d["q_offsets"], d["kv_offsets"], None, True,
+                           out=out_buf[:Tq], lse=lse_buf[:Tq])
+    jfa.backward(d["q"], d["k"], d["v"], out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], None, True,
+                 dq=dq_buf[:Tq], dk=dk_buf[:Tk], dv=dv_buf[:Tk])
+    torch.cuda.synchronize()
+    for t in (out_buf, lse_buf, dq_buf, dk_buf, dv_buf):
+        assert torch.all(t[-pad:] == 7.0)
+    e_o, e_l, _, _ = compare_forward(batch, out, lse)
+    assert e_o <= BF16_TOL["out"] and e_l <= BF16_TOL["lse"]
+
+
+@pytest.mark.parametrize("kernel", [jfa.KERNEL_FWD, jfa.KERNEL_BWD_DKDV, jfa.KERNEL_BWD_DQ])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_plan_bit_exact(kernel, causal, cfg):
+    wl = gen.WORKLOADS[cfg]
+    rng = np.random.default_rng(wl.seed)
+    ql = wl.q_len.sample(rng, wl.B)
+    kl = wl.kv_len.sample(rng, wl.B) if wl.kv_len is not None else ql
+    qo, ko = gen.offsets_from_lengths(ql), gen.offsets_from_lengths(kl)
+    tm, tn = jfa.tile_config(kernel, wl.D)
+    ref = oracle.build_plan(qo, ko, wl.H, tm, tn, causal, kv_pass=(kernel == jfa.KERNEL_BWD_DKDV))
+    hdr, items = jfa.build_plan(torch.from_numpy(qo).cuda(), torch.from_numpy(ko).cuda(), wl.H, wl.D, causal, kernel,
+                                int(qo[-1]), int(ko[-1]))
+    torch.cuda.synchronize()
+    h = hdr.cpu().numpy()
+    assert h[0] == len(ref) and h[1] == 0 and h[2] == 0
+    np.testing.assert_array_equal(items[:len(ref)].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_plan_bit_exact_random(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 3000))
+    ql = rng.integers(0, 3000, size=B) * (rng.random(B) < 0.9)
+    kl = rng.integers(0, 5000, size=B) * (rng.random(B) < 0.9)
+    qo, ko = gen.offsets_from_lengths(ql), gen.offsets_from_lengths(kl)
+    H = int(rng.integers(1, 9))
+    for kernel in (jfa.KERNEL_FWD, jfa.KERNEL_BWD_DKDV, jfa.KERNEL_BWD_DQ):
+        for causal in (False, True):
+            tm, tn = jfa.tile_config(kernel, 128)
+            ref = oracle.build_plan(qo, ko, H, tm, tn, causal, kv_pass=(kernel == jfa.KERNEL_BWD_DKDV))
+            hdr, items = jfa.build_plan(torch.from_numpy(qo).cuda(), torch.from_numpy(ko).cuda(), H, 128, causal,
+                                        kernel, int(qo[-1]), int(ko[-1]))
+            assert int(hdr[0].item()) == len(ref)
+            np.testing.assert_array_equal(items[:len(ref)].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("B", [0, 1, 5, 1023, 1024, 1025, 8192])
+def test_offsets_bit_exact(B):
+    rng = np.random.default_rng(B)
+    lens = rng.integers(0, 5000, size=B).astype(np.int32)
+    got = jfa.offsets_from_lengths(torch.from_numpy(lens).cuda())
+    np.testing.assert_array_equal(got.cpu().numpy(), oracle.exclusive_scan(lens))
+
+
+def test_invalid_arguments_raise():
+    batch = gen.make_batch(SMALL[2])
+    d = to_device(batch)
+    L = jfa.lib()
+    # D not supported
+    st = L.jfa_fwd(jfa._ptr(d["q"]), jfa._ptr(d["k"]), jfa._ptr(d["v"]), jfa._ptr(d["q_offsets"]),
+                   jfa._ptr(d["kv_offsets"]), 6, 8, 48, batch.total_q, batch.total_kv, None, 0, jfa._ptr(d["q"]),
+                   jfa._ptr(d["q"]), None, 0, None)
+    assert st == 1
+    # workspace too small
+    ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["q"])
+    lse = torch.empty(batch.total_q, 8, dtype=torch.float32, device="cuda")
+    st = L.jfa_fwd(jfa._ptr(d["q"]), jfa._ptr(d["k"]), jfa._ptr(d["v"]), jfa._ptr(d["q_offsets"]),
+                   jfa._ptr(d["kv_offsets"]), 6, 8, 64, batch.total_q, batch.total_kv, None, 0, jfa._ptr(out),
+                   jfa._ptr(lse), jfa._ptr(ws), 1024, None)
+    assert st == 2
+    assert b"workspace" in L.jfa_last_error()
+    # misaligned q
+    st = L.jfa_fwd(ctypes_offset(d["q"], 2), jfa._ptr(d["k"]), jfa._ptr(d["v"]), jfa._ptr(d["q_offsets"]),
+                   jfa._ptr(d["kv_offsets"]), 6, 8, 64, batch.total_q, batch.total_kv, None, 0, jfa._ptr(out),
+                   jfa._ptr(lse), jfa._ptr(ws), 1024, None)
+    assert st == 1
+    # B = 0 is a no-op
+    st = L.jfa_fwd(None, None, None, jfa._ptr(d["q_offsets"]), jfa._ptr(d["kv_offsets"]), 0, 8, 64, 0, 0, None, 0,
+                   None, None, jfa._ptr(ws), 1024, None)
+    assert st == 0
+
+
+def ctypes_offset(t, nbytes):
+    import ctypes
+    return ctypes.c_void_p(t.data_ptr() + nbytes)

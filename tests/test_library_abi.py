@@ -1,0 +1,59 @@
+"""The C-ABI library loads and exports every function include/jfa.h declares;
+host-only entry points behave without a GPU (no compute calls here)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from variable_length_attention_jfa_amd import jfa
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(jfa.LIB_PATH):
+        pytest.skip("libjfa.so not built (run __graft_entry__.build())")
+    return jfa.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = jfa.declared_functions()
+    assert len(names) >= 12
+    nm = subprocess.run(["nm", "-D", "--defined-only", jfa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_binding_covers_the_header():
+    assert set(jfa.declared_functions()) == set(jfa._SIGS)
+
+
+def test_host_only_queries(L):
+    assert L.jfa_fwd_workspace_bytes(4, 2, 153, 153, 32, 0) > 0
+    assert L.jfa_fwd_workspace_bytes(4, 2, 153, 153, 48, 0) == 0
+    assert L.jfa_bwd_workspace_bytes(-1, 2, 10, 10, 64, 0) == 0
+    assert L.jfa_bwd_workspace_bytes(64, 8, 31132, 31132, 64, 0) > 31132 * 8 * 4
+    tm, tn = jfa.tile_config(jfa.KERNEL_FWD, 128)
+    assert (tm, tn) == (128, 64)
+    assert jfa.tile_config(jfa.KERNEL_BWD_DKDV, 64) == (64, 128)
+    assert jfa.tile_config(jfa.KERNEL_BWD_DQ, 32, jfa.DTYPE_F32) == (128, 64)
+    with pytest.raises(jfa.JFAError):
+        jfa.tile_config(7, 128)
+    assert L.jfa_status_string(2) == b"workspace missing, misaligned or too small"
+
+
+def test_invalid_arguments_rejected_on_host(L):
+    # bad sizes are rejected before any device call
+    st = L.jfa_fwd(None, None, None, None, None, -1, 1, 64, 0, 0, None, 0, None, None, None, 0, None)
+    assert st == 1
+    assert b"invalid sizes" in L.jfa_last_error()
+    st = L.jfa_bwd(None, None, None, None, None, None, None, None, 4, 0, 64, 0, 0, None, 0, None, None, None, None, 0,
+                   None)
+    assert st == 1
+    st = L.jfa_fwd(None, None, None, None, None, 2, 2, 64, 0, 0, None, 0, None, None, None, 0, None)
+    assert st == 1 and b"offsets" in L.jfa_last_error()
+    dummy = ctypes.c_void_p(4096)
+    st = L.jfa_fwd(dummy, dummy, dummy, dummy, dummy, 2, 2, 64, 10, 10, None, 0, dummy, dummy, None, 0, None)
+    assert st == 2

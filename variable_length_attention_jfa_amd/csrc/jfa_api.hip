@@ -1,0 +1,442 @@
+// C-ABI layer of libjfa.so: argument validation, workspace layout, launches.
+// Declarations and the contract are in include/jfa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <atomic>
+#include <mutex>
+#include <vector>
+#include <string>
+
+#include "../../include/jfa.h"
+#include "jfa_common.h"
+#include "jfa_kernels.h"
+
+namespace {
+
+using jfa::PlanHeader;
+
+thread_local std::string g_last_error;
+
+jfa_status fail(jfa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+jfa_status ok() {
+  g_last_error.clear();
+  return JFA_OK;
+}
+
+struct DeviceInfo {
+  int num_cus = 0;
+  bool gfx950 = false;
+  hipError_t err = hipSuccess;
+};
+
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
+
+jfa_status device_info(DeviceInfo** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(JFA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(JFA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::call_once(g_dev_once[dev], [dev]() {
+    hipDeviceProp_t p;
+    g_dev[dev].err = hipGetDeviceProperties(&p, dev);
+    if (g_dev[dev].err == hipSuccess) {
+      g_dev[dev].num_cus = p.multiProcessorCount;
+      g_dev[dev].gfx950 = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    }
+  });
+  DeviceInfo* d = &g_dev[dev];
+  if (d->err != hipSuccess) return fail(JFA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(d->err));
+  if (!d->gfx950) return fail(JFA_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X)", dev);
+  *out = d;
+  return JFA_OK;
+}
+
+// Optional per-launch timing: HIP events recorded on the launch stream around
+// each kernel, read back on jfa_timing_collect().
+enum { kKindPlan = 0, kKindFwd = 1, kKindDelta = 2, kKindDkdv = 3, kKindDq = 4, kKindScan = 5 };
+struct TimingRec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+std::atomic<bool> g_timing{false};
+std::vector<TimingRec> g_recs;
+
+std::vector<hipEvent_t> g_event_pool;  // reused events (creation is the costly part)
+
+hipError_t take_event(hipEvent_t* ev) {
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (!g_event_pool.empty()) {
+      *ev = g_event_pool.back();
+      g_event_pool.pop_back();
+      return hipSuccess;
+    }
+  }
+  return hipEventCreate(ev);
+}
+
+template <typename F>
+hipError_t timed(int kind, hipStream_t st, F&& launch) {
+  if (!g_timing.load(std::memory_order_relaxed)) return launch();
+  hipEvent_t a = nullptr, b = nullptr;
+  hipError_t e = take_event(&a);
+  if (e == hipSuccess) e = take_event(&b);
+  if (e == hipSuccess) e = hipEventRecord(a, st);
+  if (e != hipSuccess) return e;
+  e = launch();
+  hipError_t e2 = hipEventRecord(b, st);
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_recs.push_back({kind, a, b});
+  }
+  return e != hipSuccess ? e : e2;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool valid_sizes(int B, int H, int64_t tq, int64_t tk, int D) {
+  return B >= 0 && B <= JFA_MAX_BATCH && H >= 1 && tq >= 0 && tk >= 0 && tq < (1LL << 31) && tk < (1LL << 31) &&
+         (D == 32 || D == 64 || D == 128);
+}
+
+// Upper bound on the work items of one pass: sum_b ceil(L_b / tile) <= ceil(T / tile) + B.
+int64_t max_items(int B, int H, int64_t total, int tile) { return (int64_t)H * (cdiv64(total, tile) + B); }
+
+struct FwdLayout {
+  size_t hdr = 0, items = 0, total = 0;
+  int64_t cap = 0;
+};
+FwdLayout fwd_layout(int B, int H, int64_t tq) {
+  FwdLayout L;
+  L.cap = max_items(B, H, tq, jfa::kFwdTM);
+  L.hdr = 0;
+  L.items = kAlign;
+  L.total = L.items + align_up((size_t)L.cap * 16);
+  return L;
+}
+
+struct BwdLayout {
+  size_t hdr_kv = 0, hdr_q = 64, delta = 0, items_kv = 0, items_q = 0, total = 0;
+  int64_t cap_kv = 0, cap_q = 0;
+};
+BwdLayout bwd_layout(int B, int H, int64_t tq, int64_t tk) {
+  BwdLayout L;
+  L.cap_kv = max_items(B, H, tk, jfa::kDkvTN);
+  L.cap_q = max_items(B, H, tq, jfa::kDqTM);
+  L.delta = kAlign;
+  L.items_kv = L.delta + align_up((size_t)tq * H * 4);
+  L.items_q = L.items_kv + align_up((size_t)L.cap_kv * 16);
+  L.total = L.items_q + align_up((size_t)L.cap_q * 16);
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+jfa_status check_common(const void* q, const void* k, const void* v, const int32_t* qo, const int32_t* ko, int B,
+                        int H, int D, int64_t tq, int64_t tk, const float* bias, const void* ws) {
+  if (!valid_sizes(B, H, tq, tk, D))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "invalid sizes: B=%d (0..%d), H=%d (>=1), D=%d (32/64/128), total_q=%lld, total_kv=%lld",
+                B, JFA_MAX_BATCH, H, D, (long long)tq, (long long)tk);
+  if (!qo || !ko) return fail(JFA_ERR_INVALID_ARGUMENT, "offsets must not be NULL");
+  if ((tq > 0 && !q) || (tk > 0 && (!k || !v)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "q/k/v must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "q/k/v must be 16-byte aligned");
+  if (!aligned(qo, 4) || !aligned(ko, 4) || !aligned(bias, 4))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "offsets/bias must be 4-byte aligned");
+  if (!ws || !aligned(ws, kAlign)) return fail(JFA_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  return JFA_OK;
+}
+
+jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const int32_t* qo, const int32_t* ko,
+                    int B, int H, int D, int64_t tq, int64_t tk, const float* bias, int causal, void* out,
+                    float* lse, void* ws, size_t ws_bytes, void* stream) {
+  jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, bias, ws);
+  if (s != JFA_OK) return s;
+  if ((tq > 0 && (!out || !lse))) return fail(JFA_ERR_INVALID_ARGUMENT, "out/lse must not be NULL");
+  if (!aligned(out, 16) || !aligned(lse, 4)) return fail(JFA_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
+  const FwdLayout L = fwd_layout(B, H, tq);
+  if (ws_bytes < L.total)
+    return fail(JFA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  DeviceInfo* dev = nullptr;
+  if ((s = device_info(&dev)) != JFA_OK) return s;
+  if (B == 0 || tq == 0) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+
+  jfa::PlanArgs pa{};
+  pa.q_off = qo;
+  pa.kv_off = ko;
+  pa.B = B;
+  pa.H = H;
+  pa.causal = causal ? 1 : 0;
+  pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::kFwdTM, jfa::kFwdTN, 0};
+  hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 1, st); });
+  if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+
+  jfa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_off = qo;
+  a.kv_off = ko;
+  a.bias = bias;
+  a.out = out;
+  a.lse = lse;
+  a.items = (const int4*)(w + L.items);
+  a.hdr = (PlanHeader*)(w + L.hdr);
+  a.H = H;
+  a.causal = causal ? 1 : 0;
+  a.scale2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
+  e = timed(kKindFwd, st, [&] { return jfa::launch_fwd(f32, D, a, bias != nullptr, (long)L.cap, dev->num_cus, st); });
+  if (e != hipSuccess) return fail(JFA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const void* out, const float* lse,
+                    const void* dout, const int32_t* qo, const int32_t* ko, int B, int H, int D, int64_t tq,
+                    int64_t tk, const float* bias, int causal, void* dq, void* dk, void* dv, void* ws,
+                    size_t ws_bytes, void* stream) {
+  jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, bias, ws);
+  if (s != JFA_OK) return s;
+  if (tq > 0 && (!out || !lse || !dout || !dq)) return fail(JFA_ERR_INVALID_ARGUMENT, "out/lse/dout/dq must not be NULL");
+  if (tk > 0 && (!dk || !dv)) return fail(JFA_ERR_INVALID_ARGUMENT, "dk/dv must not be NULL");
+  if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "out/dout/dq/dk/dv must be 16-byte aligned");
+  const BwdLayout L = bwd_layout(B, H, tq, tk);
+  if (ws_bytes < L.total)
+    return fail(JFA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  DeviceInfo* dev = nullptr;
+  if ((s = device_info(&dev)) != JFA_OK) return s;
+  if (B == 0 || (tq == 0 && tk == 0)) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+
+  jfa::PlanArgs pa{};
+  pa.q_off = qo;
+  pa.kv_off = ko;
+  pa.B = B;
+  pa.H = H;
+  pa.causal = causal ? 1 : 0;
+  pa.pass[0] = {(int4*)(w + L.items_kv), (PlanHeader*)(w + L.hdr_kv), (long)L.cap_kv, jfa::kDkvTM, jfa::kDkvTN, 1};
+  pa.pass[1] = {(int4*)(w + L.items_q), (PlanHeader*)(w + L.hdr_q), (long)L.cap_q, jfa::kDqTM, jfa::kDqTN, 0};
+  hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 2, st); });
+  if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+
+  jfa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.dout = dout;
+  a.q_off = qo;
+  a.kv_off = ko;
+  a.bias = bias;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = (float*)(w + L.delta);
+  a.H = H;
+  a.causal = causal ? 1 : 0;
+  a.scale = (float)(1.0 / std::sqrt((double)D));
+  a.scale2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
+  a.rows = (long)tq * H;
+  jfa::BwdArgs a_kv = a, a_q = a;
+  a_kv.items = (const int4*)(w + L.items_kv);
+  a_kv.hdr = (PlanHeader*)(w + L.hdr_kv);
+  a_q.items = (const int4*)(w + L.items_q);
+  a_q.hdr = (PlanHeader*)(w + L.hdr_q);
+  const bool has_bias = bias != nullptr;
+  e = timed(kKindDelta, st, [&] { return jfa::launch_delta(f32, D, a_kv, st); });
+  if (e == hipSuccess)
+    e = timed(kKindDkdv, st, [&] { return jfa::launch_dkdv(f32, D, a_kv, has_bias, (long)L.cap_kv, dev->num_cus, st); });
+  if (e == hipSuccess)
+    e = timed(kKindDq, st, [&] { return jfa::launch_dq(f32, D, a_q, has_bias, (long)L.cap_q, dev->num_cus, st); });
+  if (e != hipSuccess) return fail(JFA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+bool tile_of(int kernel, int* tm, int* tn) {
+  switch (kernel) {
+    case JFA_KERNEL_FWD: *tm = jfa::kFwdTM; *tn = jfa::kFwdTN; return true;
+    case JFA_KERNEL_BWD_DKDV: *tm = jfa::kDkvTM; *tn = jfa::kDkvTN; return true;
+    case JFA_KERNEL_BWD_DQ: *tm = jfa::kDqTM; *tn = jfa::kDqTN; return true;
+    default: return false;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t jfa_fwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, int D, int causal) {
+  (void)causal;
+  if (!valid_sizes(B, H, total_q, total_kv, D)) return 0;
+  return fwd_layout(B, H, total_q).total;
+}
+
+size_t jfa_bwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, int D, int causal) {
+  (void)causal;
+  if (!valid_sizes(B, H, total_q, total_kv, D)) return 0;
+  return bwd_layout(B, H, total_q, total_kv).total;
+}
+
+jfa_status jfa_fwd(const void* q, const void* k, const void* v, const int32_t* q_offsets, const int32_t* kv_offsets,
+                   int B, int H, int D, int64_t total_q, int64_t total_kv, const float* bias, int causal, void* out,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(false, q, k, v, q_offsets, kv_offsets, B, H, D, total_q, total_kv, bias, causal, out, lse,
+                  workspace, workspace_bytes, stream);
+}
+
+jfa_status jfa_fwd_f32(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                       const int32_t* kv_offsets, int B, int H, int D, int64_t total_q, int64_t total_kv,
+                       const float* bias, int causal, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return fwd_impl(true, q, k, v, q_offsets, kv_offsets, B, H, D, total_q, total_kv, bias, causal, out, lse,
+                  workspace, workspace_bytes, stream);
+}
+
+jfa_status jfa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+                   const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D, int64_t total_q,
+                   int64_t total_kv, const float* bias, int causal, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return bwd_impl(false, q, k, v, out, lse, dout, q_offsets, kv_offsets, B, H, D, total_q, total_kv, bias, causal,
+                  dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+jfa_status jfa_bwd_f32(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                       const void* dout, const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D,
+                       int64_t total_q, int64_t total_kv, const float* bias, int causal, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(true, q, k, v, out, lse, dout, q_offsets, kv_offsets, B, H, D, total_q, total_kv, bias, causal, dq,
+                  dk, dv, workspace, workspace_bytes, stream);
+}
+
+jfa_status jfa_offsets_from_lengths(const int32_t* lengths, int B, int32_t* offsets, void* stream) {
+  if (B < 0) return fail(JFA_ERR_INVALID_ARGUMENT, "B must be >= 0");
+  if (!offsets || (B > 0 && !lengths)) return fail(JFA_ERR_INVALID_ARGUMENT, "lengths/offsets must not be NULL");
+  DeviceInfo* dev = nullptr;
+  jfa_status s = device_info(&dev);
+  if (s != JFA_OK) return s;
+  hipError_t e = timed(kKindScan, (hipStream_t)stream, [&] { return jfa::launch_scan(lengths, B, offsets, (hipStream_t)stream); });
+  if (e != hipSuccess) return fail(JFA_ERR_HIP, "scan launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+jfa_status jfa_tile_config(int kernel, int D, int dtype, int* tile_m, int* tile_n) {
+  if (!tile_m || !tile_n) return fail(JFA_ERR_INVALID_ARGUMENT, "tile_m/tile_n must not be NULL");
+  if (!(D == 32 || D == 64 || D == 128)) return fail(JFA_ERR_INVALID_ARGUMENT, "D must be 32, 64 or 128");
+  if (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_F32) return fail(JFA_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (!tile_of(kernel, tile_m, tile_n)) return fail(JFA_ERR_INVALID_ARGUMENT, "unknown kernel id %d", kernel);
+  return ok();
+}
+
+size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, int D, int dtype, int kernel) {
+  int tm, tn;
+  if (!valid_sizes(B, H, total_q, total_kv, D) || !tile_of(kernel, &tm, &tn) ||
+      (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_F32))
+    return 0;
+  const int64_t cap = kernel == JFA_KERNEL_BWD_DKDV ? max_items(B, H, total_kv, tn) : max_items(B, H, total_q, tm);
+  return kAlign + align_up((size_t)cap * 16);
+}
+
+jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D, int dtype,
+                          int causal, int kernel, void* workspace, size_t workspace_bytes, void* stream) {
+  int tm, tn;
+  if (!tile_of(kernel, &tm, &tn)) return fail(JFA_ERR_INVALID_ARGUMENT, "unknown kernel id %d", kernel);
+  if (B < 0 || B > JFA_MAX_BATCH || H < 1 || !(D == 32 || D == 64 || D == 128) ||
+      (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_F32))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "invalid sizes");
+  if (!q_offsets || !kv_offsets) return fail(JFA_ERR_INVALID_ARGUMENT, "offsets must not be NULL");
+  if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < kAlign)
+    return fail(JFA_ERR_WORKSPACE, "workspace must be non-NULL, 256-byte aligned and at least 256 bytes");
+  DeviceInfo* dev = nullptr;
+  jfa_status s = device_info(&dev);
+  if (s != JFA_OK) return s;
+  char* w = (char*)workspace;
+  jfa::PlanArgs pa{};
+  pa.q_off = q_offsets;
+  pa.kv_off = kv_offsets;
+  pa.B = B;
+  pa.H = H;
+  pa.causal = causal ? 1 : 0;
+  pa.pass[0] = {(int4*)(w + kAlign), (PlanHeader*)w, (long)((workspace_bytes - kAlign) / 16), tm, tn,
+                kernel == JFA_KERNEL_BWD_DKDV ? 1 : 0};
+  hipError_t e = jfa::launch_plan(pa, 1, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+jfa_status jfa_timing_enable(int enable) {
+  g_timing.store(enable != 0);
+  return ok();
+}
+
+jfa_status jfa_timing_collect(double* total_ms, int64_t* launches, int n_kinds) {
+  if (n_kinds < 0 || (n_kinds > 0 && (!total_ms || !launches)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "total_ms/launches must hold n_kinds entries");
+  for (int i = 0; i < n_kinds; ++i) {
+    total_ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  std::vector<TimingRec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    recs.swap(g_recs);
+  }
+  hipError_t first = hipSuccess;
+  for (const TimingRec& r : recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e == hipSuccess && r.kind < n_kinds) {
+      total_ms[r.kind] += ms;
+      launches[r.kind] += 1;
+    }
+    if (e != hipSuccess && first == hipSuccess) first = e;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    for (const TimingRec& r : recs) {
+      g_event_pool.push_back(r.a);
+      g_event_pool.push_back(r.b);
+    }
+  }
+  if (first != hipSuccess) return fail(JFA_ERR_HIP, "timing events: %s", hipGetErrorString(first));
+  return ok();
+}
+
+const char* jfa_status_string(jfa_status status) {
+  switch (status) {
+    case JFA_OK: return "ok";
+    case JFA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case JFA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case JFA_ERR_UNSUPPORTED: return "unsupported device or configuration";
+    case JFA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* jfa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

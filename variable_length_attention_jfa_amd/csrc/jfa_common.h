@@ -1,0 +1,211 @@
+// Shared device helpers for the gfx950 jagged-attention kernels.
+//
+// Data layout (all tensors packed, no padding between sequences):
+//   q, k, v, out, dout, dq, dk, dv : [T, H, D] row-major, D contiguous
+//   lse, delta                     : [T, H] fp32
+//   offsets                        : int32 [B+1], prefix sums of lengths
+// A sequence b of head h is a strided view: row r lives at
+//   base + ((offsets[b] + r) * H + h) * D.
+//
+// Jagged edges ("Jagged Flash Attention (JFA)", section "Four generations",
+// item 1): rows past a sequence's end are read as zeros and never written.
+// On gfx950 this is done by a buffer resource whose record count ends at the
+// sequence's last row: out-of-range loads return 0 and out-of-range stores are
+// dropped by the hardware range check.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jfa {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) char lds_t;
+
+constexpr int kBiasRadius = 128;
+constexpr int kBiasLen = 2 * kBiasRadius + 1;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInit = -1.0e30f;  // running-max start value (finite: keeps exp2(m_old - m_new) at 0)
+
+// ---------------------------------------------------------------------------
+// Buffer views with hardware range checks.
+struct View {
+  __amdgpu_buffer_rsrc_t r;
+};
+
+__device__ __forceinline__ View make_view(const void* base, uint32_t bytes) {
+  View v;
+  v.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  return v;
+}
+
+// Rows [0, rows) of one (sequence, head) slice: row stride `row_stride` bytes,
+// `row_bytes` valid bytes per row.
+__device__ __forceinline__ View seq_view(const void* base, int rows, uint32_t row_stride, uint32_t row_bytes) {
+  uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * row_stride + row_bytes : 0u;
+  return make_view(base, bytes);
+}
+
+__device__ __forceinline__ i32x4 ld16(const View& v, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(v.r, off, 0, 0);
+}
+__device__ __forceinline__ float ld4f(const View& v, uint32_t off) {
+  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(v.r, off, 0, 0));
+}
+__device__ __forceinline__ void st16(const View& v, uint32_t off, i32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(x, v.r, off, 0, 0);
+}
+__device__ __forceinline__ void st8(const View& v, uint32_t off, i32x2 x) {
+  __builtin_amdgcn_raw_buffer_store_b64(x, v.r, off, 0, 0);
+}
+__device__ __forceinline__ void st4f(const View& v, uint32_t off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(x), v.r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA fragments. A fragment is the 8 k-values one lane feeds into a 16-deep
+// slice of a 32x32 product: lane l (half g = l / 32) owns k-slots 8g .. 8g+7.
+// bf16 uses one v_mfma_f32_32x32x16_bf16; fp32 issues eight
+// v_mfma_f32_32x32x2_f32 (k-slot 8g+e goes in step e), same contraction.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+__device__ __forceinline__ void mma(f32x16& c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& c, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[e], b.lo[e], c, 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[e], b.hi[e], c, 0, 0, 0);
+}
+
+// Fragment from 8 consecutive elements in global memory (natural layout).
+__device__ __forceinline__ Frag<bf16> gfrag(const View& v, uint32_t off, bf16*) {
+  i32x4 x = ld16(v, off);
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, x);
+  return f;
+}
+__device__ __forceinline__ Frag<float> gfrag(const View& v, uint32_t off, float*) {
+  Frag<float> f;
+  f.lo = __builtin_bit_cast(f32x4, ld16(v, off));
+  f.hi = __builtin_bit_cast(f32x4, ld16(v, off + 16));
+  return f;
+}
+
+// Fragment from 8 consecutive elements of an LDS row (natural layout).
+__device__ __forceinline__ Frag<bf16> lfrag(const lds_t* p, bf16*) {
+  Frag<bf16> f;
+  f.v = *(const __attribute__((address_space(3))) bf16x8*)p;
+  return f;
+}
+__device__ __forceinline__ Frag<float> lfrag(const lds_t* p, float*) {
+  Frag<float> f;
+  f.lo = *(const __attribute__((address_space(3))) f32x4*)p;
+  f.hi = *(const __attribute__((address_space(3))) f32x4*)(p + 16);
+  return f;
+}
+
+// Transposed fragment: k runs down the rows of a row-major LDS tile, the lane's
+// column is fixed. The k-slot order matches the row order of a 32x32 MFMA
+// result held by the other operand: slot e of half g is row
+//   rowbase + 4g + e        (e < 4)
+//   rowbase + 8 + 4g + e-4  (e >= 4).
+// bf16: two ds_read_b64_tr_b16. Each 16-lane group gives four row addresses
+// (one per lane quad) and the hardware hands lane i the i-th column of those
+// four rows. Column = colbase + (l & 31).
+template <int STRIDE>
+__device__ __forceinline__ Frag<bf16> tfrag(const lds_t* tile, int rowbase, int colbase, int lane, bf16*) {
+  const int g = lane >> 5;
+  const int row = rowbase + 4 * g + ((lane & 15) >> 2);
+  const int col = colbase + ((lane & 31) >> 4) * 16 + (lane & 3) * 4;
+  const lds_t* p = tile + row * STRIDE + col * 2;
+  s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 8 * STRIDE));
+  Frag<bf16> f;
+  bf16x4 a4 = __builtin_bit_cast(bf16x4, a), b4 = __builtin_bit_cast(bf16x4, b);
+  f.v = (bf16x8){a4[0], a4[1], a4[2], a4[3], b4[0], b4[1], b4[2], b4[3]};
+  return f;
+}
+template <int STRIDE>
+__device__ __forceinline__ Frag<float> tfrag(const lds_t* tile, int rowbase, int colbase, int lane, float*) {
+  const int g = lane >> 5;
+  const lds_t* p = tile + (rowbase + 4 * g) * STRIDE + (colbase + (lane & 31)) * 4;
+  Frag<float> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f.lo[e] = *(const __attribute__((address_space(3))) float*)(p + e * STRIDE);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f.hi[e] = *(const __attribute__((address_space(3))) float*)(p + (8 + e) * STRIDE);
+  return f;
+}
+
+// Fragment from half (c = 0 or 1) of a 32x32 fp32 result: elements 8c .. 8c+7,
+// i.e. rows 16c + {4g..4g+3, 8+4g..8+4g+3} of that result.
+__device__ __forceinline__ Frag<bf16> rfrag(const f32x16& s, int c, bf16*) {
+  Frag<bf16> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)s[8 * c + e];
+  return f;
+}
+__device__ __forceinline__ Frag<float> rfrag(const f32x16& s, int c, float*) {
+  Frag<float> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.lo[e] = s[8 * c + e]; f.hi[e] = s[8 * c + 4 + e]; }
+  return f;
+}
+
+// Value held by the lane 32 positions away (other half of the wave).
+__device__ __forceinline__ float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return (threadIdx.x & 32) ? __int_as_float(r[0]) : __int_as_float(r[1]);
+}
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
+// Row (within a 32x32 MFMA result) of element i held by a lane of half g.
+__device__ __forceinline__ constexpr int res_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+
+// Store 4 consecutive fp32 values as T (8 or 16 bytes) at byte offset off.
+__device__ __forceinline__ void store4(const View& v, uint32_t off, float a, float b, float c, float d, bf16*) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  bf16x2 lo = {(bf16)a, (bf16)b}, hi = {(bf16)c, (bf16)d};
+  i32x2 x = {__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+  st8(v, off, x);
+}
+__device__ __forceinline__ void store4(const View& v, uint32_t off, float a, float b, float c, float d, float*) {
+  i32x4 x = {__float_as_int(a), __float_as_int(b), __float_as_int(c), __float_as_int(d)};
+  st16(v, off, x);
+}
+
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Work-list header in the caller's workspace.
+struct PlanHeader {
+  int count;    // items in the list
+  int ticket;   // next item to hand out (zeroed by the plan kernel)
+  int status;   // 0 ok, 1 list did not fit the workspace
+  int pad[13];
+};
+static_assert(sizeof(PlanHeader) == 64, "header is 64 bytes");
+
+// Fetch the next work-list index for this workgroup (thread 0 takes a ticket).
+__device__ __forceinline__ int next_item(int* ticket, int* sh) {
+  if (threadIdx.x == 0) *sh = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int it = *sh;
+  __syncthreads();  // every wave has read *sh before thread 0 may overwrite it
+  return it;
+}
+
+}  // namespace jfa

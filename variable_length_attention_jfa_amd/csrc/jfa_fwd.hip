@@ -1,0 +1,244 @@
+// Forward pass of jagged exact-softmax attention on gfx950.
+//
+// One persistent workgroup (4 waves) takes work items (b, h, query tile of 128
+// rows) from the longest-first list and walks the key/value blocks of that
+// sequence ("Jagged Flash Attention (JFA)", sections "Why standard
+// FlashAttention falls short" and "Four generations" item 3). Each wave owns
+// 32 query rows. Per 64-key block:
+//   S^T = K Q^T          bf16 MFMA 32x32x16, K from LDS (natural), Q in VGPRs
+//   online softmax       one lane per query: 16 scores per half-wave lane,
+//                        the two halves combined with one permlane32 swap
+//   O^T += V^T P^T       V read transposed from LDS (ds_read_b64_tr_b16),
+//                        P straight from the score registers
+// Tiling + running max / running sum: "TLX-Optimized Jagged Flash Attention:
+// Approaching FA4-Level Performance on Blackwell", section "Why Jagged Flash
+// Attention Deserves Attention".
+//
+// Jagged edges ("Jagged Flash Attention (JFA)", "Four generations" item 1):
+// keys past the sequence end load as zeros, so their score is the bias value
+// (0 without bias) and their value row is 0. They add nothing to O and add
+// exp(score - m) each to the running sum, which is subtracted once in the
+// epilogue (the block holding them is the last one visited, so m is final
+// when they are counted). Query rows past the end load as zeros and their
+// stores are dropped. Only blocks that straddle the causal diagonal use an
+// element mask (which then also drops keys past the end).
+#include "jfa_common.h"
+#include "jfa_kernels.h"
+
+namespace jfa {
+
+template <typename T, int D>
+struct FwdTiles {
+  static constexpr int BM = 128;  // query rows per item (4 waves x 32)
+  static constexpr int BN = 64;   // keys per block
+  static constexpr int THREADS = 256;
+  static constexpr int ROWB = D * (int)sizeof(T);
+  static constexpr int KS = ROWB + 16;  // K tile row stride: 16-byte natural reads, conflict-free
+  static constexpr int VS = ROWB + 32;  // V tile row stride: transposed reads, conflict-free
+  static constexpr int KTILE = BN * KS;
+  static constexpr int VTILE = BN * VS;
+  static constexpr int STAGE = KTILE + VTILE;
+  static constexpr int CPR = ROWB / 16;              // 16-byte pieces per row
+  static constexpr int CPT = BN * CPR / THREADS;     // pieces per thread per tile
+  static constexpr int BIAS_OFF = 2 * STAGE;
+  static constexpr int LDS = BIAS_OFF + 1040;
+  static_assert((BN * CPR) % THREADS == 0, "tile pieces divide the workgroup");
+  static_assert(BM == kFwdTM && BN == kFwdTN, "tile shape published to the planner");
+};
+
+
+
+template <typename T, int D, bool BIAS>
+__global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_kernel(FwdArgs a) {
+  using C = FwdTiles<T, D>;
+  constexpr int BM = C::BM, BN = C::BN, ES = (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ int sh_item;
+  lds_t* lds = (lds_t*)smem;
+  __attribute__((address_space(3))) float* bias_lds = (__attribute__((address_space(3))) float*)(lds + C::BIAS_OFF);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int H = a.H;
+  const uint32_t gstride = (uint32_t)H * C::ROWB;  // bytes between consecutive tokens
+  const int n_items = a.hdr->count;
+
+  for (;;) {
+    const int it = next_item(&a.hdr->ticket, &sh_item);
+    if (it >= n_items) break;
+    const int4 item = a.items[it];
+    const int b = item.x, h = item.y, qt = item.z;
+    const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
+    const int k0 = a.kv_off[b], Lk = a.kv_off[b + 1] - k0;
+    const int row0 = qt * BM;
+    const int n_kv = a.causal ? cdiv(min(min(row0 + BM, Lq), Lk), BN) : cdiv(Lk, BN);
+
+    const size_t qrow = ((size_t)q0 * H + h) * C::ROWB, krow = ((size_t)k0 * H + h) * C::ROWB;
+    const View qv = seq_view((const char*)a.q + qrow, Lq, gstride, C::ROWB);
+    const View kv = seq_view((const char*)a.k + krow, Lk, gstride, C::ROWB);
+    const View vv = seq_view((const char*)a.v + krow, Lk, gstride, C::ROWB);
+
+    if (BIAS) {
+      for (int i = tid; i < kBiasLen; i += C::THREADS) bias_lds[i] = a.bias[h * kBiasLen + i] * kLog2e;
+    }
+
+    const int wr0 = row0 + 32 * w;  // first query row of this wave
+    const bool wave_on = wr0 < Lq;
+    const int qi = wr0 + l32;       // this lane's query row
+    Frag<T> qf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = gfrag(qv, (uint32_t)qi * gstride + (16 * kk + 8 * g) * ES, (T*)0);
+
+    i32x4 kr[C::CPT], vr[C::CPT];
+    auto gload = [&](int j) {
+#pragma unroll
+      for (int c = 0; c < C::CPT; ++c) {
+        const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
+        const uint32_t off = (uint32_t)(j * BN + row) * gstride + col * 16;
+        kr[c] = ld16(kv, off);
+        vr[c] = ld16(vv, off);
+      }
+    };
+    auto swrite = [&](int s) {
+#pragma unroll
+      for (int c = 0; c < C::CPT; ++c) {
+        const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
+        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + row * C::KS + col * 16) = kr[c];
+        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + C::KTILE + row * C::VS + col * 16) = vr[c];
+      }
+    };
+    if (n_kv > 0) {
+      gload(0);
+      swrite(0);
+    }
+    __syncthreads();
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
+    float m = kNegInit, l = 0.f;
+    int last_tile = -1;
+    bool last_masked = false;
+
+    for (int j = 0; j < n_kv; ++j) {
+      const int s = j & 1;
+      if (j + 1 < n_kv) gload(j + 1);
+      const int key0 = j * BN;
+      const bool active = wave_on && (!a.causal || key0 <= wr0 + 31);
+      if (active) {
+        const bool masked = a.causal && (key0 + BN - 1 > wr0);
+        last_tile = j;
+        last_masked = masked;
+        const lds_t* kt = lds + s * C::STAGE;
+        const lds_t* vt = kt + C::KTILE;
+        f32x16 sc[BN / 32];
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+          sc[kb] = (f32x16){};
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk)
+            mma(sc[kb], lfrag(kt + (32 * kb + l32) * C::KS + (16 * kk + 8 * g) * ES, (T*)0), qf[kk]);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kj = key0 + 32 * kb + res_row(i, g);
+            float x = sc[kb][i] * a.scale2;
+            if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+            if (masked && (kj > qi || kj >= Lk)) x = -INFINITY;
+            sc[kb][i] = x;
+            mx = fmaxf(mx, x);
+          }
+        }
+        mx = half_max(mx);
+        const float mn = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(sc[kb][i] - mn);
+            sc[kb][i] = p;
+            l += p;
+          }
+        }
+#pragma unroll
+        for (int kc = 0; kc < BN / 16; ++kc) {
+          const Frag<T> pf = rfrag(sc[kc >> 1], kc & 1, (T*)0);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) mma(o[db], tfrag<C::VS>(vt, 16 * kc, 32 * db, lane, (T*)0), pf);
+        }
+      }
+      if (j + 1 < n_kv) swrite((j + 1) & 1);
+      __syncthreads();
+    }
+
+    // Epilogue: combine the two half-wave partial sums, remove the pad terms.
+    float lt = l + other_half(l);
+    if (wave_on && last_tile >= 0 && !last_masked) {
+      const int pad1 = (last_tile + 1) * BN;
+      if (pad1 > Lk) {
+        if (!BIAS) {
+          lt -= (float)(pad1 - Lk) * __builtin_amdgcn_exp2f(-m);
+        } else {
+          float sub = 0.f;
+          for (int kj = Lk + g; kj < pad1; kj += 2)
+            sub += __builtin_amdgcn_exp2f(bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius] - m);
+          lt -= sub + other_half(sub);
+        }
+      }
+    }
+    if (wave_on) {
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      const View ov = seq_view((char*)a.out + qrow, Lq, gstride, C::ROWB);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = 32 * db + 8 * r + 4 * g;
+          store4(ov, (uint32_t)qi * gstride + d * ES, o[db][4 * r] * inv, o[db][4 * r + 1] * inv,
+                 o[db][4 * r + 2] * inv, o[db][4 * r + 3] * inv, (T*)0);
+        }
+      }
+      if (g == 0) {
+        const float lse = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+        const View lv = seq_view(a.lse + (size_t)q0 * H + h, Lq, (uint32_t)H * 4, 4);
+        st4f(lv, (uint32_t)qi * H * 4, lse);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_t(const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
+  auto kern = bias ? jfa_fwd_kernel<T, D, true> : jfa_fwd_kernel<T, D, false>;
+  static int occ_b = 0, occ_n = 0;
+  int& occ = bias ? occ_b : occ_n;
+  if (occ == 0) {
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, 0);
+    if (e != hipSuccess) return e;
+    if (occ < 1) occ = 1;
+  }
+  const long grid = max(1L, min(max_items, (long)num_cus * occ));
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// Host-side entry used by the C-ABI layer.
+hipError_t launch_fwd(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
+  if (f32) {
+    if (D == 32) return launch_fwd_t<float, 32>(a, bias, max_items, num_cus, st);
+    if (D == 64) return launch_fwd_t<float, 64>(a, bias, max_items, num_cus, st);
+    return launch_fwd_t<float, 128>(a, bias, max_items, num_cus, st);
+  }
+  if (D == 32) return launch_fwd_t<bf16, 32>(a, bias, max_items, num_cus, st);
+  if (D == 64) return launch_fwd_t<bf16, 64>(a, bias, max_items, num_cus, st);
+  return launch_fwd_t<bf16, 128>(a, bias, max_items, num_cus, st);
+}
+
+}  // namespace jfa

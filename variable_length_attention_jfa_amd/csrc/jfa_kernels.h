@@ -1,0 +1,77 @@
+// Kernel argument blocks and launch entry points shared by the kernels and
+// the C-ABI layer (host code sees only these declarations).
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace jfa {
+
+struct PlanHeader;
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int* q_off;
+  const int* kv_off;
+  const float* bias;  // [H][257] or null
+  void* out;
+  float* lse;
+  const int4* items;
+  PlanHeader* hdr;
+  int H;
+  int causal;
+  float scale2;  // softmax scale * log2(e)
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  const int* q_off;
+  const int* kv_off;
+  const float* bias;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;        // [Tq, H] fp32 (workspace)
+  const int4* items;   // work list of this pass
+  PlanHeader* hdr;
+  int H;
+  int causal;
+  float scale;         // 1/sqrt(D)
+  float scale2;        // scale * log2(e)
+  long rows;           // Tq * H (delta kernel)
+};
+
+struct PlanPass {
+  int4* items;
+  PlanHeader* hdr;
+  long capacity;  // items that fit the workspace
+  int TM, TN;     // query rows / keys per tile and per visited block
+  int kv_pass;
+};
+
+struct PlanArgs {
+  const int* q_off;
+  const int* kv_off;
+  int B, H, causal;
+  PlanPass pass[2];
+};
+
+// Tile shapes (query rows x keys) of each kernel.
+constexpr int kFwdTM = 128, kFwdTN = 64;
+constexpr int kDkvTM = 64, kDkvTN = 128;
+constexpr int kDqTM = 128, kDqTN = 64;
+
+// Persistent launches: grid = min(max_items, CUs x resident workgroups per CU).
+hipError_t launch_fwd(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
+hipError_t launch_delta(bool f32, int D, const BwdArgs& a, hipStream_t st);
+hipError_t launch_dkdv(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
+hipError_t launch_dq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
+hipError_t launch_plan(const PlanArgs& a, int npass, hipStream_t st);
+hipError_t launch_scan(const int* lengths, int B, int* offsets, hipStream_t st);
+
+}  // namespace jfa
