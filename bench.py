@@ -45,6 +45,37 @@ def valid_pairs(q_lengths, kv_lengths, causal):
     return total
 
 
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources; HBM byte counts recorded for other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "variable_length_attention_jfa_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as fh:
+                h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:12]
+
+
+def recorded_traffic(kernel_label: str, workload: int):
+    """HBM bytes per launch from the committed rocprofv3 summaries (FETCH_SIZE and
+    WRITE_SIZE, scaled by the plain-copy calibration), or None if none matches the
+    current kernel sources."""
+    import glob
+    import re
+    src = kernel_source_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt"))):
+        with open(path) as fh:
+            for line in fh:
+                if "traffic-line" not in line:
+                    continue
+                kv = dict(re.findall(r"(\w+)=(\S+)", line))
+                if kv.get("kernel") == kernel_label and kv.get("workload") == str(workload) and kv.get("source") == src:
+                    return (float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
+                            float(kv["write_kib"]) * float(kv["write_scale"])) * 1024.0
+    return None
+
+
 # Algorithmic flops per valid pair per head, as multiples of D, for each kernel:
 # forward QK^T + PV; dK/dV pass recomputes QK^T and dO V^T and forms dV, dK;
 # dQ pass recomputes QK^T and dO V^T and forms dQ.
@@ -117,11 +148,26 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None)
     avg_ms = kt[dom][0] / kt[dom][1]
     alg = KERNEL_FLOPS_PER_PAIR_D[dom] * wl.D * wl.H * pairs
     achieved = alg / (avg_ms * 1e-3) / 1e12
-    res["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                       "frac": achieved / peak, "traffic": None,
-                       "avg_launch_ms": avg_ms, "algorithmic_flops_per_launch": alg}
+    label = f"jfa_{'fwd' if dom == 'forward' else dom}_kernel<{wl.dtype},D={wl.D}{',bias' if wl.bias else ''}>"
+    res["roofline"] = {"kernel": label, "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                       "frac": achieved / peak, "traffic": recorded_traffic(label, idx), "traffic_unit": "bytes/launch",
+                       "avg_launch_ms": avg_ms, "algorithmic_flops_per_launch": alg,
+                       "algorithmic_bytes_per_launch": algorithmic_bytes(dom, batch)}
     res["_batch"] = batch
     return res
+
+
+def algorithmic_bytes(kernel: str, batch) -> int:
+    """Bytes the kernel must move at least once: its inputs read, its outputs written."""
+    wl = batch.wl
+    e = 2 if wl.dtype == "bf16" else 4
+    tq, tk = batch.total_q * wl.H * wl.D * e, batch.total_kv * wl.H * wl.D * e
+    rows = batch.total_q * wl.H * 4
+    if kernel == "forward":      # q, k, v in; out, lse out
+        return tq + 2 * tk + tq + rows
+    if kernel == "dkdv":         # q, k, v, dout, lse, delta in; dk, dv out
+        return 2 * tq + 2 * tk + 2 * rows + 2 * tk
+    return 2 * tq + 2 * tk + 2 * rows + tq   # dq: q, k, v, dout, lse, delta in; dq out
 
 
 def cpu_baseline(batch, budget_s=15.0):
@@ -163,6 +209,8 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="also report workloads 1..5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="also run a plain device copy of MB mebibytes (reference for HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -177,6 +225,16 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     main_res = run_workload(args.workload, args.steps, args.warmup, torch, jfa, gen)
     print(f"[bench] workload {args.workload}: {main_res['tflops_step']:.1f} TFLOP/s fwd+bwd, "

@@ -59,9 +59,9 @@ struct DkvTiles {
   static constexpr int BNK = 128;  // keys per item (4 waves x 32)
   static constexpr int BMQ = 64;   // query rows per staged block
   static constexpr int THREADS = 256;
-  static constexpr int ROWB = D * (int)sizeof(T);
-  static constexpr int S = ROWB + 16;
-  static constexpr int QTILE = BMQ * S;
+  using TL = Tile<T, D>;
+  static constexpr int ROWB = TL::ROWB;
+  static constexpr int QTILE = BMQ * ROWB;
   static constexpr int STAGE = 2 * QTILE + 2 * BMQ * 4;  // Q, dO, lse2, delta
   static constexpr int CPR = ROWB / 16;
   static constexpr int CPT = BMQ * CPR / THREADS;
@@ -137,8 +137,9 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv_
 #pragma unroll
       for (int c = 0; c < C::CPT; ++c) {
         const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
-        *(__attribute__((address_space(3))) i32x4*)(st + row * C::S + col * 16) = qr[c];
-        *(__attribute__((address_space(3))) i32x4*)(st + C::QTILE + row * C::S + col * 16) = dr[c];
+        const int o = C::TL::chunk(row, col);
+        *(__attribute__((address_space(3))) i32x4*)(st + o) = qr[c];
+        *(__attribute__((address_space(3))) i32x4*)(st + C::QTILE + o) = dr[c];
       }
       if (tid < 2 * BMQ) *(__attribute__((address_space(3))) float*)(st + 2 * C::QTILE + tid * 4) = lr;
     };
@@ -146,6 +147,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv_
       gload(qb0);
       swrite(0);
     }
+    wait_vmem();
     __syncthreads();
 
     f32x16 dk[D / 32], dv[D / 32];
@@ -171,9 +173,8 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv_
         f32x16 sc = (f32x16){}, dp = (f32x16){};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          const int off = (32 * sb + l32) * C::S + (16 * kk + 8 * g) * ES;
-          mma(sc, lfrag(qt + off, (T*)0), kf[kk]);
-          mma(dp, lfrag(dot + off, (T*)0), vf[kk]);
+          mma(sc, lfrag<D>(qt, 32 * sb + l32, 16 * kk + 8 * g, (T*)0), kf[kk]);
+          mma(dp, lfrag<D>(dot, 32 * sb + l32, 16 * kk + 8 * g, (T*)0), vf[kk]);
         }
         // sc[i] = S[query 32sb + res_row(i,g)][key kj]
 #pragma unroll
@@ -193,8 +194,8 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv_
           const Frag<T> sf = rfrag(dp, c, (T*)0);
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            mma(dv[db], tfrag<C::S>(dot, 32 * sb + 16 * c, 32 * db, lane, (T*)0), pf);
-            mma(dk[db], tfrag<C::S>(qt, 32 * sb + 16 * c, 32 * db, lane, (T*)0), sf);
+            mma(dv[db], tfrag<D>(dot, 32 * sb + 16 * c, 32 * db, lane, (T*)0), pf);
+            mma(dk[db], tfrag<D>(qt, 32 * sb + 16 * c, 32 * db, lane, (T*)0), sf);
           }
         }
       }
@@ -227,9 +228,9 @@ struct DqTiles {
   static constexpr int BM = 128;  // query rows per item (4 waves x 32)
   static constexpr int BN = 64;   // keys per staged block
   static constexpr int THREADS = 256;
-  static constexpr int ROWB = D * (int)sizeof(T);
-  static constexpr int S = ROWB + 16;
-  static constexpr int KTILE = BN * S;
+  using TL = Tile<T, D>;
+  static constexpr int ROWB = TL::ROWB;
+  static constexpr int KTILE = BN * ROWB;
   static constexpr int STAGE = 2 * KTILE;
   static constexpr int CPR = ROWB / 16;
   static constexpr int CPT = BN * CPR / THREADS;
@@ -301,14 +302,16 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dq_ke
 #pragma unroll
       for (int c = 0; c < C::CPT; ++c) {
         const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
-        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + row * C::S + col * 16) = kr[c];
-        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + C::KTILE + row * C::S + col * 16) = vr[c];
+        const int o = C::TL::chunk(row, col);
+        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + o) = kr[c];
+        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + C::KTILE + o) = vr[c];
       }
     };
     if (n_kv > 0) {
       gload(0);
       swrite(0);
     }
+    wait_vmem();
     __syncthreads();
 
     f32x16 dq[D / 32];
@@ -335,9 +338,8 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dq_ke
           dp[kb] = (f32x16){};
 #pragma unroll
           for (int kk = 0; kk < D / 16; ++kk) {
-            const int off = (32 * kb + l32) * C::S + (16 * kk + 8 * g) * ES;
-            mma(sc[kb], lfrag(kt + off, (T*)0), qf[kk]);
-            mma(dp[kb], lfrag(vt + off, (T*)0), df[kk]);
+            mma(sc[kb], lfrag<D>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), qf[kk]);
+            mma(dp[kb], lfrag<D>(vt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), df[kk]);
           }
         }
 #pragma unroll
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dq_ke
         for (int kc = 0; kc < BN / 16; ++kc) {
           const Frag<T> sf = rfrag(dp[kc >> 1], kc & 1, (T*)0);
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) mma(dq[db], tfrag<C::S>(kt, 16 * kc, 32 * db, lane, (T*)0), sf);
+          for (int db = 0; db < D / 32; ++db) mma(dq[db], tfrag<D>(kt, 16 * kc, 32 * db, lane, (T*)0), sf);
         }
       }
       if (j + 1 < n_kv) swrite((j + 1) & 1);

@@ -102,49 +102,76 @@ __device__ __forceinline__ Frag<float> gfrag(const View& v, uint32_t off, float*
   return f;
 }
 
-// Fragment from 8 consecutive elements of an LDS row (natural layout).
-__device__ __forceinline__ Frag<bf16> lfrag(const lds_t* p, bf16*) {
+// ---------------------------------------------------------------------------
+// LDS tiles: ROWS x D elements, rows of ROWB = D * sizeof(T) bytes with no
+// padding. The 16-byte chunks of each row are permuted by an XOR with a
+// function of the row, chosen so that (on the 64-bank, 4-byte LDS of gfx950)
+//   * 16-byte operand reads (16 lanes per cycle, 16 consecutive rows, same
+//     chunk),
+//   * transposing reads (32 lanes per cycle, 4 consecutive rows x 64 bytes),
+//   * 16-byte staging writes (whole rows)
+// each touch every bank at most once per cycle.
+template <typename T, int D>
+struct Tile {
+  static constexpr int ROWB = D * (int)sizeof(T);
+  static constexpr int CPR = ROWB / 16;
+  __device__ __forceinline__ static int swz(int r) {
+    if constexpr (CPR >= 16) return 4 * (r & 3) + ((r >> 2) & 3);
+    else if constexpr (CPR == 8) return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+    else return (r >> 2) & 3;
+  }
+  // byte offset of 16-byte chunk c of row r
+  __device__ __forceinline__ static int chunk(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
+  // byte offset of byte b (within the unpermuted row) of row r
+  __device__ __forceinline__ static int byte(int r, int b) { return chunk(r, b >> 4) + (b & 15); }
+};
+
+// Fragment from 8 consecutive elements (row r, elements col .. col+7) of a tile.
+template <int D>
+__device__ __forceinline__ Frag<bf16> lfrag(const lds_t* tile, int r, int col, bf16*) {
   Frag<bf16> f;
-  f.v = *(const __attribute__((address_space(3))) bf16x8*)p;
+  f.v = *(const __attribute__((address_space(3))) bf16x8*)(tile + Tile<bf16, D>::byte(r, col * 2));
   return f;
 }
-__device__ __forceinline__ Frag<float> lfrag(const lds_t* p, float*) {
+template <int D>
+__device__ __forceinline__ Frag<float> lfrag(const lds_t* tile, int r, int col, float*) {
   Frag<float> f;
-  f.lo = *(const __attribute__((address_space(3))) f32x4*)p;
-  f.hi = *(const __attribute__((address_space(3))) f32x4*)(p + 16);
+  f.lo = *(const __attribute__((address_space(3))) f32x4*)(tile + Tile<float, D>::byte(r, col * 4));
+  f.hi = *(const __attribute__((address_space(3))) f32x4*)(tile + Tile<float, D>::byte(r, col * 4 + 16));
   return f;
 }
 
-// Transposed fragment: k runs down the rows of a row-major LDS tile, the lane's
-// column is fixed. The k-slot order matches the row order of a 32x32 MFMA
-// result held by the other operand: slot e of half g is row
+// Transposed fragment: k runs down the rows of the tile, the lane's column is
+// fixed. The k-slot order matches the row order of a 32x32 MFMA result held
+// by the other operand: slot e of half g is row
 //   rowbase + 4g + e        (e < 4)
 //   rowbase + 8 + 4g + e-4  (e >= 4).
 // bf16: two ds_read_b64_tr_b16. Each 16-lane group gives four row addresses
 // (one per lane quad) and the hardware hands lane i the i-th column of those
 // four rows. Column = colbase + (l & 31).
-template <int STRIDE>
+template <int D>
 __device__ __forceinline__ Frag<bf16> tfrag(const lds_t* tile, int rowbase, int colbase, int lane, bf16*) {
+  using TL = Tile<bf16, D>;
   const int g = lane >> 5;
   const int row = rowbase + 4 * g + ((lane & 15) >> 2);
-  const int col = colbase + ((lane & 31) >> 4) * 16 + (lane & 3) * 4;
-  const lds_t* p = tile + row * STRIDE + col * 2;
-  s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-  s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 8 * STRIDE));
+  const int b = (colbase + ((lane & 31) >> 4) * 16 + (lane & 3) * 4) * 2;
+  s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + TL::byte(row, b)));
+  s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + TL::byte(row + 8, b)));
   Frag<bf16> f;
-  bf16x4 a4 = __builtin_bit_cast(bf16x4, a), b4 = __builtin_bit_cast(bf16x4, b);
-  f.v = (bf16x8){a4[0], a4[1], a4[2], a4[3], b4[0], b4[1], b4[2], b4[3]};
+  bf16x4 x4 = __builtin_bit_cast(bf16x4, x), y4 = __builtin_bit_cast(bf16x4, y);
+  f.v = (bf16x8){x4[0], x4[1], x4[2], x4[3], y4[0], y4[1], y4[2], y4[3]};
   return f;
 }
-template <int STRIDE>
+template <int D>
 __device__ __forceinline__ Frag<float> tfrag(const lds_t* tile, int rowbase, int colbase, int lane, float*) {
+  using TL = Tile<float, D>;
   const int g = lane >> 5;
-  const lds_t* p = tile + (rowbase + 4 * g) * STRIDE + (colbase + (lane & 31)) * 4;
+  const int b = (colbase + (lane & 31)) * 4;
   Frag<float> f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) f.lo[e] = *(const __attribute__((address_space(3))) float*)(p + e * STRIDE);
+  for (int e = 0; e < 4; ++e) f.lo[e] = *(const __attribute__((address_space(3))) float*)(tile + TL::byte(rowbase + 4 * g + e, b));
 #pragma unroll
-  for (int e = 0; e < 4; ++e) f.hi[e] = *(const __attribute__((address_space(3))) float*)(p + (8 + e) * STRIDE);
+  for (int e = 0; e < 4; ++e) f.hi[e] = *(const __attribute__((address_space(3))) float*)(tile + TL::byte(rowbase + 8 + 4 * g + e, b));
   return f;
 }
 
@@ -189,6 +216,16 @@ __device__ __forceinline__ void store4(const View& v, uint32_t off, float a, flo
 }
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Wait until every outstanding vector-memory load of this wave has landed.
+// Used once per work item after the register-resident operand fragments are
+// loaded: it tells the compiler's wait-count tracking that nothing older than
+// the tile prefetches is in flight inside the main loop, so the MFMAs there
+// do not wait on the next tile's prefetch.
+__device__ __forceinline__ void wait_vmem() {
+  // gfx9 s_waitcnt encoding: vmcnt = 0, expcnt = 7 (bits 6:4), lgkmcnt = 15 (bits 11:8)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
 
 // Work-list header in the caller's workspace.
 struct PlanHeader {

@@ -27,17 +27,17 @@
 
 namespace jfa {
 
+constexpr float kRescaleSlack = 8.0f;  // log2 units: P never exceeds 256
+
 template <typename T, int D>
 struct FwdTiles {
   static constexpr int BM = 128;  // query rows per item (4 waves x 32)
   static constexpr int BN = 64;   // keys per block
   static constexpr int THREADS = 256;
-  static constexpr int ROWB = D * (int)sizeof(T);
-  static constexpr int KS = ROWB + 16;  // K tile row stride: 16-byte natural reads, conflict-free
-  static constexpr int VS = ROWB + 32;  // V tile row stride: transposed reads, conflict-free
-  static constexpr int KTILE = BN * KS;
-  static constexpr int VTILE = BN * VS;
-  static constexpr int STAGE = KTILE + VTILE;
+  using TL = Tile<T, D>;
+  static constexpr int ROWB = TL::ROWB;
+  static constexpr int KTILE = BN * ROWB;
+  static constexpr int STAGE = 2 * KTILE;  // K then V
   static constexpr int CPR = ROWB / 16;              // 16-byte pieces per row
   static constexpr int CPT = BN * CPR / THREADS;     // pieces per thread per tile
   static constexpr int BIAS_OFF = 2 * STAGE;
@@ -45,8 +45,6 @@ struct FwdTiles {
   static_assert((BN * CPR) % THREADS == 0, "tile pieces divide the workgroup");
   static_assert(BM == kFwdTM && BN == kFwdTN, "tile shape published to the planner");
 };
-
-
 
 template <typename T, int D, bool BIAS>
 __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_kernel(FwdArgs a) {
@@ -102,14 +100,16 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
 #pragma unroll
       for (int c = 0; c < C::CPT; ++c) {
         const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
-        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + row * C::KS + col * 16) = kr[c];
-        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + C::KTILE + row * C::VS + col * 16) = vr[c];
+        const int o = C::TL::chunk(row, col);
+        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + o) = kr[c];
+        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + C::KTILE + o) = vr[c];
       }
     };
     if (n_kv > 0) {
       gload(0);
       swrite(0);
     }
+    wait_vmem();
     __syncthreads();
 
     f32x16 o[D / 32];
@@ -136,42 +136,73 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
           sc[kb] = (f32x16){};
 #pragma unroll
           for (int kk = 0; kk < D / 16; ++kk)
-            mma(sc[kb], lfrag(kt + (32 * kb + l32) * C::KS + (16 * kk + 8 * g) * ES, (T*)0), qf[kk]);
+            mma(sc[kb], lfrag<D>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), qf[kk]);
         }
+        // Scores in log2 units: x = s * scale * log2(e) (+ bias * log2(e)).
         float mx = -INFINITY;
+        const bool plain = !BIAS && !masked;
+        if (plain) {
+          // max on the raw dot products; the scale is folded into the exp below
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
+          for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kj = key0 + 32 * kb + res_row(i, g);
-            float x = sc[kb][i] * a.scale2;
-            if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
-            if (masked && (kj > qi || kj >= Lk)) x = -INFINITY;
-            sc[kb][i] = x;
-            mx = fmaxf(mx, x);
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+          mx = half_max(mx) * a.scale2;
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int kj = key0 + 32 * kb + res_row(i, g);
+              float x = sc[kb][i] * a.scale2;
+              if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+              if (masked && (kj > qi || kj >= Lk)) x = -INFINITY;
+              sc[kb][i] = x;
+              mx = fmaxf(mx, x);
+            }
           }
+          mx = half_max(mx);
         }
-        mx = half_max(mx);
-        const float mn = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        m = mn;
-        l *= alpha;
+        // Running max with slack: m only moves when the block max exceeds it
+        // by more than kRescaleSlack, so P <= 2^kRescaleSlack and O, l are
+        // rescaled only on those (rare) blocks. l and O share m, so the final
+        // O / l and lse = m + log2(l) are unchanged.
+        const bool grow = mx > m + kRescaleSlack;
+        if (__any(grow)) {
+          const float mn = grow ? mx : m;
+          const float alpha = __builtin_amdgcn_exp2f(m - mn);
+          m = mn;
+          l *= alpha;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+          for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        }
+        if (plain) {
+          const float nm = -m;
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
+          for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(sc[kb][i] - mn);
-            sc[kb][i] = p;
-            l += p;
+            for (int i = 0; i < 16; ++i) {
+              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], a.scale2, nm));
+              sc[kb][i] = p;
+              l += p;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float p = __builtin_amdgcn_exp2f(sc[kb][i] - m);
+              sc[kb][i] = p;
+              l += p;
+            }
           }
         }
 #pragma unroll
         for (int kc = 0; kc < BN / 16; ++kc) {
           const Frag<T> pf = rfrag(sc[kc >> 1], kc & 1, (T*)0);
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) mma(o[db], tfrag<C::VS>(vt, 16 * kc, 32 * db, lane, (T*)0), pf);
+          for (int db = 0; db < D / 32; ++db) mma(o[db], tfrag<D>(vt, 16 * kc, 32 * db, lane, (T*)0), pf);
         }
       }
       if (j + 1 < n_kv) swrite((j + 1) & 1);
