@@ -62,6 +62,8 @@ typedef enum {
 
 #define JFA_BIAS_RADIUS 128 /* bias table is [H][2 * JFA_BIAS_RADIUS + 1] */
 #define JFA_MAX_BATCH 8192  /* largest B accepted by one call */
+#define JFA_PLAN_QUEUES 8   /* work-list queues, one per XCD */
+#define JFA_PLAN_HEADER_BYTES 2048
 
 /* Kernel ids for jfa_tile_config / jfa_build_plan. */
 #define JFA_KERNEL_FWD 0       /* forward: tiles of query rows            */
@@ -120,11 +122,18 @@ jfa_status jfa_offsets_from_lengths(const int32_t* lengths, int B, int32_t* offs
  * is one tile of tile_n keys and its cost counts tile_m-row query blocks. */
 jfa_status jfa_tile_config(int kernel, int D, int dtype, int* tile_m, int* tile_n);
 
-/* Builds the longest-first work list the given kernel runs on, into
- * `workspace`: a 64-byte header (int32 count, ticket, status, ...) followed
- * by `count` items of four int32 (b, h, tile, cost). Order: cost descending
- * (costs of 1023 and more tie), then b, h, tile ascending. Exposed so that the
- * list can be checked against an independent builder. */
+/* Builds the longest-first work lists the given kernel runs on, into
+ * `workspace`: a JFA_PLAN_HEADER_BYTES header of int32 {count, status, nq,
+ * pad, start[8], qcount[8], ...; queue q's ticket at int32 index 32 * (q + 1)}
+ * followed by `count` items of four
+ * int32 (b, h, tile, cost). The items of one (b, h) form a group whose cost
+ * is the sum of its items' costs; groups are ranked by cost descending, then
+ * b, then h, and group rank g goes to queue g mod 16 < 8 ? g mod 8 :
+ * 15 - g mod 16 (one queue per XCD; a workgroup drains its own queue, then
+ * the others). Inside a queue groups follow their rank; inside a group items
+ * follow cost descending, then tile ascending. Queue q holds items
+ * [start[q], start[q] + qcount[q]). Exposed so that the lists can be checked
+ * against an independent builder. */
 jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D, int dtype,
                           int causal, int kernel, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -10,4 +10,4 @@ Modules:
   plan       the longest-first work list and the offsets scan, as integers
 """
 from .attention import forward, backward, valid_pairs  # noqa: F401
-from .plan import build_plan, q_tile_cost, kv_tile_cost, exclusive_scan, COST_KEY_CAP  # noqa: F401
+from .plan import build_plan, build_plan_queues, q_tile_cost, kv_tile_cost, exclusive_scan, snake, N_QUEUES  # noqa: F401

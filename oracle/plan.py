@@ -1,11 +1,11 @@
-"""Integer reference for the offsets scan and the longest-first work list
+"""Integer reference for the offsets scan and the longest-first work lists
 (test infrastructure only).
 
 Sources: jagged tensors addressed by prefix-sum offsets ("Jagged Flash
 Attention (JFA)", section "Definition"); short sequences must not leave compute
 units idle ("Why standard FlashAttention falls short"); persistent kernel
 scheduling ("Four generations", item 3). The pages give no cost model or order;
-the reading used here is the plainest longest-processing-time-first list:
+the reading used here:
 
   q pass (forward and the dQ pass): one item per (b, h, t) with t a tile of TM
     query rows, t < ceil(Lq/TM). Its cost is the number of TN-wide key blocks
@@ -16,9 +16,15 @@ the reading used here is the plainest longest-processing-time-first list:
     ceil(Lq/TM), or with the causal mask 0 if t*TN >= Lq else
     ceil(Lq/TM) - floor(t*TN/TM).
 
-Items are ordered by descending cost (cost values at or above COST_KEY_CAP - 1
-share one key), then by b, h, t ascending, which makes the order unique.
-Items of cost 0 stay in the list: they still own outputs that must be written.
+Order, longest first at two levels. The items of one (b, h) form a group
+whose cost is the sum of its items' costs (the same for every h of a
+sequence). Groups are ranked by group cost descending, then b, then h. Group
+rank g goes to queue snake(g): g mod 2Q < Q ? g mod Q : 2Q-1 - (g mod 2Q),
+with Q queues (one per XCD of the GPU, so that the items sharing one (b, h)'s
+keys and values run under one L2). Inside a queue, groups follow their rank;
+inside a group, items are ordered by cost descending, then t ascending. The
+queues are stored one after the other. Items of cost 0 stay in the lists:
+they still own outputs that must be written.
 """
 from __future__ import annotations
 
@@ -26,7 +32,7 @@ from typing import List, Tuple
 
 import numpy as np
 
-COST_KEY_CAP = 1024
+N_QUEUES = 8
 
 
 def _cdiv(a: int, b: int) -> int:
@@ -57,20 +63,44 @@ def kv_tile_cost(Lq: int, Lk: int, t: int, TM: int, TN: int, causal: bool) -> in
     return nq - first_key // TM
 
 
-def build_plan(q_offsets, kv_offsets, H: int, TM: int, TN: int, causal: bool,
-               kv_pass: bool = False) -> np.ndarray:
-    """Work list as an int32 array [n_items, 4] of (b, h, tile, cost)."""
+def snake(g: int, n_queues: int) -> int:
+    r = g % (2 * n_queues)
+    return r if r < n_queues else 2 * n_queues - 1 - r
+
+
+def build_plan_queues(q_offsets, kv_offsets, H: int, TM: int, TN: int, causal: bool, kv_pass: bool = False,
+                      n_queues: int = N_QUEUES) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Work lists as (items int32 [n, 4] of (b, h, tile, cost) with the queues
+    stored one after the other, starts int32 [n_queues], counts int32 [n_queues])."""
     qo = [int(x) for x in q_offsets]
     ko = [int(x) for x in kv_offsets]
-    items: List[Tuple[int, int, int, int]] = []
-    for b in range(len(qo) - 1):
+    B = len(qo) - 1
+    seq_items: List[List[Tuple[int, int]]] = []   # per sequence: (tile, cost) in group order
+    seq_cost: List[int] = []
+    for b in range(B):
         Lq, Lk = qo[b + 1] - qo[b], ko[b + 1] - ko[b]
         if kv_pass:
             n, costf = _cdiv(Lk, TN), kv_tile_cost
         else:
             n, costf = _cdiv(Lq, TM), q_tile_cost
+        tiles = [(t, costf(Lq, Lk, t, TM, TN, causal)) for t in range(n)]
+        tiles.sort(key=lambda tc: (-tc[1], tc[0]))
+        seq_items.append(tiles)
+        seq_cost.append(sum(c for _, c in tiles))
+    order = sorted(range(B), key=lambda b: (-seq_cost[b], b))
+    queues: List[List[Tuple[int, int, int, int]]] = [[] for _ in range(n_queues)]
+    g = 0
+    for b in order:
         for h in range(H):
-            for t in range(n):
-                items.append((b, h, t, costf(Lq, Lk, t, TM, TN, causal)))
-    items.sort(key=lambda it: (-min(it[3], COST_KEY_CAP - 1), it[0], it[1], it[2]))
-    return np.array(items, dtype=np.int32).reshape(-1, 4)
+            queues[snake(g, n_queues)].extend((b, h, t, c) for t, c in seq_items[b])
+            g += 1
+    counts = np.array([len(qu) for qu in queues], dtype=np.int32)
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int32)
+    items = np.array([it for qu in queues for it in qu], dtype=np.int32).reshape(-1, 4)
+    return items, starts, counts
+
+
+def build_plan(q_offsets, kv_offsets, H: int, TM: int, TN: int, causal: bool, kv_pass: bool = False,
+               n_queues: int = N_QUEUES) -> np.ndarray:
+    """All items, queues concatenated (see build_plan_queues)."""
+    return build_plan_queues(q_offsets, kv_offsets, H, TM, TN, causal, kv_pass, n_queues)[0]

@@ -134,32 +134,35 @@ def test_plan_bit_exact(kernel, causal, cfg):
     ql = wl.q_len.sample(rng, wl.B)
     kl = wl.kv_len.sample(rng, wl.B) if wl.kv_len is not None else ql
     qo, ko = gen.offsets_from_lengths(ql), gen.offsets_from_lengths(kl)
-    tm, tn = jfa.tile_config(kernel, wl.D)
-    ref = oracle.build_plan(qo, ko, wl.H, tm, tn, causal, kv_pass=(kernel == jfa.KERNEL_BWD_DKDV))
-    hdr, items = jfa.build_plan(torch.from_numpy(qo).cuda(), torch.from_numpy(ko).cuda(), wl.H, wl.D, causal, kernel,
+    _check_plan(qo, ko, wl.H, wl.D, causal, kernel)
+
+
+def _check_plan(qo, ko, H, D, causal, kernel):
+    tm, tn = jfa.tile_config(kernel, D)
+    ref, starts, counts = oracle.build_plan_queues(qo, ko, H, tm, tn, causal, kv_pass=(kernel == jfa.KERNEL_BWD_DKDV),
+                                                   n_queues=jfa.PLAN_QUEUES)
+    hdr, items = jfa.build_plan(torch.from_numpy(qo).cuda(), torch.from_numpy(ko).cuda(), H, D, causal, kernel,
                                 int(qo[-1]), int(ko[-1]))
     torch.cuda.synchronize()
     h = hdr.cpu().numpy()
-    assert h[0] == len(ref) and h[1] == 0 and h[2] == 0
+    assert h[0] == len(ref) and h[1] == 0 and h[2] == jfa.PLAN_QUEUES
+    np.testing.assert_array_equal(h[4:12], starts)
+    np.testing.assert_array_equal(h[12:20], counts)
+    np.testing.assert_array_equal(h[32:32 * 9:32], 0)  # tickets
     np.testing.assert_array_equal(items[:len(ref)].cpu().numpy(), ref)
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_plan_bit_exact_random(seed):
     rng = np.random.default_rng(seed)
-    B = int(rng.integers(1, 3000))
+    B = int(rng.integers(1, 3000)) if seed else 8192
     ql = rng.integers(0, 3000, size=B) * (rng.random(B) < 0.9)
     kl = rng.integers(0, 5000, size=B) * (rng.random(B) < 0.9)
     qo, ko = gen.offsets_from_lengths(ql), gen.offsets_from_lengths(kl)
     H = int(rng.integers(1, 9))
     for kernel in (jfa.KERNEL_FWD, jfa.KERNEL_BWD_DKDV, jfa.KERNEL_BWD_DQ):
         for causal in (False, True):
-            tm, tn = jfa.tile_config(kernel, 128)
-            ref = oracle.build_plan(qo, ko, H, tm, tn, causal, kv_pass=(kernel == jfa.KERNEL_BWD_DKDV))
-            hdr, items = jfa.build_plan(torch.from_numpy(qo).cuda(), torch.from_numpy(ko).cuda(), H, 128, causal,
-                                        kernel, int(qo[-1]), int(ko[-1]))
-            assert int(hdr[0].item()) == len(ref)
-            np.testing.assert_array_equal(items[:len(ref)].cpu().numpy(), ref)
+            _check_plan(qo, ko, H, 128, causal, kernel)
 
 
 @pytest.mark.parametrize("B", [0, 1, 5, 1023, 1024, 1025, 8192])
@@ -180,22 +183,22 @@ def test_invalid_arguments_raise():
                    jfa._ptr(d["q"]), None, 0, None)
     assert st == 1
     # workspace too small
-    ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(d["q"])
     lse = torch.empty(batch.total_q, 8, dtype=torch.float32, device="cuda")
     st = L.jfa_fwd(jfa._ptr(d["q"]), jfa._ptr(d["k"]), jfa._ptr(d["v"]), jfa._ptr(d["q_offsets"]),
                    jfa._ptr(d["kv_offsets"]), 6, 8, 64, batch.total_q, batch.total_kv, None, 0, jfa._ptr(out),
-                   jfa._ptr(lse), jfa._ptr(ws), 1024, None)
+                   jfa._ptr(lse), jfa._ptr(ws), 4096, None)
     assert st == 2
     assert b"workspace" in L.jfa_last_error()
     # misaligned q
     st = L.jfa_fwd(ctypes_offset(d["q"], 2), jfa._ptr(d["k"]), jfa._ptr(d["v"]), jfa._ptr(d["q_offsets"]),
                    jfa._ptr(d["kv_offsets"]), 6, 8, 64, batch.total_q, batch.total_kv, None, 0, jfa._ptr(out),
-                   jfa._ptr(lse), jfa._ptr(ws), 1024, None)
+                   jfa._ptr(lse), jfa._ptr(ws), 4096, None)
     assert st == 1
     # B = 0 is a no-op
     st = L.jfa_fwd(None, None, None, jfa._ptr(d["q_offsets"]), jfa._ptr(d["kv_offsets"]), 0, 8, 64, 0, 0, None, 0,
-                   None, None, jfa._ptr(ws), 1024, None)
+                   None, None, jfa._ptr(ws), 4096, None)
     assert st == 0
 
 

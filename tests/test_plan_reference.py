@@ -1,7 +1,8 @@
-"""Pins for the integer reference of the work list and the offsets scan.
+"""Pins for the integer reference of the work lists and the offsets scan.
 
 Costs are checked against brute force: a tile's cost must equal the number of
-blocks that hold at least one (query, key) pair the attention uses.
+blocks that hold at least one (query, key) pair the attention uses. The list
+order is checked against its stated properties.
 """
 import numpy as np
 import pytest
@@ -47,34 +48,55 @@ def test_costs_brute_force(TM, TN):
                 assert P.kv_tile_cost(Lq, Lk, t, TM, TN, causal) == _brute_kv_cost(Lq, Lk, t, TM, TN, causal)
 
 
+def test_snake_deal():
+    assert [P.snake(g, 4) for g in range(10)] == [0, 1, 2, 3, 3, 2, 1, 0, 0, 1]
+    assert [P.snake(g, 1) for g in range(3)] == [0, 0, 0]
+
+
+@pytest.mark.parametrize("n_queues", [1, 8])
 @pytest.mark.parametrize("kv_pass", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
-def test_plan_is_a_sorted_permutation(kv_pass, causal):
-    rng = np.random.default_rng(3 + kv_pass + 2 * causal)
-    lq = rng.integers(0, 700, size=23)
-    lk = rng.integers(0, 900, size=23)
+def test_plan_properties(kv_pass, causal, n_queues):
+    rng = np.random.default_rng(3 + kv_pass + 2 * causal + n_queues)
+    B, H, TM, TN = 23, 3, 128, 64
+    lq = rng.integers(0, 700, size=B)
+    lk = rng.integers(0, 900, size=B)
     qo, ko = oracle.exclusive_scan(lq), oracle.exclusive_scan(lk)
-    H, TM, TN = 3, 128, 64
-    items = oracle.build_plan(qo, ko, H, TM, TN, causal, kv_pass)
-    expect = set()
-    for b in range(23):
+    items, starts, counts = oracle.build_plan_queues(qo, ko, H, TM, TN, causal, kv_pass, n_queues)
+    # every (b, h, t) exactly once, with its cost
+    expect = {}
+    for b in range(B):
         n = -(-int(lk[b]) // TN) if kv_pass else -(-int(lq[b]) // TM)
+        f = P.kv_tile_cost if kv_pass else P.q_tile_cost
         for h in range(H):
             for t in range(n):
-                expect.add((b, h, t))
-    got = [tuple(int(x) for x in it[:3]) for it in items]
-    assert len(got) == len(expect) and set(got) == expect
-    keys = [(-min(int(it[3]), P.COST_KEY_CAP - 1), int(it[0]), int(it[1]), int(it[2])) for it in items]
-    assert all(keys[i] < keys[i + 1] for i in range(len(keys) - 1))
-
-
-def test_cost_key_cap_ties_break_by_index():
-    # two sequences whose costs exceed the cap share one key and keep b order
-    lq = np.array([1, 1])
-    lk = np.array([2000 * 64, 1500 * 64])
-    items = oracle.build_plan(oracle.exclusive_scan(lq), oracle.exclusive_scan(lk), 1, 64, 64, False)
-    assert [int(x) for x in items[:, 0]] == [0, 1]
-    assert [int(x) for x in items[:, 3]] == [2000, 1500]
+                expect[(b, h, t)] = f(int(lq[b]), int(lk[b]), t, TM, TN, causal)
+    got = {(int(a), int(b_), int(c)): int(d) for a, b_, c, d in items}
+    assert len(items) == len(expect) and got == expect
+    assert counts.sum() == len(items) and starts[0] == 0 and np.all(np.diff(starts) == counts[:-1])
+    # group costs: one per sequence; groups are contiguous inside a queue and ranked longest first
+    gcost = {}
+    for (b, h, t), c in expect.items():
+        gcost[b] = gcost.get(b, 0) + c
+    order = sorted(range(B), key=lambda b: (-gcost.get(b, 0), b))
+    rank = {}
+    g = 0
+    for b in order:
+        for h in range(H):
+            rank[(b, h)] = g
+            g += 1
+    for qi in range(n_queues):
+        qu = items[starts[qi]:starts[qi] + counts[qi]]
+        groups = []
+        for b, h, t, c in qu:
+            if not groups or groups[-1] != (b, h):
+                groups.append((int(b), int(h)))
+        assert len(groups) == len(set(groups)), "a group must be contiguous"
+        assert all(P.snake(rank[gr], n_queues) == qi for gr in groups)
+        assert [rank[gr] for gr in groups] == sorted(rank[gr] for gr in groups)
+        for gr in groups:
+            its = [(int(c), int(t)) for b, h, t, c in qu if (b, h) == gr]
+            assert its == sorted(its, key=lambda ct: (-ct[0], ct[1]))
 
 
 def test_exclusive_scan():

@@ -11,9 +11,12 @@
 #include <vector>
 #include <string>
 
-#include "../../include/jfa.h"
+#include "jfa.h"
 #include "jfa_common.h"
 #include "jfa_kernels.h"
+
+static_assert(sizeof(jfa::PlanHeader) == JFA_PLAN_HEADER_BYTES, "work-list header layout published in jfa.h");
+static_assert(jfa::kPlanQueues == JFA_PLAN_QUEUES, "queue count published in jfa.h");
 
 namespace {
 
@@ -128,20 +131,20 @@ FwdLayout fwd_layout(int B, int H, int64_t tq) {
   FwdLayout L;
   L.cap = max_items(B, H, tq, jfa::kFwdTM);
   L.hdr = 0;
-  L.items = kAlign;
+  L.items = sizeof(PlanHeader);
   L.total = L.items + align_up((size_t)L.cap * 16);
   return L;
 }
 
 struct BwdLayout {
-  size_t hdr_kv = 0, hdr_q = 64, delta = 0, items_kv = 0, items_q = 0, total = 0;
+  size_t hdr_kv = 0, hdr_q = sizeof(PlanHeader), delta = 0, items_kv = 0, items_q = 0, total = 0;
   int64_t cap_kv = 0, cap_q = 0;
 };
 BwdLayout bwd_layout(int B, int H, int64_t tq, int64_t tk) {
   BwdLayout L;
   L.cap_kv = max_items(B, H, tk, jfa::kDkvTN);
   L.cap_q = max_items(B, H, tq, jfa::kDqTM);
-  L.delta = kAlign;
+  L.delta = 2 * sizeof(PlanHeader);
   L.items_kv = L.delta + align_up((size_t)tq * H * 4);
   L.items_q = L.items_kv + align_up((size_t)L.cap_kv * 16);
   L.total = L.items_q + align_up((size_t)L.cap_q * 16);
@@ -188,7 +191,7 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.B = B;
   pa.H = H;
   pa.causal = causal ? 1 : 0;
-  pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::kFwdTM, jfa::kFwdTN, 0};
+  pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::kFwdTM, jfa::kFwdTN, 0, jfa::kPlanQueues};
   hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 1, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
 
@@ -237,8 +240,8 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.B = B;
   pa.H = H;
   pa.causal = causal ? 1 : 0;
-  pa.pass[0] = {(int4*)(w + L.items_kv), (PlanHeader*)(w + L.hdr_kv), (long)L.cap_kv, jfa::kDkvTM, jfa::kDkvTN, 1};
-  pa.pass[1] = {(int4*)(w + L.items_q), (PlanHeader*)(w + L.hdr_q), (long)L.cap_q, jfa::kDqTM, jfa::kDqTN, 0};
+  pa.pass[0] = {(int4*)(w + L.items_kv), (PlanHeader*)(w + L.hdr_kv), (long)L.cap_kv, jfa::kDkvTM, jfa::kDkvTN, 1, jfa::kPlanQueues};
+  pa.pass[1] = {(int4*)(w + L.items_q), (PlanHeader*)(w + L.hdr_q), (long)L.cap_q, jfa::kDqTM, jfa::kDqTN, 0, jfa::kPlanQueues};
   hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 2, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
 
@@ -357,7 +360,7 @@ size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv,
       (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_F32))
     return 0;
   const int64_t cap = kernel == JFA_KERNEL_BWD_DKDV ? max_items(B, H, total_kv, tn) : max_items(B, H, total_q, tm);
-  return kAlign + align_up((size_t)cap * 16);
+  return sizeof(PlanHeader) + align_up((size_t)cap * 16);
 }
 
 jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D, int dtype,
@@ -368,7 +371,7 @@ jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, i
       (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_F32))
     return fail(JFA_ERR_INVALID_ARGUMENT, "invalid sizes");
   if (!q_offsets || !kv_offsets) return fail(JFA_ERR_INVALID_ARGUMENT, "offsets must not be NULL");
-  if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < kAlign)
+  if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < sizeof(PlanHeader))
     return fail(JFA_ERR_WORKSPACE, "workspace must be non-NULL, 256-byte aligned and at least 256 bytes");
   DeviceInfo* dev = nullptr;
   jfa_status s = device_info(&dev);
@@ -380,8 +383,8 @@ jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, i
   pa.B = B;
   pa.H = H;
   pa.causal = causal ? 1 : 0;
-  pa.pass[0] = {(int4*)(w + kAlign), (PlanHeader*)w, (long)((workspace_bytes - kAlign) / 16), tm, tn,
-                kernel == JFA_KERNEL_BWD_DKDV ? 1 : 0};
+  pa.pass[0] = {(int4*)(w + sizeof(PlanHeader)), (PlanHeader*)w, (long)((workspace_bytes - sizeof(PlanHeader)) / 16), tm, tn,
+                kernel == JFA_KERNEL_BWD_DKDV ? 1 : 0, jfa::kPlanQueues};
   hipError_t e = jfa::launch_plan(pa, 1, (hipStream_t)stream);
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
   return ok();

@@ -227,22 +227,70 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// Work-list header in the caller's workspace.
+// Work-list header in the caller's workspace: kMaxQueues queues stored one
+// after the other in the item array (one queue per XCD). Each queue's ticket
+// sits on its own 128-byte line, away from the read-only words, so that the
+// atomics of one queue do not serialise the others' traffic in L2.
+constexpr int kMaxQueues = 8;
 struct PlanHeader {
-  int count;    // items in the list
-  int ticket;   // next item to hand out (zeroed by the plan kernel)
-  int status;   // 0 ok, 1 list did not fit the workspace
-  int pad[13];
+  int count;                 // items in all queues
+  int status;                // 0 ok, 1 the list did not fit the workspace
+  int nq;                    // queues in use
+  int pad0;
+  int start[kMaxQueues];     // first item of each queue
+  int qcount[kMaxQueues];    // items of each queue
+  int pad1[12];
+  struct {
+    int value;               // next item of the queue to hand out (zeroed by the plan kernel)
+    int pad[31];
+  } ticket[kMaxQueues];
+  int pad2[224];
 };
-static_assert(sizeof(PlanHeader) == 64, "header is 64 bytes");
+static_assert(sizeof(PlanHeader) == 2048, "header is 2048 bytes");
 
-// Fetch the next work-list index for this workgroup (thread 0 takes a ticket).
-__device__ __forceinline__ int next_item(int* ticket, int* sh) {
-  if (threadIdx.x == 0) *sh = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Per-workgroup copy of the queue bounds plus the work-list cursor.
+struct QueueCursor {
+  int start[kMaxQueues];
+  int count[kMaxQueues];
+  int nq;
+  int item;  // broadcast slot
+};
+
+// Loads the queue bounds into LDS (call once, before the first next_item;
+// the barrier inside next_item orders it).
+__device__ __forceinline__ void load_queues(const PlanHeader* hdr, QueueCursor* qc) {
+  if (threadIdx.x < kMaxQueues) {
+    qc->start[threadIdx.x] = hdr->start[threadIdx.x];
+    qc->count[threadIdx.x] = hdr->qcount[threadIdx.x];
+  }
+  if (threadIdx.x == kMaxQueues) qc->nq = max(hdr->nq, 1);
+}
+
+// Next work item for this workgroup. Thread 0 takes tickets from its home
+// queue (the one its XCD drains) and, once that is empty, from the others in
+// turn; *q and *left live in thread 0 only (*left < 0: not started). Returns
+// -1 when every queue is empty.
+__device__ __forceinline__ int next_item(PlanHeader* hdr, QueueCursor* qc, int* q, int* left) {
+  __syncthreads();  // queue bounds loaded; every wave is done with the previous item's slot
+  if (threadIdx.x == 0) {
+    if (*left < 0) {
+      *q = (int)(blockIdx.x % (unsigned)qc->nq);
+      *left = qc->nq;
+    }
+    int it = -1;
+    while (*left > 0) {
+      const int t = __hip_atomic_fetch_add(&hdr->ticket[*q].value, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t < qc->count[*q]) {
+        it = qc->start[*q] + t;
+        break;
+      }
+      *q = *q + 1 == qc->nq ? 0 : *q + 1;
+      *left -= 1;
+    }
+    qc->item = it;
+  }
   __syncthreads();
-  const int it = *sh;
-  __syncthreads();  // every wave has read *sh before thread 0 may overwrite it
-  return it;
+  return qc->item;
 }
 
 }  // namespace jfa

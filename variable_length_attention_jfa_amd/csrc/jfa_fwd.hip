@@ -51,18 +51,19 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
   using C = FwdTiles<T, D>;
   constexpr int BM = C::BM, BN = C::BN, ES = (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-  __shared__ int sh_item;
+  __shared__ QueueCursor qcur;
   lds_t* lds = (lds_t*)smem;
   __attribute__((address_space(3))) float* bias_lds = (__attribute__((address_space(3))) float*)(lds + C::BIAS_OFF);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int H = a.H;
   const uint32_t gstride = (uint32_t)H * C::ROWB;  // bytes between consecutive tokens
-  const int n_items = a.hdr->count;
+  load_queues(a.hdr, &qcur);
+  int home_q = 0, queues_left = -1;
 
   for (;;) {
-    const int it = next_item(&a.hdr->ticket, &sh_item);
-    if (it >= n_items) break;
+    const int it = next_item(a.hdr, &qcur, &home_q, &queues_left);
+    if (it < 0) break;
     const int4 item = a.items[it];
     const int b = item.x, h = item.y, qt = item.z;
     const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;

@@ -52,7 +52,10 @@ struct PlanPass {
   long capacity;  // items that fit the workspace
   int TM, TN;     // query rows / keys per tile and per visited block
   int kv_pass;
+  int nq;         // queues (one per XCD)
 };
+
+constexpr int kPlanQueues = 8;  // MI355X: 8 XCDs
 
 struct PlanArgs {
   const int* q_off;

@@ -1,25 +1,27 @@
-// Offsets-driven, longest-first work list for the persistent kernels, and the
+// Offsets-driven, longest-first work lists for the persistent kernels, and the
 // lengths -> offsets scan.
 //
 // Short sequences must not leave compute units idle ("Jagged Flash Attention
 // (JFA)", section "Why standard FlashAttention falls short"), and the kernels
-// are persistent ("Four generations", item 3). The list is built on the GPU
-// from the offsets so that no host round trip is needed:
+// are persistent ("Four generations", item 3). The lists are built on the GPU
+// from the offsets, so no host round trip is needed:
 //
 //   tiles  : q pass  -> (b, t) with t < ceil(Lq_b / TM)
 //            kv pass -> (b, t) with t < ceil(Lk_b / TN)
 //   cost   : key blocks (q pass) or query blocks (kv pass) the tile visits
-//   order  : cost descending (costs >= kCostCap-1 share one key), then b, h, t
-//   items  : (b, h, t, cost), H per tile
+//   groups : the tiles of one (b, h); group cost = sum of its tile costs
+//   order  : groups by cost descending, then b, then h; group rank g is dealt
+//            to queue snake(g) (0..Q-1, Q-1..0, ...), one queue per XCD, so
+//            that the items sharing one (b, h)'s keys and values run on one
+//            XCD and share its L2; inside a group, tiles by cost descending,
+//            then t ascending
+//   items  : (b, h, t, cost), queues stored one after the other
 //
-// Construction is a stable counting sort done by one 1024-thread workgroup:
-// a histogram of tile keys, a descending scan of it, then tiles are ranked
-// inside their key chunk by chunk (per-wave ballots give the rank among equal
-// keys; per-wave counts in LDS give the offset of earlier waves). The item
-// position of (b, h, t) follows from the tile's rank because, inside one
-// sequence, the tiles with a given key form one contiguous run of t.
-// Everything is integer arithmetic in a fixed order, so the list is the same
-// on every run and equal to a plain sort with the same key.
+// One 1024-thread workgroup builds one list: sequences are ranked by a bitonic
+// sort of (group cost, b) in LDS; group positions inside each queue come from
+// one block-wide scan per chunk of 1024 groups, laid out so that each queue's
+// groups are contiguous in the scan. All integer arithmetic in a fixed order:
+// the list is the same on every run.
 #include "jfa_common.h"
 #include "jfa_kernels.h"
 
@@ -27,10 +29,7 @@ namespace jfa {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kCostCap = 1024;
 constexpr int kPlanMaxB = 8192;
-
-
 
 __device__ __forceinline__ int plan_tiles(int Lq, int Lk, const PlanPass& p) {
   return p.kv_pass ? cdiv(Lk, p.TN) : cdiv(Lq, p.TM);
@@ -48,7 +47,26 @@ __device__ __forceinline__ int plan_cost(int Lq, int Lk, int t, const PlanPass& 
   return nq - first_key / p.TM;
 }
 
-__device__ __forceinline__ int plan_key(int cost) { return min(cost, kCostCap - 1); }
+// Position of tile t in its group's order (cost descending, then t ascending).
+// Costs are monotone in t: non-increasing in the causal kv pass and constant
+// without the causal mask, so the order is t itself there. In the causal q
+// pass cost(t) = ceil(min((t+1)*TM, Lq, Lk) / TN) is non-decreasing: the tiles
+// with cost c are t in [floor((c-1)*TN/TM), t1) with t1 = floor(c*TN/TM) if
+// some tile reaches cost c+1 (min(Lq, Lk) > c*TN), else n. Tile t comes after
+// the n - t1 tiles of larger cost and the t - t0 tiles of equal cost before it.
+__device__ __forceinline__ int plan_pos(int Lq, int Lk, int t, int n, const PlanPass& p, int causal) {
+  const int lmin = min(Lq, Lk);
+  if (!causal || p.kv_pass || lmin == 0) return t;
+  const int c = plan_cost(Lq, Lk, t, p, causal);
+  const int t0 = ((c - 1) * p.TN) / p.TM;
+  const int t1 = lmin > c * p.TN ? min((c * p.TN) / p.TM, n) : n;
+  return (n - t1) + (t - t0);
+}
+
+__device__ __forceinline__ int snake(int g, int nq) {
+  const int r = g % (2 * nq);
+  return r < nq ? r : 2 * nq - 1 - r;
+}
 
 // Exclusive scan over the workgroup; returns the prefix, *total gets the sum.
 __device__ int block_exclusive_scan(int v, int* total, int* wsum) {
@@ -78,149 +96,122 @@ __device__ int block_exclusive_scan(int v, int* total, int* wsum) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
-  __shared__ int tile_base[kPlanMaxB + 1];
-  __shared__ int hist[kCostCap];
-  __shared__ int start[kCostCap];
-  __shared__ int running[kCostCap];
-  __shared__ unsigned char wcnt[kPlanWaves][kCostCap];
+  __shared__ unsigned long long key[kPlanMaxB];  // (inverted group cost, b), sorted ascending
+  __shared__ int lq_s[kPlanMaxB], lk_s[kPlanMaxB];  // sequence lengths
   __shared__ int wsum[2 * kPlanWaves];
+  __shared__ int qtotal[kMaxQueues], qstart[kMaxQueues], qcarry[kMaxQueues];
+  __shared__ int excl[kPlanThreads];
+  __shared__ int gbase[kPlanThreads];
+  __shared__ int2 gbh[kPlanThreads];
 
   const PlanPass p = a.pass[blockIdx.x];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int B = a.B, H = a.H;
+  const int tid = threadIdx.x;
+  const int B = a.B, H = a.H, NQ = p.nq;
+  int P = 2;
+  while (P < B) P <<= 1;
 
-  for (int i = tid; i < kCostCap; i += kPlanThreads) {
-    hist[i] = 0;
-    running[i] = 0;
-  }
-  for (int i = tid; i < kPlanWaves * kCostCap; i += kPlanThreads) (&wcnt[0][0])[i] = 0;
-
-  // 1. tile counts per sequence -> tile_base (exclusive prefix)
-  int carry = 0;
-  for (int c0 = 0; c0 < B; c0 += kPlanThreads) {
-    const int b = c0 + tid;
-    int n = 0;
+  // 1. tiles and group cost of every sequence
+  for (int b = tid; b < P; b += kPlanThreads) {
+    unsigned long long k = ~0ull;
     if (b < B) {
       const int Lq = a.q_off[b + 1] - a.q_off[b], Lk = a.kv_off[b + 1] - a.kv_off[b];
-      n = plan_tiles(Lq, Lk, p);
+      const int n = plan_tiles(Lq, Lk, p);
+      int gc = 0;
+      for (int t = 0; t < n; ++t) gc += plan_cost(Lq, Lk, t, p, a.causal);
+      lq_s[b] = Lq;
+      lk_s[b] = Lk;
+      k = ((unsigned long long)(0x7FFFFFFFu - (unsigned)gc) << 32) | (unsigned)b;
+    }
+    key[b] = k;
+  }
+  if (tid < kMaxQueues) {
+    qtotal[tid] = 0;
+    qcarry[tid] = 0;
+  }
+  __syncthreads();
+
+  // 2. bitonic sort of the P keys (ascending: cost descending, then b)
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += kPlanThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long x = key[i], y = key[ixj];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) {
+            key[i] = y;
+            key[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // 3. queue sizes (group g = rank * H + h goes to queue snake(g))
+  const int G = B * H;
+  for (int g = tid; g < G; g += kPlanThreads) {
+    const int b = (int)(key[g / H] & 0xFFFFFFFFu);
+    atomicAdd(&qtotal[snake(g, NQ)], plan_tiles(lq_s[b], lk_s[b], p));
+  }
+  __syncthreads();
+  if (tid == 0) {
+    long total = 0;
+    for (int q = 0; q < NQ; ++q) {
+      qstart[q] = (int)total;
+      total += qtotal[q];
+    }
+    const bool fits = total <= p.capacity;
+    p.hdr->count = fits ? (int)total : 0;
+    p.hdr->status = fits ? 0 : 1;
+    p.hdr->nq = NQ;
+    for (int q = 0; q < kMaxQueues; ++q) {
+      p.hdr->start[q] = (fits && q < NQ) ? qstart[q] : 0;
+      p.hdr->qcount[q] = (fits && q < NQ) ? qtotal[q] : 0;
+      p.hdr->ticket[q].value = 0;
+    }
+    wsum[0] = fits ? 0 : 1;
+  }
+  __syncthreads();
+  if (wsum[0]) return;  // the list does not fit: nothing is written (uniform branch)
+  __syncthreads();
+
+  // 4. positions inside each queue, chunk by chunk. Thread tid of a chunk
+  //    handles the i-th group of queue x in that chunk, so that each queue's
+  //    groups are contiguous in one block scan; then all threads write the
+  //    chunk's items, one item per thread at a time.
+  const int per_q = kPlanThreads / NQ;  // groups of one queue in a chunk of kPlanThreads groups
+  const int x = tid / per_q, i = tid % per_q;
+  for (int c0 = 0; c0 < G; c0 += kPlanThreads) {
+    const int g = c0 + 2 * NQ * (i >> 1) + ((i & 1) ? 2 * NQ - 1 - x : x);
+    int b = 0, n = 0;
+    if (g < G) {
+      b = (int)(key[g / H] & 0xFFFFFFFFu);
+      n = plan_tiles(lq_s[b], lk_s[b], p);
     }
     int tot;
     const int ex = block_exclusive_scan(n, &tot, wsum);
-    if (b < B) tile_base[b] = carry + ex;
-    carry += tot;
-  }
-  if (tid == 0) tile_base[B] = carry;
-  __syncthreads();
-  const int NT = tile_base[B];
-  if ((long)NT * H > p.capacity) {
-    if (tid == 0) {
-      p.hdr->count = 0;
-      p.hdr->ticket = 0;
-      p.hdr->status = 1;
-    }
-    return;
-  }
-
-  auto locate = [&](int x, int& b, int& t) {
-    int lo = 0, hi = B;  // largest b with tile_base[b] <= x
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (tile_base[mid] <= x) lo = mid; else hi = mid;
-    }
-    b = lo;
-    t = x - tile_base[lo];
-  };
-
-  // 2. histogram of keys
-  for (int x = tid; x < NT; x += kPlanThreads) {
-    int b, t;
-    locate(x, b, t);
-    const int Lq = a.q_off[b + 1] - a.q_off[b], Lk = a.kv_off[b + 1] - a.kv_off[b];
-    atomicAdd(&hist[plan_key(plan_cost(Lq, Lk, t, p, a.causal))], 1);
-  }
-  __syncthreads();
-
-  // 3. start[key] = number of tiles with a larger key
-  {
-    const int key = kCostCap - 1 - tid;  // kCostCap == kPlanThreads
-    int tot;
-    const int ex = block_exclusive_scan(hist[key], &tot, wsum);
-    start[key] = ex;
-  }
-  __syncthreads();
-
-  // 4. stable rank inside each key, chunk by chunk, then the items
-  for (int c0 = 0; c0 < NT; c0 += kPlanThreads) {
-    const int x = c0 + tid;
-    const bool valid = x < NT;
-    int b = 0, t = 0, Lq = 0, Lk = 0, cost = 0, key = -1;
-    if (valid) {
-      locate(x, b, t);
-      Lq = a.q_off[b + 1] - a.q_off[b];
-      Lk = a.kv_off[b + 1] - a.kv_off[b];
-      cost = plan_cost(Lq, Lk, t, p, a.causal);
-      key = plan_key(cost);
-    }
-    int lrank = 0, wc = 0;
-    unsigned long long rem = __ballot(valid);
-    while (rem) {
-      const int leader = __ffsll((unsigned long long)rem) - 1;
-      const int k0 = __shfl(key, leader);
-      const unsigned long long same = __ballot(valid && key == k0);
-      if (valid && key == k0) {
-        lrank = __popcll(same & ((1ull << lane) - 1ull));
-        wc = __popcll(same);
-      }
-      rem &= ~same;
-    }
-    if (valid && lrank == 0) wcnt[w][key] = (unsigned char)wc;
+    excl[tid] = ex;
     __syncthreads();
-    int pre = 0, post = 0, r = 0;
-    if (valid) {
-      for (int v = 0; v < kPlanWaves; ++v) {
-        const int cnt = wcnt[v][key];
-        if (v < w) pre += cnt;
-        if (v > w) post += cnt;
+    const int pos = ex - excl[x * per_q];
+    gbase[tid] = qstart[x] + qcarry[x] + pos;  // first item of this group in the list
+    gbh[tid] = make_int2(b, g < G ? g % H : 0);
+    __syncthreads();
+    if (i == per_q - 1) qcarry[x] += pos + n;  // last group of queue x in this chunk
+    for (int f = tid; f < tot; f += kPlanThreads) {
+      int lo = 0, hi = kPlanThreads - 1;  // last thread slot with excl <= f
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (excl[mid] <= f) lo = mid; else hi = mid - 1;
       }
-      r = running[key] + pre + lrank;
+      const int gb = gbh[lo].x, gh = gbh[lo].y;
+      const int t = f - excl[lo];
+      const int Lq = lq_s[gb], Lk = lk_s[gb];
+      const int nt = plan_tiles(Lq, Lk, p);
+      const long at = (long)gbase[lo] + plan_pos(Lq, Lk, t, nt, p, a.causal);
+      if (at >= 0 && at < p.capacity) p.items[at] = make_int4(gb, gh, t, plan_cost(Lq, Lk, t, p, a.causal));
     }
     __syncthreads();
-    if (valid && lrank == wc - 1 && post == 0) running[key] = r + 1;
-    if (valid && lrank == 0) wcnt[w][key] = 0;
-    __syncthreads();
-
-    if (valid) {
-      // run [t0, t1) of tiles of sequence b that share this key
-      const int n = plan_tiles(Lq, Lk, p);
-      int t0 = 0, t1 = n;
-      if (a.causal) {
-        int lo = 0, hi = t;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (plan_key(plan_cost(Lq, Lk, mid, p, a.causal)) == key) hi = mid; else lo = mid + 1;
-        }
-        t0 = lo;
-        lo = t + 1;
-        hi = n;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (plan_key(plan_cost(Lq, Lk, mid, p, a.causal)) != key) hi = mid; else lo = mid + 1;
-        }
-        t1 = lo;
-      }
-      const int j = t - t0, run = t1 - t0;
-      const long base = (long)H * (start[key] + (r - j)) + j;
-      const long n_items = (long)NT * H;
-      for (int h = 0; h < H; ++h) {
-        const long pos = base + (long)h * run;
-        if (pos >= 0 && pos < n_items) p.items[pos] = make_int4(b, h, t, cost);
-      }
-    }
-  }
-  if (tid == 0) {
-    p.hdr->count = NT * H;
-    p.hdr->ticket = 0;
-    p.hdr->status = 0;
   }
 }
 

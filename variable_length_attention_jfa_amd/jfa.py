@@ -28,6 +28,8 @@ KERNEL_FWD, KERNEL_BWD_DKDV, KERNEL_BWD_DQ = 0, 1, 2
 DTYPE_BF16, DTYPE_F32 = 0, 1
 BIAS_RADIUS = 128
 WORKSPACE_ALIGN = 256
+PLAN_HEADER_BYTES = 2048
+PLAN_QUEUES = 8
 
 _LIB = None
 
@@ -188,7 +190,7 @@ def tile_config(kernel: int, D: int, dtype: int = DTYPE_BF16) -> Tuple[int, int]
 
 def build_plan(q_offsets: torch.Tensor, kv_offsets: torch.Tensor, H: int, D: int, causal: bool, kernel: int,
                total_q: int, total_kv: int, dtype: int = DTYPE_BF16) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Runs the on-device work-list builder; returns (header int32[16], items int32[n, 4]) on the device."""
+    """Runs the on-device work-list builder; returns (header int32[512], items int32[n, 4]) on the device."""
     _check_tensor("q_offsets", q_offsets, torch.int32, 1)
     _check_tensor("kv_offsets", kv_offsets, torch.int32, 1)
     B = q_offsets.numel() - 1
@@ -201,8 +203,8 @@ def build_plan(q_offsets: torch.Tensor, kv_offsets: torch.Tensor, H: int, D: int
                           nbytes, _stream())
     _check("jfa_build_plan", st)
     off = wp - ws.data_ptr()
-    header = ws[off:off + 64].view(torch.int32)
-    items = ws[off + WORKSPACE_ALIGN:off + nbytes].view(torch.int32).view(-1, 4)
+    header = ws[off:off + PLAN_HEADER_BYTES].view(torch.int32)
+    items = ws[off + PLAN_HEADER_BYTES:off + nbytes].view(torch.int32).view(-1, 4)
     return header, items
 
 
