@@ -101,7 +101,8 @@ jfa_status jfa_bwd(const void* q, const void* k, const void* v, const void* out,
                    int D, int64_t total_q, int64_t total_kv, const float* bias, int causal, void* dq,
                    void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
-/* fp32 twins: identical parameters, every tensor of element type fp32. */
+/* fp32 twins: identical parameters, every tensor of element type fp32;
+ * D must be 32 or 64 (JFA_ERR_UNSUPPORTED for 128). */
 jfa_status jfa_fwd_f32(const void* q, const void* k, const void* v, const int32_t* q_offsets,
                        const int32_t* kv_offsets, int B, int H, int D, int64_t total_q, int64_t total_kv,
                        const float* bias, int causal, void* out, float* lse, void* workspace,

@@ -62,6 +62,12 @@ def test_small_workload_parity(cfg):
 @pytest.mark.parametrize("causal,bias,asym", [(False, False, False), (True, False, False), (False, True, True),
                                               (True, True, True)])
 def test_feature_grid(dtype, D, causal, bias, asym):
+    if dtype == "f32" and D == 128:
+        batch = gen.make_batch(gen.Workload("grid", 2, 1, D, dtype, causal, bias, gen.LengthDist("uniform", 1, 30)))
+        with pytest.raises(jfa.JFAError) as e:
+            _run(batch)
+        assert e.value.status == 3  # JFA_ERR_UNSUPPORTED
+        return
     base = gen.Workload("grid", 4, 2, D, dtype, causal, bias, gen.LengthDist("uniform", 1, 300),
                         gen.LengthDist("uniform", 1, 330) if asym else None, seed=100 + D)
     _check(gen.make_batch(base), label=f"grid {dtype} D={D} causal={causal} bias={bias} asym={asym}")
@@ -186,9 +192,10 @@ def test_invalid_arguments_raise():
     ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(d["q"])
     lse = torch.empty(batch.total_q, 8, dtype=torch.float32, device="cuda")
+    need = L.jfa_fwd_workspace_bytes(6, 8, batch.total_q, batch.total_kv, 64, 0)
     st = L.jfa_fwd(jfa._ptr(d["q"]), jfa._ptr(d["k"]), jfa._ptr(d["v"]), jfa._ptr(d["q_offsets"]),
                    jfa._ptr(d["kv_offsets"]), 6, 8, 64, batch.total_q, batch.total_kv, None, 0, jfa._ptr(out),
-                   jfa._ptr(lse), jfa._ptr(ws), 4096, None)
+                   jfa._ptr(lse), jfa._ptr(ws), need - 16, None)
     assert st == 2
     assert b"workspace" in L.jfa_last_error()
     # misaligned q

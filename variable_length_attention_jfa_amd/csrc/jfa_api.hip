@@ -129,7 +129,7 @@ struct FwdLayout {
 };
 FwdLayout fwd_layout(int B, int H, int64_t tq) {
   FwdLayout L;
-  L.cap = max_items(B, H, tq, jfa::kFwdTM);
+  L.cap = max_items(B, H, tq, 128);  // smallest forward tile: an upper bound for every variant
   L.hdr = 0;
   L.items = sizeof(PlanHeader);
   L.total = L.items + align_up((size_t)L.cap * 16);
@@ -174,6 +174,7 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
                     float* lse, void* ws, size_t ws_bytes, void* stream) {
   jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, bias, ws);
   if (s != JFA_OK) return s;
+  if (f32 && D > 64) return fail(JFA_ERR_UNSUPPORTED, "fp32 tensors support D = 32 or 64");
   if ((tq > 0 && (!out || !lse))) return fail(JFA_ERR_INVALID_ARGUMENT, "out/lse must not be NULL");
   if (!aligned(out, 16) || !aligned(lse, 4)) return fail(JFA_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
   const FwdLayout L = fwd_layout(B, H, tq);
@@ -191,7 +192,8 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.B = B;
   pa.H = H;
   pa.causal = causal ? 1 : 0;
-  pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::kFwdTM, jfa::kFwdTN, 0, jfa::kPlanQueues};
+  pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::fwd_tile_rows(f32, D), jfa::kFwdTN, 0,
+                jfa::kPlanQueues};
   hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 1, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
 
@@ -220,6 +222,7 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
                     size_t ws_bytes, void* stream) {
   jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, bias, ws);
   if (s != JFA_OK) return s;
+  if (f32 && D > 64) return fail(JFA_ERR_UNSUPPORTED, "fp32 tensors support D = 32 or 64");
   if (tq > 0 && (!out || !lse || !dout || !dq)) return fail(JFA_ERR_INVALID_ARGUMENT, "out/lse/dout/dq must not be NULL");
   if (tk > 0 && (!dk || !dv)) return fail(JFA_ERR_INVALID_ARGUMENT, "dk/dv must not be NULL");
   if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
@@ -279,9 +282,9 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   return ok();
 }
 
-bool tile_of(int kernel, int* tm, int* tn) {
+bool tile_of(int kernel, int D, int dtype, int* tm, int* tn) {
   switch (kernel) {
-    case JFA_KERNEL_FWD: *tm = jfa::kFwdTM; *tn = jfa::kFwdTN; return true;
+    case JFA_KERNEL_FWD: *tm = jfa::fwd_tile_rows(dtype == JFA_DTYPE_F32, D); *tn = jfa::kFwdTN; return true;
     case JFA_KERNEL_BWD_DKDV: *tm = jfa::kDkvTM; *tn = jfa::kDkvTN; return true;
     case JFA_KERNEL_BWD_DQ: *tm = jfa::kDqTM; *tn = jfa::kDqTN; return true;
     default: return false;
@@ -350,14 +353,14 @@ jfa_status jfa_tile_config(int kernel, int D, int dtype, int* tile_m, int* tile_
   if (!tile_m || !tile_n) return fail(JFA_ERR_INVALID_ARGUMENT, "tile_m/tile_n must not be NULL");
   if (!(D == 32 || D == 64 || D == 128)) return fail(JFA_ERR_INVALID_ARGUMENT, "D must be 32, 64 or 128");
   if (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_F32) return fail(JFA_ERR_INVALID_ARGUMENT, "unknown dtype");
-  if (!tile_of(kernel, tile_m, tile_n)) return fail(JFA_ERR_INVALID_ARGUMENT, "unknown kernel id %d", kernel);
+  if (!tile_of(kernel, D, dtype, tile_m, tile_n)) return fail(JFA_ERR_INVALID_ARGUMENT, "unknown kernel id %d", kernel);
   return ok();
 }
 
 size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, int D, int dtype, int kernel) {
   int tm, tn;
-  if (!valid_sizes(B, H, total_q, total_kv, D) || !tile_of(kernel, &tm, &tn) ||
-      (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_F32))
+  if (!valid_sizes(B, H, total_q, total_kv, D) || (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_F32) ||
+      !tile_of(kernel, D, dtype, &tm, &tn))
     return 0;
   const int64_t cap = kernel == JFA_KERNEL_BWD_DKDV ? max_items(B, H, total_kv, tn) : max_items(B, H, total_q, tm);
   return sizeof(PlanHeader) + align_up((size_t)cap * 16);
@@ -366,10 +369,10 @@ size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv,
 jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D, int dtype,
                           int causal, int kernel, void* workspace, size_t workspace_bytes, void* stream) {
   int tm, tn;
-  if (!tile_of(kernel, &tm, &tn)) return fail(JFA_ERR_INVALID_ARGUMENT, "unknown kernel id %d", kernel);
   if (B < 0 || B > JFA_MAX_BATCH || H < 1 || !(D == 32 || D == 64 || D == 128) ||
       (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_F32))
     return fail(JFA_ERR_INVALID_ARGUMENT, "invalid sizes");
+  if (!tile_of(kernel, D, dtype, &tm, &tn)) return fail(JFA_ERR_INVALID_ARGUMENT, "unknown kernel id %d", kernel);
   if (!q_offsets || !kv_offsets) return fail(JFA_ERR_INVALID_ARGUMENT, "offsets must not be NULL");
   if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < sizeof(PlanHeader))
     return fail(JFA_ERR_WORKSPACE, "workspace must be non-NULL, 256-byte aligned and at least 256 bytes");

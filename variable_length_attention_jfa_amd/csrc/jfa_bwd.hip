@@ -242,7 +242,7 @@ struct DqTiles {
 };
 
 template <typename T, int D, bool BIAS>
-__global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_dq_kernel(BwdArgs a) {
   using C = DqTiles<T, D>;
   constexpr int BM = C::BM, BN = C::BN, ES = (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -269,8 +269,6 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dq_ke
     const size_t qrow = ((size_t)q0 * H + h) * C::ROWB, krow = ((size_t)k0 * H + h) * C::ROWB;
     const View qv = seq_view((const char*)a.q + qrow, Lq, gstride, C::ROWB);
     const View dov = seq_view((const char*)a.dout + qrow, Lq, gstride, C::ROWB);
-    const View kv = seq_view((const char*)a.k + krow, Lk, gstride, C::ROWB);
-    const View vv = seq_view((const char*)a.v + krow, Lk, gstride, C::ROWB);
     const View lv = seq_view(a.lse + (size_t)q0 * H + h, Lq, (uint32_t)H * 4, 4);
     const View dlv = seq_view(a.delta + (size_t)q0 * H + h, Lq, (uint32_t)H * 4, 4);
 
@@ -290,30 +288,17 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dq_ke
     const float lse2 = ld4f(lv, (uint32_t)qi * H * 4) * kLog2e;
     const float dlt = ld4f(dlv, (uint32_t)qi * H * 4);
 
-    i32x4 kr[C::CPT], vr[C::CPT];
-    auto gload = [&](int j) {
-#pragma unroll
-      for (int c = 0; c < C::CPT; ++c) {
-        const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
-        const uint32_t off = (uint32_t)(j * BN + row) * gstride + col * 16;
-        kr[c] = ld16(kv, off);
-        vr[c] = ld16(vv, off);
-      }
+    // K/V blocks through a two-stage LDS ring filled by direct loads: block
+    // j+1 is requested while block j is computed.
+    const DmaView kd = dma_view((const char*)a.k + krow, Lk, gstride, C::ROWB);
+    const DmaView vd = dma_view((const char*)a.v + krow, Lk, gstride, C::ROWB);
+    auto issue = [&](int j) {
+      lds_t* st = lds + (j & 1) * C::STAGE;
+      dma_tile<T, D, BN, 4>(kd, gstride, j * BN, st, w, lane);
+      dma_tile<T, D, BN, 4>(vd, gstride, j * BN, st + C::KTILE, w, lane);
     };
-    auto swrite = [&](int s) {
-#pragma unroll
-      for (int c = 0; c < C::CPT; ++c) {
-        const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
-        const int o = C::TL::chunk(row, col);
-        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + o) = kr[c];
-        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + C::KTILE + o) = vr[c];
-      }
-    };
-    if (n_kv > 0) {
-      gload(0);
-      swrite(0);
-    }
-    wait_vmem();
+    if (n_kv > 0) issue(0);
+    wait_vmem();  // Q, dO, lse, Delta and the first K/V block have landed
     __syncthreads();
 
     f32x16 dq[D / 32];
@@ -322,7 +307,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dq_ke
 
     for (int j = 0; j < n_kv; ++j) {
       const int s = j & 1;
-      if (j + 1 < n_kv) gload(j + 1);
+      if (j + 1 < n_kv) issue(j + 1);
       const int key0 = j * BN;
       const bool active = wave_on && (!a.causal || key0 <= wr0 + 31);
       if (active) {
@@ -363,7 +348,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dq_ke
           for (int db = 0; db < D / 32; ++db) mma(dq[db], tfrag<D>(kt, 16 * kc, 32 * db, lane, (T*)0), sf);
         }
       }
-      if (j + 1 < n_kv) swrite((j + 1) & 1);
+      wait_vmem();
       __syncthreads();
     }
 
@@ -420,7 +405,7 @@ static hipError_t launch_dq_t(const BwdArgs& a, long max_items, int num_cus, hip
     if (F32) {                                            \
       if ((D) == 32) { using T = float; constexpr int DD = 32; return CALL; }  \
       if ((D) == 64) { using T = float; constexpr int DD = 64; return CALL; }  \
-      { using T = float; constexpr int DD = 128; return CALL; }                \
+      return hipErrorInvalidValue; /* fp32 with D = 128 is rejected on the host */ \
     }                                                     \
     if ((D) == 32) { using T = bf16; constexpr int DD = 32; return CALL; }     \
     if ((D) == 64) { using T = bf16; constexpr int DD = 64; return CALL; }     \

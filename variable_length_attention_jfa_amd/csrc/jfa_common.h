@@ -217,6 +217,77 @@ __device__ __forceinline__ void store4(const View& v, uint32_t off, float a, flo
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// ---------------------------------------------------------------------------
+// Direct global -> LDS tile loads. One wave instruction moves 64 x 16 bytes
+// into 1 KB of LDS, lane l landing at byte 16*l (gfx950 buffer_load_dwordx4
+// with the LDS bit; out-of-range lanes write zeros). The tile layout is
+// permuted (Tile::swz), so each lane fetches the global 16-byte piece whose
+// permuted position is its LDS slot.
+//
+// The instruction is issued from inline assembly on purpose: the compiler
+// cannot tell which LDS stage a direct load writes, so for its own loads it
+// waits for every outstanding one before any LDS read, which would make the
+// prefetch ring synchronous. Here the kernels order the ring themselves with
+// explicit vmcnt waits and barriers. M0 carries the LDS address; nothing else
+// in these kernels uses M0.
+struct DmaView {
+  i32x4 w;  // buffer resource words: base, stride 0, record count, format
+};
+
+__device__ __forceinline__ DmaView dma_view(const void* base, int rows, uint32_t row_stride, uint32_t row_bytes) {
+  const uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * row_stride + row_bytes : 0u;
+  const unsigned long long a = (unsigned long long)base;
+  DmaView v;
+  v.w[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  v.w[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  v.w[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  v.w[3] = 0x00020000;
+  return v;
+}
+
+__device__ __forceinline__ void dma16(const DmaView& v, const lds_t* dst, uint32_t voff) {
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)dst);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(v.w)
+               : "memory", "m0");
+}
+
+// Rows row0 .. row0+ROWS-1 of the view into an LDS tile; the waves split the
+// tile's 1 KB blocks.
+template <typename T, int D, int ROWS, int WAVES>
+__device__ __forceinline__ void dma_tile(const DmaView& v, uint32_t gstride, int row0, lds_t* tile, int wave, int lane) {
+  using TL = Tile<T, D>;
+  constexpr int NBLK = ROWS * TL::ROWB / 1024;
+  static_assert(NBLK % WAVES == 0 || NBLK < WAVES, "tile blocks divide the waves (or one block per wave)");
+#pragma unroll
+  for (int k = wave; k < NBLK; k += WAVES) {
+    const int P = k * 1024 + 16 * lane;
+    const int r = P / TL::ROWB, pc = (P % TL::ROWB) >> 4;
+    const uint32_t goff = (uint32_t)(row0 + r) * gstride + (uint32_t)((pc ^ TL::swz(r)) << 4);
+    dma16(v, tile + k * 1024, goff);
+  }
+}
+template <typename T, int D, int ROWS, int WAVES>
+constexpr int dma_loads_per_wave() {
+  return ROWS * Tile<T, D>::ROWB / 1024 >= WAVES ? ROWS * Tile<T, D>::ROWB / 1024 / WAVES : 1;
+}
+
+// s_waitcnt with vmcnt = n (0..63), expcnt and lgkmcnt left alone. The count
+// must be a compile-time constant, so small runtime values are dispatched.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+template <int STEP, int MAXK>
+__device__ __forceinline__ void wait_vmcnt_tiles(int k) {  // wait until at most k*STEP loads remain
+  if constexpr (MAXK <= 0) {
+    wait_vmcnt_c<0>();
+  } else {
+    if (k >= MAXK) wait_vmcnt_c<MAXK * STEP>();
+    else wait_vmcnt_tiles<STEP, MAXK - 1>(k);
+  }
+}
+
 // Wait until every outstanding vector-memory load of this wave has landed.
 // Used once per work item after the register-resident operand fragments are
 // loaded: it tells the compiler's wait-count tracking that nothing older than

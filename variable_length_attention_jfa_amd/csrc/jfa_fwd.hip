@@ -43,7 +43,7 @@ struct FwdTiles {
   static constexpr int BIAS_OFF = 2 * STAGE;
   static constexpr int LDS = BIAS_OFF + 1040;
   static_assert((BN * CPR) % THREADS == 0, "tile pieces divide the workgroup");
-  static_assert(BM == kFwdTM && BN == kFwdTN, "tile shape published to the planner");
+  static_assert(BM == FwdRows<T, D>::value && BN == kFwdTN, "tile shape published to the planner");
 };
 
 template <typename T, int D, bool BIAS>
@@ -261,12 +261,17 @@ static hipError_t launch_fwd_t(const FwdArgs& a, bool bias, long max_items, int 
   return hipGetLastError();
 }
 
+int fwd_tile_rows(bool f32, int D) {
+  if (f32) return D == 32 ? FwdRows<float, 32>::value : FwdRows<float, 64>::value;
+  return D == 32 ? FwdRows<bf16, 32>::value : (D == 64 ? FwdRows<bf16, 64>::value : FwdRows<bf16, 128>::value);
+}
+
 // Host-side entry used by the C-ABI layer.
 hipError_t launch_fwd(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
   if (f32) {
     if (D == 32) return launch_fwd_t<float, 32>(a, bias, max_items, num_cus, st);
     if (D == 64) return launch_fwd_t<float, 64>(a, bias, max_items, num_cus, st);
-    return launch_fwd_t<float, 128>(a, bias, max_items, num_cus, st);
+    return hipErrorInvalidValue;  // fp32 with D = 128 is rejected on the host
   }
   if (D == 32) return launch_fwd_t<bf16, 32>(a, bias, max_items, num_cus, st);
   if (D == 64) return launch_fwd_t<bf16, 64>(a, bias, max_items, num_cus, st);

@@ -64,8 +64,12 @@ struct PlanArgs {
   PlanPass pass[2];
 };
 
-// Tile shapes (query rows x keys) of each kernel.
-constexpr int kFwdTM = 128, kFwdTN = 64;
+// Tile shapes (query rows x keys) of each kernel. The forward's waves per
+// workgroup (32 query rows each) depend on the element type and D.
+template <typename T, int D> struct FwdWaves { static constexpr int value = 4; };
+template <typename T, int D> struct FwdRows { static constexpr int value = 32 * FwdWaves<T, D>::value; };
+constexpr int kFwdTN = 64;
+int fwd_tile_rows(bool f32, int D);
 constexpr int kDkvTM = 64, kDkvTN = 128;
 constexpr int kDqTM = 128, kDqTN = 64;
 
