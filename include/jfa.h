@@ -23,7 +23,8 @@
  *                                            non-decreasing, offsets[B] = total
  *   bias                  [H, 257]           fp32, or NULL for no bias
  * T is bf16 for jfa_fwd / jfa_bwd and fp32 for jfa_fwd_f32 / jfa_bwd_f32.
- * Accumulation is fp32 in every variant. D must be 32, 64 or 128.
+ * Accumulation is fp32 in every variant. D must be 32, 64 or 128; H must be
+ * 1 .. JFA_MAX_HEADS.
  * Each sequence's slice of one tensor (length * H * D * sizeof(T)) must be
  * below 4 GiB. kv_offsets may alias q_offsets.
  *
@@ -62,6 +63,7 @@ typedef enum {
 
 #define JFA_BIAS_RADIUS 128 /* bias table is [H][2 * JFA_BIAS_RADIUS + 1] */
 #define JFA_MAX_BATCH 8192  /* largest B accepted by one call */
+#define JFA_MAX_HEADS 65535 /* largest H accepted by one call */
 #define JFA_PLAN_QUEUES 8   /* work-list queues, one per XCD */
 #define JFA_PLAN_HEADER_BYTES 2048
 

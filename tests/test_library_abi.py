@@ -34,7 +34,10 @@ def test_host_only_queries(L):
     assert L.jfa_fwd_workspace_bytes(4, 2, 153, 153, 32, 0) > 0
     assert L.jfa_fwd_workspace_bytes(4, 2, 153, 153, 48, 0) == 0
     assert L.jfa_bwd_workspace_bytes(-1, 2, 10, 10, 64, 0) == 0
-    assert L.jfa_bwd_workspace_bytes(64, 8, 31132, 31132, 64, 0) > 31132 * 8 * 4
+    assert L.jfa_bwd_workspace_bytes(64, 8, 31132, 31132, 64, 0) > 31132 * 8 * 8
+    assert L.jfa_fwd_workspace_bytes(4, 65535, 10, 10, 64, 0) > 0
+    assert L.jfa_fwd_workspace_bytes(4, 65536, 10, 10, 64, 0) == 0  # beyond JFA_MAX_HEADS
+    assert L.jfa_bwd_workspace_bytes(4, 0, 10, 10, 64, 0) == 0
     for kernel in (jfa.KERNEL_FWD, jfa.KERNEL_BWD_DKDV, jfa.KERNEL_BWD_DQ):
         tm, tn = jfa.tile_config(kernel, 128)
         assert tm % 32 == 0 and tn % 32 == 0 and tm > 0 and tn > 0

@@ -116,7 +116,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool valid_sizes(int B, int H, int64_t tq, int64_t tk, int D) {
-  return B >= 0 && B <= JFA_MAX_BATCH && H >= 1 && tq >= 0 && tk >= 0 && tq < (1LL << 31) && tk < (1LL << 31) &&
+  return B >= 0 && B <= JFA_MAX_BATCH && H >= 1 && H <= JFA_MAX_HEADS && tq >= 0 && tk >= 0 && tq < (1LL << 31) && tk < (1LL << 31) &&
          (D == 32 || D == 64 || D == 128);
 }
 
@@ -137,15 +137,15 @@ FwdLayout fwd_layout(int B, int H, int64_t tq) {
 }
 
 struct BwdLayout {
-  size_t hdr_kv = 0, hdr_q = sizeof(PlanHeader), delta = 0, items_kv = 0, items_q = 0, total = 0;
+  size_t hdr_kv = 0, hdr_q = sizeof(PlanHeader), rowc = 0, items_kv = 0, items_q = 0, total = 0;
   int64_t cap_kv = 0, cap_q = 0;
 };
 BwdLayout bwd_layout(int B, int H, int64_t tq, int64_t tk) {
   BwdLayout L;
   L.cap_kv = max_items(B, H, tk, jfa::kDkvTN);
   L.cap_q = max_items(B, H, tq, jfa::kDqTM);
-  L.delta = 2 * sizeof(PlanHeader);
-  L.items_kv = L.delta + align_up((size_t)tq * H * 4);
+  L.rowc = 2 * sizeof(PlanHeader);
+  L.items_kv = L.rowc + align_up((size_t)tq * H * 8);
   L.items_q = L.items_kv + align_up((size_t)L.cap_kv * 16);
   L.total = L.items_q + align_up((size_t)L.cap_q * 16);
   return L;
@@ -156,8 +156,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 jfa_status check_common(const void* q, const void* k, const void* v, const int32_t* qo, const int32_t* ko, int B,
                         int H, int D, int64_t tq, int64_t tk, const float* bias, const void* ws) {
   if (!valid_sizes(B, H, tq, tk, D))
-    return fail(JFA_ERR_INVALID_ARGUMENT, "invalid sizes: B=%d (0..%d), H=%d (>=1), D=%d (32/64/128), total_q=%lld, total_kv=%lld",
-                B, JFA_MAX_BATCH, H, D, (long long)tq, (long long)tk);
+    return fail(JFA_ERR_INVALID_ARGUMENT, "invalid sizes: B=%d (0..%d), H=%d (1..%d), D=%d (32/64/128), total_q=%lld, total_kv=%lld",
+                B, JFA_MAX_BATCH, H, JFA_MAX_HEADS, D, (long long)tq, (long long)tk);
   if (!qo || !ko) return fail(JFA_ERR_INVALID_ARGUMENT, "offsets must not be NULL");
   if ((tq > 0 && !q) || (tk > 0 && (!k || !v)))
     return fail(JFA_ERR_INVALID_ARGUMENT, "q/k/v must not be NULL");
@@ -243,7 +243,7 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.B = B;
   pa.H = H;
   pa.causal = causal ? 1 : 0;
-  pa.pass[0] = {(int4*)(w + L.items_kv), (PlanHeader*)(w + L.hdr_kv), (long)L.cap_kv, jfa::kDkvTM, jfa::kDkvTN, 1, jfa::kPlanQueues};
+  pa.pass[0] = {(int4*)(w + L.items_kv), (PlanHeader*)(w + L.hdr_kv), (long)L.cap_kv, jfa::dkv_tile_rows(f32, D), jfa::kDkvTN, 1, jfa::kPlanQueues};
   pa.pass[1] = {(int4*)(w + L.items_q), (PlanHeader*)(w + L.hdr_q), (long)L.cap_q, jfa::kDqTM, jfa::kDqTN, 0, jfa::kPlanQueues};
   hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 2, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
@@ -261,12 +261,12 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.delta = (float*)(w + L.delta);
+  a.rowc = (float2*)(w + L.rowc);
   a.H = H;
   a.causal = causal ? 1 : 0;
   a.scale = (float)(1.0 / std::sqrt((double)D));
   a.scale2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
-  a.rows = (long)tq * H;
+  a.tq = (long)tq;
   jfa::BwdArgs a_kv = a, a_q = a;
   a_kv.items = (const int4*)(w + L.items_kv);
   a_kv.hdr = (PlanHeader*)(w + L.hdr_kv);
@@ -285,7 +285,7 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
 bool tile_of(int kernel, int D, int dtype, int* tm, int* tn) {
   switch (kernel) {
     case JFA_KERNEL_FWD: *tm = jfa::fwd_tile_rows(dtype == JFA_DTYPE_F32, D); *tn = jfa::kFwdTN; return true;
-    case JFA_KERNEL_BWD_DKDV: *tm = jfa::kDkvTM; *tn = jfa::kDkvTN; return true;
+    case JFA_KERNEL_BWD_DKDV: *tm = jfa::dkv_tile_rows(dtype == JFA_DTYPE_F32, D); *tn = jfa::kDkvTN; return true;
     case JFA_KERNEL_BWD_DQ: *tm = jfa::kDqTM; *tn = jfa::kDqTN; return true;
     default: return false;
   }

@@ -8,11 +8,17 @@
 //   dS = P * (dP - Delta), dQ = dS K / sqrt(D), dK = dS^T Q / sqrt(D),
 // with P recomputed from the forward's log-sum-exp: P = exp(S - lse).
 //
-//  * jfa_delta_kernel : Delta per (token, head), one pass over O and dO.
-//  * jfa_dkdv_kernel  : item = (b, h, 128-key tile); each wave owns 32 keys
-//                       (K, V fragments in VGPRs) and walks 64-row query
-//                       blocks staged in LDS; dK, dV stay in registers and
-//                       are stored once.
+//  * jfa_delta_kernel : Delta per (token, head), one pass over O and dO, stored
+//                       as a pair with lse * log2(e) so that one 8-byte load
+//                       gives a row's two softmax constants.
+//  * jfa_dkdv_kernel  : item = (b, h, 128-key tile), 8 waves in 4 pairs; each
+//                       pair owns 32 keys. The score wave of a pair keeps K
+//                       of its keys in VGPRs, turns each 32-row query block
+//                       into P and accumulates dV = P^T dO; the gradient wave
+//                       keeps V, takes P through LDS one block behind, and
+//                       computes dP, dS and dK = dS^T Q. Query blocks stream
+//                       through a 4-slot LDS ring, staged in registers two
+//                       blocks ahead.
 //  * jfa_dq_kernel    : item = (b, h, 128-row query tile); each wave owns 32
 //                       queries (Q, dO fragments in VGPRs) and walks 64-key
 //                       blocks staged in LDS; dQ is stored once.
@@ -30,50 +36,366 @@ namespace jfa {
 
 // ---------------------------------------------------------------------------
 template <typename T, int D>
+struct DeltaShape {
+  static constexpr int ROWB = D * (int)sizeof(T), TPR = ROWB / 16;  // threads per row
+  static constexpr int RPP = 256 / TPR;                               // rows per pass of the block
+  static constexpr int PASSES = 4;                                    // rows per thread, loads in flight together
+  static constexpr int RPB = RPP * PASSES;                            // rows per block
+};
+
+// rows = (token, head) pairs in memory order: reads and writes both stream.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void jfa_delta_kernel(BwdArgs a) {
-  constexpr int ROWB = D * (int)sizeof(T), TPR = ROWB / 16, RPB = 256 / TPR;
-  const long row = (long)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int part = threadIdx.x % TPR;
-  float acc = 0.f;
-  if (row < a.rows) {
-    const i32x4 o = *(const i32x4*)((const char*)a.out + row * ROWB + part * 16);
-    const i32x4 d = *(const i32x4*)((const char*)a.dout + row * ROWB + part * 16);
-    if (sizeof(T) == 2) {
-      const bf16x8 o8 = __builtin_bit_cast(bf16x8, o), d8 = __builtin_bit_cast(bf16x8, d);
+  using S = DeltaShape<T, D>;
+  const long rows = a.tq * a.H;
+  const int part = threadIdx.x % S::TPR;
+  const long r0 = (long)blockIdx.x * S::RPB + threadIdx.x / S::TPR;
+  i32x4 o[S::PASSES], d[S::PASSES];
+  float l[S::PASSES];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += (float)o8[e] * (float)d8[e];
-    } else {
-      const f32x4 o4 = __builtin_bit_cast(f32x4, o), d4 = __builtin_bit_cast(f32x4, d);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc += o4[e] * d4[e];
+  for (int k = 0; k < S::PASSES; ++k) {
+    const long row = r0 + k * S::RPP;
+    o[k] = d[k] = (i32x4){};
+    l[k] = 0.f;
+    if (row < rows) {
+      o[k] = *(const i32x4*)((const char*)a.out + row * S::ROWB + part * 16);
+      d[k] = *(const i32x4*)((const char*)a.dout + row * S::ROWB + part * 16);
+      if (part == 0) l[k] = a.lse[row];
     }
   }
 #pragma unroll
-  for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
-  if (row < a.rows && part == 0) a.delta[row] = acc;
+  for (int k = 0; k < S::PASSES; ++k) {
+    float acc = 0.f;
+    if (sizeof(T) == 2) {
+      const bf16x8 o8 = __builtin_bit_cast(bf16x8, o[k]), d8 = __builtin_bit_cast(bf16x8, d[k]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)o8[e] * (float)d8[e];
+    } else {
+      const f32x4 o4 = __builtin_bit_cast(f32x4, o[k]), d4 = __builtin_bit_cast(f32x4, d[k]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc += o4[e] * d4[e];
+    }
+#pragma unroll
+    for (int s = S::TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
+    const long row = r0 + k * S::RPP;
+    if (row < rows && part == 0) a.rowc[row] = make_float2(l[k] * kLog2e, acc);
+  }
 }
 
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct DkvTiles {
+  static constexpr int PAIRS = 4;           // 32-key slices per item
+  static constexpr int BNK = 32 * PAIRS;    // keys per item
+  static constexpr int BMQ = 32;            // query rows per staged block
+  static constexpr int NSLOT = 4;           // score waves on block j, gradient waves on j-1, loads for j+1, j+2
+  static constexpr int WAVES = 2 * PAIRS;
+  static constexpr int THREADS = 64 * WAVES;
+  using TL = Tile<T, D>;
+  static constexpr int ROWB = TL::ROWB;
+  static constexpr int QTILE = BMQ * ROWB;  // Q (or dO) rows of one block
+  static constexpr int QBLK = QTILE / 1024; // 1 KB load instructions per tile
+  static constexpr int RCOFF = 2 * QTILE;   // (lse2, Delta) of the block's rows
+  static constexpr int SLOT = 2 * QTILE + BMQ * 8;
+  static constexpr int NQC = QTILE / 16;    // 16-byte pieces per tile
+  static constexpr int NCH = (2 * NQC + THREADS - 1) / THREADS;  // Q and dO pieces per thread
+  static constexpr int PBUF = NSLOT * SLOT;  // [block parity][pair] fp32 P of a 32 x 32 block, lane order
+  static constexpr int PBLK = 64 * 64;       // 64 lanes x 16 floats
+  static constexpr int PBUF_BYTES = 2 * PAIRS * PBLK;
+  static constexpr int BIAS_OFF = PBUF + PBUF_BYTES;
+  static constexpr int LDS = BIAS_OFF + 1040;
+  static_assert(BMQ <= THREADS, "row constants: one row per thread");
+  static_assert(BMQ == kDkvTM && BNK == kDkvTN, "tile shape published to the planner");
+};
+
+// State of one dK/dV work item, identical in every wave of the workgroup.
+struct DkvItem {
+  int b, h, Lq, Lk, kw_base, qb0, nblk;
+  const char* qbase;
+  const char* dobase;
+  const float2* rcbase;
+  size_t krow;
+};
+
+template <typename T, int D>
+__device__ __forceinline__ bool dkv_begin(const BwdArgs& a, QueueCursor* qc, int* home_q, int* left, DkvItem& it) {
+  using C = DkvTiles<T, D>;
+  const int i = next_item(a.hdr, qc, home_q, left);
+  if (i < 0) return false;
+  const int4 item = a.items[i];
+  it.b = uni(item.x);
+  it.h = uni(item.y);
+  const int q0 = uni(a.q_off[it.b]), k0 = uni(a.kv_off[it.b]);
+  it.Lq = uni(a.q_off[it.b + 1]) - q0;
+  it.Lk = uni(a.kv_off[it.b + 1]) - k0;
+  it.kw_base = uni(item.z) * C::BNK;
+  const int nq = cdiv(it.Lq, C::BMQ);
+  it.qb0 = a.causal ? (it.kw_base >= it.Lq ? nq : it.kw_base / C::BMQ) : 0;
+  it.nblk = nq - it.qb0;
+  const size_t qrow = ((size_t)q0 * a.H + it.h) * C::ROWB;
+  it.qbase = uni((const char*)a.q + qrow);
+  it.dobase = uni((const char*)a.dout + qrow);
+  it.rcbase = uni(a.rowc + (size_t)q0 * a.H + it.h);
+  it.krow = ((size_t)k0 * a.H + it.h) * C::ROWB;
+  return true;
+}
+
+// Query block jb (rows (qb0 + jb) * BMQ ...) staged through registers: the
+// global loads are issued before a step's compute and written to ring slot
+// jb % NSLOT after it, so their latency hides behind the compute.
+template <typename T, int D>
+struct DkvStage {
+  i32x4 c[DkvTiles<T, D>::NCH];
+  i32x2 rc;
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void dkv_gload(const DkvItem& it, int jb, uint32_t gstride, int H, int tid, DkvStage<T, D>& st) {
+  using C = DkvTiles<T, D>;
+  const int r0 = (it.qb0 + jb) * C::BMQ;
+  const int rows = min(C::BMQ, it.Lq - r0);
+  const View qv = seq_view(it.qbase + (size_t)r0 * gstride, rows, gstride, C::ROWB);
+  const View dv = seq_view(it.dobase + (size_t)r0 * gstride, rows, gstride, C::ROWB);
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) {
+    const int x = tid + C::THREADS * c;
+    if (x < 2 * C::NQC) {
+      const int y = x % C::NQC, row = y / C::TL::CPR, col = y % C::TL::CPR;
+      st.c[c] = ld16(x < C::NQC ? qv : dv, (uint32_t)row * gstride + col * 16);
+    }
+  }
+  if (tid < C::BMQ) st.rc = ld8(seq_view(it.rcbase + (size_t)r0 * H, rows, 8 * H, 8), 8 * H * tid);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void dkv_swrite(int jb, int tid, const DkvStage<T, D>& st, lds_t* lds) {
+  using C = DkvTiles<T, D>;
+  lds_t* sl = lds + (jb % C::NSLOT) * C::SLOT;
+#pragma unroll
+  for (int c = 0; c < C::NCH; ++c) {
+    const int x = tid + C::THREADS * c;
+    if (x < 2 * C::NQC) {
+      const int y = x % C::NQC, row = y / C::TL::CPR, col = y % C::TL::CPR;
+      *(__attribute__((address_space(3))) i32x4*)(sl + (x < C::NQC ? 0 : C::QTILE) + C::TL::chunk(row, col)) = st.c[c];
+    }
+  }
+  if (tid < C::BMQ) *(__attribute__((address_space(3))) i32x2*)(sl + C::RCOFF + 8 * tid) = st.rc;
+}
+
+// Blocks 0 and 1 of an item, both loads in flight together.
+template <typename T, int D>
+__device__ __forceinline__ void dkv_prologue(const DkvItem& it, uint32_t gstride, int H, int tid, lds_t* lds) {
+  DkvStage<T, D> s0, s1;
+  if (it.nblk > 0) dkv_gload<T, D>(it, 0, gstride, H, tid, s0);
+  if (it.nblk > 1) dkv_gload<T, D>(it, 1, gstride, H, tid, s1);
+  if (it.nblk > 0) dkv_swrite<T, D>(0, tid, s0, lds);
+  if (it.nblk > 1) dkv_swrite<T, D>(1, tid, s1, lds);
+}
+
+// Blocks whose queries can see some key of the slice starting at kw0.
+__device__ __forceinline__ bool dkv_active(int qs0, int kw0, int Lk, int causal) {
+  return kw0 < Lk && (!causal || qs0 + 31 >= kw0);
+}
+
+template <typename T, int D, bool BIAS>
+__device__ __forceinline__ void dkv_score_role(const BwdArgs& a, lds_t* lds, QueueCursor* qc) {
+  using C = DkvTiles<T, D>;
+  constexpr int BMQ = C::BMQ, ES = (int)sizeof(T);
+  __attribute__((address_space(3))) float* bias_lds = (__attribute__((address_space(3))) float*)(lds + C::BIAS_OFF);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: views and loops stay scalar
+  const int pair = w;
+  const uint32_t gstride = (uint32_t)a.H * C::ROWB;
+  int home_q = 0, left = -1;
+  DkvItem it;
+  DkvStage<T, D> stg;
+  while (dkv_begin<T, D>(a, qc, &home_q, &left, it)) {
+    if (BIAS) {  // read by the score waves only, which load it themselves
+      for (int i = tid; i < kBiasLen; i += 64 * C::PAIRS) bias_lds[i] = a.bias[it.h * kBiasLen + i] * kLog2e;
+    }
+    const int kw0 = it.kw_base + 32 * pair, kj = kw0 + l32;
+    const View kv = seq_view((const char*)a.k + it.krow + (size_t)kw0 * gstride, max(0, min(32, it.Lk - kw0)), gstride, C::ROWB);
+    Frag<T> kf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) kf[kk] = gfrag(kv, (uint32_t)l32 * gstride + (16 * kk + 8 * g) * ES, (T*)0);
+    f32x16 dv[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dv[db] = (f32x16){};
+    dkv_prologue<T, D>(it, gstride, a.H, tid, lds);
+    wait_vmem();  // K fragments in: no wait for them inside the loop
+    __syncthreads();
+
+    for (int jb = 0; jb <= it.nblk; ++jb) {
+      if (jb + 2 < it.nblk) dkv_gload<T, D>(it, jb + 2, gstride, a.H, tid, stg);
+      const int qs0 = (it.qb0 + jb) * BMQ;
+      if (jb < it.nblk && dkv_active(qs0, kw0, it.Lk, a.causal)) {
+        const bool masked = a.causal && qs0 < kw0 + 31;
+        const lds_t* qt = lds + (jb % C::NSLOT) * C::SLOT;
+        const __attribute__((address_space(3))) float* rc = (const __attribute__((address_space(3))) float*)(qt + C::RCOFF);
+        // S = Q K^T (lane = key kj, element i = query qs0 + res_row(i, g))
+        f32x16 sc = (f32x16){};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) mma(sc, lfrag<D>(qt, l32, 16 * kk + 8 * g, (T*)0), kf[kk]);
+        // P = exp2(S * scale * log2(e) - lse2 (+ bias)), zero above the diagonal
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = res_row(i, g);
+          const int qi = qs0 + r;
+          float x = sc[i] * a.scale2 - rc[2 * r];
+          if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+          float p = __builtin_amdgcn_exp2f(x);
+          if (masked && kj > qi) p = 0.f;
+          sc[i] = p;
+        }
+        // handed to the gradient wave of the pair in fp32, lane order
+        lds_t* pb = lds + C::PBUF + ((jb & 1) * C::PAIRS + pair) * C::PBLK;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *(__attribute__((address_space(3))) f32x4*)(pb + 1024 * e + 16 * lane) =
+              (f32x4){sc[4 * e], sc[4 * e + 1], sc[4 * e + 2], sc[4 * e + 3]};
+        // dV^T += dO^T P^T
+        const lds_t* dot = qt + C::QTILE;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const Frag<T> pf = rfrag(sc, c, (T*)0);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) mma(dv[db], tfrag<D>(dot, 16 * c, 32 * db, lane, (T*)0), pf);
+        }
+      }
+      if (jb + 2 < it.nblk) dkv_swrite<T, D>(jb + 2, tid, stg, lds);
+      __syncthreads();
+    }
+
+    // dV^T: lane holds rows d = 32db + res_row(i,g) of key kj.
+    if (kw0 < it.Lk) {
+      const View dvv = seq_view((char*)a.dv + it.krow + (size_t)kw0 * gstride, min(32, it.Lk - kw0), gstride, C::ROWB);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = 32 * db + 8 * r + 4 * g;
+          store4(dvv, (uint32_t)l32 * gstride + d * ES, dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2],
+                 dv[db][4 * r + 3], (T*)0);
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void dkv_grad_role(const BwdArgs& a, lds_t* lds, QueueCursor* qc) {
+  using C = DkvTiles<T, D>;
+  constexpr int BMQ = C::BMQ, ES = (int)sizeof(T);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = w - C::PAIRS;
+  const uint32_t gstride = (uint32_t)a.H * C::ROWB;
+  int home_q = 0, left = -1;
+  DkvItem it;
+  DkvStage<T, D> stg;
+  while (dkv_begin<T, D>(a, qc, &home_q, &left, it)) {
+    const int kw0 = it.kw_base + 32 * pair;
+    const View vv = seq_view((const char*)a.v + it.krow + (size_t)kw0 * gstride, max(0, min(32, it.Lk - kw0)), gstride, C::ROWB);
+    Frag<T> vf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) vf[kk] = gfrag(vv, (uint32_t)l32 * gstride + (16 * kk + 8 * g) * ES, (T*)0);
+    f32x16 dk[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dk[db] = (f32x16){};
+    dkv_prologue<T, D>(it, gstride, a.H, tid, lds);
+    wait_vmem();  // V fragments in
+    __syncthreads();
+
+    for (int jb = 0; jb <= it.nblk; ++jb) {
+      if (jb + 2 < it.nblk) dkv_gload<T, D>(it, jb + 2, gstride, a.H, tid, stg);
+      const int jp = jb - 1;  // block whose P the score wave handed over in the previous step
+      if (jp >= 0 && dkv_active((it.qb0 + jp) * BMQ, kw0, it.Lk, a.causal)) {
+        const lds_t* qt = lds + (jp % C::NSLOT) * C::SLOT;
+        const lds_t* dot = qt + C::QTILE;
+        const __attribute__((address_space(3))) float* rc = (const __attribute__((address_space(3))) float*)(qt + C::RCOFF);
+        // dP = dO V^T (same layout as S: lane = key, element i = query res_row(i, g))
+        f32x16 dp = (f32x16){};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) mma(dp, lfrag<D>(dot, l32, 16 * kk + 8 * g, (T*)0), vf[kk]);
+        const lds_t* pb = lds + C::PBUF + ((jp & 1) * C::PAIRS + pair) * C::PBLK;
+        f32x16 p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x4 x = *(const __attribute__((address_space(3))) f32x4*)(pb + 1024 * e + 16 * lane);
+          p[4 * e] = x[0];
+          p[4 * e + 1] = x[1];
+          p[4 * e + 2] = x[2];
+          p[4 * e + 3] = x[3];
+        }
+        // dS = P (dP - Delta)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dp[i] = p[i] * (dp[i] - rc[2 * res_row(i, g) + 1]);
+        // dK^T += Q^T dS^T
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const Frag<T> sf = rfrag(dp, c, (T*)0);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) mma(dk[db], tfrag<D>(qt, 16 * c, 32 * db, lane, (T*)0), sf);
+        }
+      }
+      if (jb + 2 < it.nblk) dkv_swrite<T, D>(jb + 2, tid, stg, lds);
+      __syncthreads();
+    }
+
+    // dK^T: lane holds rows d = 32db + res_row(i,g) of key kw0 + l32.
+    if (kw0 < it.Lk) {
+      const View dkv = seq_view((char*)a.dk + it.krow + (size_t)kw0 * gstride, min(32, it.Lk - kw0), gstride, C::ROWB);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = 32 * db + 8 * r + 4 * g;
+          store4(dkv, (uint32_t)l32 * gstride + d * ES, dk[db][4 * r] * a.scale, dk[db][4 * r + 1] * a.scale,
+                 dk[db][4 * r + 2] * a.scale, dk[db][4 * r + 3] * a.scale, (T*)0);
+        }
+      }
+    }
+  }
+}
+
+// The two roles run the same item sequence and meet at the same barriers
+// (two per item fetch, one after the prologue, one per block step).
+template <typename T, int D, bool BIAS>
+__global__ __launch_bounds__(512, (D * sizeof(T) <= 128 ? 4 : 2)) void jfa_dkdv_kernel(BwdArgs a) {
+  using C = DkvTiles<T, D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ QueueCursor qcur;
+  lds_t* lds = (lds_t*)smem;
+  load_queues(a.hdr, &qcur);
+  if ((threadIdx.x >> 6) < C::PAIRS) dkv_score_role<T, D, BIAS>(a, lds, &qcur);
+  else dkv_grad_role<T, D>(a, lds, &qcur);
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV pass for D <= 64, one role per wave: 4 waves x 32 keys, each wave
+// keeping its K, V fragments and dK, dV accumulators in VGPRs and walking
+// 64-row query blocks staged in LDS (register prefetch, two LDS stages).
+// Small enough per wave for two workgroups per CU.
+template <typename T, int D>
+struct Dkv1Tiles {
   static constexpr int BNK = 128;  // keys per item (4 waves x 32)
   static constexpr int BMQ = 64;   // query rows per staged block
   static constexpr int THREADS = 256;
   using TL = Tile<T, D>;
   static constexpr int ROWB = TL::ROWB;
   static constexpr int QTILE = BMQ * ROWB;
-  static constexpr int STAGE = 2 * QTILE + 2 * BMQ * 4;  // Q, dO, lse2, delta
+  static constexpr int STAGE = 2 * QTILE + 2 * BMQ * 4;  // Q, dO, (lse2, Delta) pairs
   static constexpr int CPR = ROWB / 16;
   static constexpr int CPT = BMQ * CPR / THREADS;
   static constexpr int BIAS_OFF = 2 * STAGE;
   static constexpr int LDS = BIAS_OFF + 1040;
   static_assert((BMQ * CPR) % THREADS == 0, "tile pieces divide the workgroup");
-  static_assert(BMQ == kDkvTM && BNK == kDkvTN, "tile shape published to the planner");
+  static_assert(BMQ == kDkv1TM && BNK == kDkvTN, "tile shape published to the planner");
 };
 
 template <typename T, int D, bool BIAS>
-__global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv_kernel(BwdArgs a) {
-  using C = DkvTiles<T, D>;
+__global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv1_kernel(BwdArgs a) {
+  using C = Dkv1Tiles<T, D>;
   constexpr int BNK = C::BNK, BMQ = C::BMQ, ES = (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   __shared__ QueueCursor qcur;
@@ -103,8 +425,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv_
     const View dov = seq_view((const char*)a.dout + qrow, Lq, gstride, C::ROWB);
     const View kv = seq_view((const char*)a.k + krow, Lk, gstride, C::ROWB);
     const View vv = seq_view((const char*)a.v + krow, Lk, gstride, C::ROWB);
-    const View lv = seq_view(a.lse + (size_t)q0 * H + h, Lq, (uint32_t)H * 4, 4);
-    const View dlv = seq_view(a.delta + (size_t)q0 * H + h, Lq, (uint32_t)H * 4, 4);
+    const View rcv = seq_view(a.rowc + (size_t)q0 * H + h, Lq, 8 * H, 8);
 
     if (BIAS) {
       for (int i = tid; i < kBiasLen; i += C::THREADS) bias_lds[i] = a.bias[h * kBiasLen + i] * kLog2e;
@@ -121,7 +442,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv_
     }
 
     i32x4 qr[C::CPT], dr[C::CPT];
-    float lr = 0.f;
+    i32x2 lr = {};
     auto gload = [&](int qb) {
 #pragma unroll
       for (int c = 0; c < C::CPT; ++c) {
@@ -130,8 +451,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv_
         qr[c] = ld16(qv, off);
         dr[c] = ld16(dov, off);
       }
-      if (tid < BMQ) lr = ld4f(lv, (uint32_t)(qb * BMQ + tid) * H * 4) * kLog2e;
-      else if (tid < 2 * BMQ) lr = ld4f(dlv, (uint32_t)(qb * BMQ + tid - BMQ) * H * 4);
+      if (tid < BMQ) lr = ld8(rcv, (uint32_t)(qb * BMQ + tid) * 8 * H);
     };
     auto swrite = [&](int s) {
       lds_t* st = lds + s * C::STAGE;
@@ -142,7 +462,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv_
         *(__attribute__((address_space(3))) i32x4*)(st + o) = qr[c];
         *(__attribute__((address_space(3))) i32x4*)(st + C::QTILE + o) = dr[c];
       }
-      if (tid < 2 * BMQ) *(__attribute__((address_space(3))) float*)(st + 2 * C::QTILE + tid * 4) = lr;
+      if (tid < BMQ) *(__attribute__((address_space(3))) i32x2*)(st + 2 * C::QTILE + 8 * tid) = lr;
     };
     if (qb0 < nq) {
       gload(qb0);
@@ -163,8 +483,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv_
       if (qb + 1 < nq) gload(qb + 1);
       const lds_t* qt = lds + s * C::STAGE;
       const lds_t* dot = qt + C::QTILE;
-      const __attribute__((address_space(3))) float* lse2 = (const __attribute__((address_space(3))) float*)(qt + 2 * C::QTILE);
-      const __attribute__((address_space(3))) float* dl = lse2 + BMQ;
+      const __attribute__((address_space(3))) float* rc = (const __attribute__((address_space(3))) float*)(qt + 2 * C::QTILE);
 #pragma unroll
       for (int sb = 0; sb < BMQ / 32; ++sb) {
         const int qs0 = qb * BMQ + 32 * sb;  // first query of this 32-row sub-block
@@ -182,12 +501,12 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv_
         for (int i = 0; i < 16; ++i) {
           const int r = 32 * sb + res_row(i, g);
           const int qi = qb * BMQ + r;
-          float x = sc[i] * a.scale2 - lse2[r];
+          float x = sc[i] * a.scale2 - rc[2 * r];
           if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
           float p = __builtin_amdgcn_exp2f(x);
           if (masked && kj > qi) p = 0.f;
           sc[i] = p;
-          dp[i] = p * (dp[i] - dl[r]);
+          dp[i] = p * (dp[i] - rc[2 * r + 1]);
         }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -269,8 +588,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
     const size_t qrow = ((size_t)q0 * H + h) * C::ROWB, krow = ((size_t)k0 * H + h) * C::ROWB;
     const View qv = seq_view((const char*)a.q + qrow, Lq, gstride, C::ROWB);
     const View dov = seq_view((const char*)a.dout + qrow, Lq, gstride, C::ROWB);
-    const View lv = seq_view(a.lse + (size_t)q0 * H + h, Lq, (uint32_t)H * 4, 4);
-    const View dlv = seq_view(a.delta + (size_t)q0 * H + h, Lq, (uint32_t)H * 4, 4);
+    const View rcv = seq_view(a.rowc + (size_t)q0 * H + h, Lq, 8 * H, 8);
 
     if (BIAS) {
       for (int i = tid; i < kBiasLen; i += C::THREADS) bias_lds[i] = a.bias[h * kBiasLen + i] * kLog2e;
@@ -285,8 +603,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
       qf[kk] = gfrag(qv, (uint32_t)qi * gstride + (16 * kk + 8 * g) * ES, (T*)0);
       df[kk] = gfrag(dov, (uint32_t)qi * gstride + (16 * kk + 8 * g) * ES, (T*)0);
     }
-    const float lse2 = ld4f(lv, (uint32_t)qi * H * 4) * kLog2e;
-    const float dlt = ld4f(dlv, (uint32_t)qi * H * 4);
+    const i32x2 rcq = ld8(rcv, (uint32_t)qi * 8 * H);
+    const float lse2 = __int_as_float(rcq[0]), dlt = __int_as_float(rcq[1]);
 
     // K/V blocks through a two-stage LDS ring filled by direct loads: block
     // j+1 is requested while block j is computed.
@@ -369,17 +687,16 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
 
 // ---------------------------------------------------------------------------
 template <typename K>
-static long persistent_grid(K kern, int& occ, long max_items, int num_cus) {
+static long persistent_grid(K kern, int& occ, long max_items, int num_cus, int threads = 256) {
   if (occ == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, 0) != hipSuccess || occ < 1) occ = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0) != hipSuccess || occ < 1) occ = 1;
   }
   return max(1L, min(max_items, (long)num_cus * occ));
 }
 
 template <typename T, int D>
 static hipError_t launch_delta_t(const BwdArgs& a, hipStream_t st) {
-  constexpr int RPB = 256 / (D * (int)sizeof(T) / 16);
-  const long nblk = (a.rows + RPB - 1) / RPB;
+  const long nblk = (a.tq * a.H + DeltaShape<T, D>::RPB - 1) / DeltaShape<T, D>::RPB;
   if (nblk > 0) hipLaunchKernelGGL((jfa_delta_kernel<T, D>), dim3((unsigned)nblk), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -387,10 +704,18 @@ static hipError_t launch_delta_t(const BwdArgs& a, hipStream_t st) {
 template <typename T, int D, bool BIAS>
 static hipError_t launch_dkdv_t(const BwdArgs& a, long max_items, int num_cus, hipStream_t st) {
   static int occ = 0;
-  const long g = persistent_grid(jfa_dkdv_kernel<T, D, BIAS>, occ, max_items, num_cus);
-  hipLaunchKernelGGL((jfa_dkdv_kernel<T, D, BIAS>), dim3((unsigned)g), dim3(256), 0, st, a);
+  if constexpr (D * sizeof(T) <= 128) {
+    const long g = persistent_grid(jfa_dkdv1_kernel<T, D, BIAS>, occ, max_items, num_cus);
+    hipLaunchKernelGGL((jfa_dkdv1_kernel<T, D, BIAS>), dim3((unsigned)g), dim3(256), 0, st, a);
+  } else {
+    constexpr int threads = DkvTiles<T, D>::THREADS;
+    const long g = persistent_grid(jfa_dkdv_kernel<T, D, BIAS>, occ, max_items, num_cus, threads);
+    hipLaunchKernelGGL((jfa_dkdv_kernel<T, D, BIAS>), dim3((unsigned)g), dim3(threads), 0, st, a);
+  }
   return hipGetLastError();
 }
+
+int dkv_tile_rows(bool f32, int D) { return D * (f32 ? 4 : 2) <= 128 ? kDkv1TM : kDkvTM; }
 
 template <typename T, int D, bool BIAS>
 static hipError_t launch_dq_t(const BwdArgs& a, long max_items, int num_cus, hipStream_t st) {

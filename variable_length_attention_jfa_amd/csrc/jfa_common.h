@@ -59,6 +59,9 @@ __device__ __forceinline__ i32x4 ld16(const View& v, uint32_t off) {
 __device__ __forceinline__ float ld4f(const View& v, uint32_t off) {
   return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(v.r, off, 0, 0));
 }
+__device__ __forceinline__ i32x2 ld8(const View& v, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(v.r, off, 0, 0);
+}
 __device__ __forceinline__ void st16(const View& v, uint32_t off, i32x4 x) {
   __builtin_amdgcn_raw_buffer_store_b128(x, v.r, off, 0, 0);
 }
@@ -190,6 +193,38 @@ __device__ __forceinline__ Frag<float> rfrag(const f32x16& s, int c, float*) {
   return f;
 }
 
+// A whole-wave fragment parked in LDS (16 bytes per lane per 1 KB piece, lane
+// order), for handing an operand from one wave to another.
+__device__ __forceinline__ void put_frag(lds_t* p, const Frag<bf16>& f, int lane) {
+  *(__attribute__((address_space(3))) i32x4*)(p + 16 * lane) = __builtin_bit_cast(i32x4, f.v);
+}
+__device__ __forceinline__ void put_frag(lds_t* p, const Frag<float>& f, int lane) {
+  *(__attribute__((address_space(3))) f32x4*)(p + 16 * lane) = f.lo;
+  *(__attribute__((address_space(3))) f32x4*)(p + 1024 + 16 * lane) = f.hi;
+}
+__device__ __forceinline__ Frag<bf16> get_frag(const lds_t* p, int lane, bf16*) {
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) i32x4*)(p + 16 * lane));
+  return f;
+}
+__device__ __forceinline__ Frag<float> get_frag(const lds_t* p, int lane, float*) {
+  Frag<float> f;
+  f.lo = *(const __attribute__((address_space(3))) f32x4*)(p + 16 * lane);
+  f.hi = *(const __attribute__((address_space(3))) f32x4*)(p + 1024 + 16 * lane);
+  return f;
+}
+
+// Wave-uniform copies (scalar registers) of values the compiler cannot prove
+// uniform.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <typename P>
+__device__ __forceinline__ P* uni(P* p) {
+  const unsigned long long a = (unsigned long long)p;
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32));
+  return (P*)(((unsigned long long)hi << 32) | lo);
+}
+
 // Value held by the lane 32 positions away (other half of the wave).
 __device__ __forceinline__ float other_half(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
@@ -251,20 +286,24 @@ __device__ __forceinline__ void dma16(const DmaView& v, const lds_t* dst, uint32
                : "memory", "m0");
 }
 
+// 1 KB block k of an LDS tile whose row 0 is row row0 of the view.
+template <typename T, int D>
+__device__ __forceinline__ void dma_block(const DmaView& v, uint32_t gstride, int row0, lds_t* tile, int k, int lane) {
+  using TL = Tile<T, D>;
+  const int P = k * 1024 + 16 * lane;
+  const int r = P / TL::ROWB, pc = (P % TL::ROWB) >> 4;
+  const uint32_t goff = (uint32_t)(row0 + r) * gstride + (uint32_t)((pc ^ TL::swz(r)) << 4);
+  dma16(v, tile + k * 1024, goff);
+}
+
 // Rows row0 .. row0+ROWS-1 of the view into an LDS tile; the waves split the
 // tile's 1 KB blocks.
 template <typename T, int D, int ROWS, int WAVES>
 __device__ __forceinline__ void dma_tile(const DmaView& v, uint32_t gstride, int row0, lds_t* tile, int wave, int lane) {
-  using TL = Tile<T, D>;
-  constexpr int NBLK = ROWS * TL::ROWB / 1024;
+  constexpr int NBLK = ROWS * Tile<T, D>::ROWB / 1024;
   static_assert(NBLK % WAVES == 0 || NBLK < WAVES, "tile blocks divide the waves (or one block per wave)");
 #pragma unroll
-  for (int k = wave; k < NBLK; k += WAVES) {
-    const int P = k * 1024 + 16 * lane;
-    const int r = P / TL::ROWB, pc = (P % TL::ROWB) >> 4;
-    const uint32_t goff = (uint32_t)(row0 + r) * gstride + (uint32_t)((pc ^ TL::swz(r)) << 4);
-    dma16(v, tile + k * 1024, goff);
-  }
+  for (int k = wave; k < NBLK; k += WAVES) dma_block<T, D>(v, gstride, row0, tile, k, lane);
 }
 template <typename T, int D, int ROWS, int WAVES>
 constexpr int dma_loads_per_wave() {
@@ -277,6 +316,14 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt_c() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Wait until at most n (uniform across the wave) vector-memory operations of
+// this wave are outstanding; n above 3 waits for 3 (stricter, still correct).
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if (n <= 0) wait_vmcnt_c<0>();
+  else if (n == 1) wait_vmcnt_c<1>();
+  else if (n == 2) wait_vmcnt_c<2>();
+  else wait_vmcnt_c<3>();
 }
 template <int STEP, int MAXK>
 __device__ __forceinline__ void wait_vmcnt_tiles(int k) {  // wait until at most k*STEP loads remain
@@ -361,7 +408,9 @@ __device__ __forceinline__ int next_item(PlanHeader* hdr, QueueCursor* qc, int* 
     qc->item = it;
   }
   __syncthreads();
-  return qc->item;
+  // The same value in every lane: item fields, views and addresses derived
+  // from it then live in scalar registers.
+  return __builtin_amdgcn_readfirstlane(qc->item);
 }
 
 }  // namespace jfa

@@ -36,14 +36,14 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;        // [Tq, H] fp32 (workspace)
+  float2* rowc;        // [Tq, H] (lse * log2(e), Delta) per query row (workspace)
   const int4* items;   // work list of this pass
   PlanHeader* hdr;
   int H;
   int causal;
   float scale;         // 1/sqrt(D)
   float scale2;        // scale * log2(e)
-  long rows;           // Tq * H (delta kernel)
+  long tq;             // query tokens (rows of rowc per head)
 };
 
 struct PlanPass {
@@ -70,7 +70,11 @@ template <typename T, int D> struct FwdWaves { static constexpr int value = 4; }
 template <typename T, int D> struct FwdRows { static constexpr int value = 32 * FwdWaves<T, D>::value; };
 constexpr int kFwdTN = 64;
 int fwd_tile_rows(bool f32, int D);
-constexpr int kDkvTM = 64, kDkvTN = 128;
+// dK/dV pass: rows of 128 bytes or less (bf16 D <= 64, fp32 D = 32) use the
+// one-role kernel with 64-row query blocks, wider rows the two-role kernel
+// with 32-row blocks.
+constexpr int kDkvTM = 32, kDkv1TM = 64, kDkvTN = 128;
+int dkv_tile_rows(bool f32, int D);
 constexpr int kDqTM = 128, kDqTN = 64;
 
 // Persistent launches: grid = min(max_items, CUs x resident workgroups per CU).
