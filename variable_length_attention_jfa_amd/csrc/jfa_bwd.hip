@@ -361,7 +361,7 @@ __device__ __forceinline__ void dkv_grad_role(const BwdArgs& a, lds_t* lds, Queu
 // The two roles run the same item sequence and meet at the same barriers
 // (two per item fetch, one after the prologue, one per block step).
 template <typename T, int D, bool BIAS>
-__global__ __launch_bounds__(512, (D * sizeof(T) <= 128 ? 4 : 2)) void jfa_dkdv_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkv_two_roles(const BwdArgs& a) {
   using C = DkvTiles<T, D>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   __shared__ QueueCursor qcur;
@@ -394,7 +394,7 @@ struct Dkv1Tiles {
 };
 
 template <typename T, int D, bool BIAS>
-__global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv1_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
   using C = Dkv1Tiles<T, D>;
   constexpr int BNK = C::BNK, BMQ = C::BMQ, ES = (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -540,6 +540,20 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 256 ? 1 : 2)) void jfa_dkdv1
       }
     }
   }
+}
+
+// dK/dV kernel: one role per wave for rows of up to 128 bytes, score and
+// gradient wave pairs for wider rows.
+template <typename T, int D>
+struct DkvShape {
+  static constexpr bool one_role = D * sizeof(T) <= 128;
+  static constexpr int threads = one_role ? Dkv1Tiles<T, D>::THREADS : 512;
+};
+
+template <typename T, int D, bool BIAS>
+__global__ __launch_bounds__((DkvShape<T, D>::threads), 2) void jfa_dkdv_kernel(BwdArgs a) {
+  if constexpr (DkvShape<T, D>::one_role) dkv_one_role<T, D, BIAS>(a);
+  else dkv_two_roles<T, D, BIAS>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -704,18 +718,18 @@ static hipError_t launch_delta_t(const BwdArgs& a, hipStream_t st) {
 template <typename T, int D, bool BIAS>
 static hipError_t launch_dkdv_t(const BwdArgs& a, long max_items, int num_cus, hipStream_t st) {
   static int occ = 0;
-  if constexpr (D * sizeof(T) <= 128) {
-    const long g = persistent_grid(jfa_dkdv1_kernel<T, D, BIAS>, occ, max_items, num_cus);
-    hipLaunchKernelGGL((jfa_dkdv1_kernel<T, D, BIAS>), dim3((unsigned)g), dim3(256), 0, st, a);
-  } else {
-    constexpr int threads = DkvTiles<T, D>::THREADS;
-    const long g = persistent_grid(jfa_dkdv_kernel<T, D, BIAS>, occ, max_items, num_cus, threads);
-    hipLaunchKernelGGL((jfa_dkdv_kernel<T, D, BIAS>), dim3((unsigned)g), dim3(threads), 0, st, a);
-  }
+  constexpr int threads = DkvShape<T, D>::threads;
+  const long g = persistent_grid(jfa_dkdv_kernel<T, D, BIAS>, occ, max_items, num_cus, threads);
+  hipLaunchKernelGGL((jfa_dkdv_kernel<T, D, BIAS>), dim3((unsigned)g), dim3(threads), 0, st, a);
   return hipGetLastError();
 }
 
-int dkv_tile_rows(bool f32, int D) { return D * (f32 ? 4 : 2) <= 128 ? kDkv1TM : kDkvTM; }
+int dkv_tile_rows(bool f32, int D) {
+  const bool one = f32 ? (D == 32 ? DkvShape<float, 32>::one_role : DkvShape<float, 64>::one_role)
+                       : (D == 32 ? DkvShape<bf16, 32>::one_role
+                                  : D == 64 ? DkvShape<bf16, 64>::one_role : DkvShape<bf16, 128>::one_role);
+  return one ? kDkv1TM : kDkvTM;
+}
 
 template <typename T, int D, bool BIAS>
 static hipError_t launch_dq_t(const BwdArgs& a, long max_items, int num_cus, hipStream_t st) {
