@@ -118,9 +118,9 @@ struct DkvItem {
 };
 
 template <typename T, int D>
-__device__ __forceinline__ bool dkv_begin(const BwdArgs& a, QueueCursor* qc, int* home_q, int* left, DkvItem& it) {
+__device__ __forceinline__ bool dkv_begin(const BwdArgs& a, QueueCursor* qc, TicketState& tk, DkvItem& it) {
   using C = DkvTiles<T, D>;
-  const int i = next_item(a.hdr, qc, home_q, left);
+  const int i = next_item(a.hdr, qc, tk);
   if (i < 0) return false;
   const int4 item = a.items[i];
   it.b = uni(item.x);
@@ -206,10 +206,10 @@ __device__ __forceinline__ void dkv_score_role(const BwdArgs& a, lds_t* lds, Que
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: views and loops stay scalar
   const int pair = w;
   const uint32_t gstride = (uint32_t)a.H * C::ROWB;
-  int home_q = 0, left = -1;
+  TicketState tk;
   DkvItem it;
   DkvStage<T, D> stg;
-  while (dkv_begin<T, D>(a, qc, &home_q, &left, it)) {
+  while (dkv_begin<T, D>(a, qc, tk, it)) {
     if (BIAS) {  // read by the score waves only, which load it themselves
       for (int i = tid; i < kBiasLen; i += 64 * C::PAIRS) bias_lds[i] = a.bias[it.h * kBiasLen + i] * kLog2e;
     }
@@ -290,10 +290,10 @@ __device__ __forceinline__ void dkv_grad_role(const BwdArgs& a, lds_t* lds, Queu
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = w - C::PAIRS;
   const uint32_t gstride = (uint32_t)a.H * C::ROWB;
-  int home_q = 0, left = -1;
+  TicketState tk;
   DkvItem it;
   DkvStage<T, D> stg;
-  while (dkv_begin<T, D>(a, qc, &home_q, &left, it)) {
+  while (dkv_begin<T, D>(a, qc, tk, it)) {
     const int kw0 = it.kw_base + 32 * pair;
     const View vv = seq_view((const char*)a.v + it.krow + (size_t)kw0 * gstride, max(0, min(32, it.Lk - kw0)), gstride, C::ROWB);
     Frag<T> vf[D / 16];
@@ -402,14 +402,15 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
   lds_t* lds = (lds_t*)smem;
   __attribute__((address_space(3))) float* bias_lds = (__attribute__((address_space(3))) float*)(lds + C::BIAS_OFF);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave branches stay scalar
   const int H = a.H;
   const uint32_t gstride = (uint32_t)H * C::ROWB;
   load_queues(a.hdr, &qcur);
-  int home_q = 0, queues_left = -1;
+  TicketState tk;
 
   for (;;) {
-    const int it = next_item(a.hdr, &qcur, &home_q, &queues_left);
+    const int it = next_item(a.hdr, &qcur, tk);
     if (it < 0) break;
     const int4 item = a.items[it];
     const int b = item.x, h = item.y, kt = item.z;
@@ -583,14 +584,15 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
   lds_t* lds = (lds_t*)smem;
   __attribute__((address_space(3))) float* bias_lds = (__attribute__((address_space(3))) float*)(lds + C::BIAS_OFF);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave branches stay scalar
   const int H = a.H;
   const uint32_t gstride = (uint32_t)H * C::ROWB;
   load_queues(a.hdr, &qcur);
-  int home_q = 0, queues_left = -1;
+  TicketState tk;
 
   for (;;) {
-    const int it = next_item(a.hdr, &qcur, &home_q, &queues_left);
+    const int it = next_item(a.hdr, &qcur, tk);
     if (it < 0) break;
     const int4 item = a.items[it];
     const int b = item.x, h = item.y, qt = item.z;

@@ -384,26 +384,34 @@ __device__ __forceinline__ void load_queues(const PlanHeader* hdr, QueueCursor* 
   if (threadIdx.x == kMaxQueues) qc->nq = max(hdr->nq, 1);
 }
 
+// Per-workgroup ticket state, meaningful in thread 0 only.
+struct TicketState {
+  int q = 0;      // queue being drained
+  int left = -1;  // queues not yet found empty (< 0: not started)
+};
+
 // Next work item for this workgroup. Thread 0 takes tickets from its home
 // queue (the one its XCD drains) and, once that is empty, from the others in
-// turn; *q and *left live in thread 0 only (*left < 0: not started). Returns
-// -1 when every queue is empty.
-__device__ __forceinline__ int next_item(PlanHeader* hdr, QueueCursor* qc, int* q, int* left) {
+// turn. Tickets are taken one at a time, when the previous item is done: a
+// workgroup never holds a claim on an item it is not working on, so the
+// longest-first order decides which items start first. Returns -1 when every
+// queue is empty.
+__device__ __forceinline__ int next_item(PlanHeader* hdr, QueueCursor* qc, TicketState& ts) {
   __syncthreads();  // queue bounds loaded; every wave is done with the previous item's slot
   if (threadIdx.x == 0) {
-    if (*left < 0) {
-      *q = (int)(blockIdx.x % (unsigned)qc->nq);
-      *left = qc->nq;
+    if (ts.left < 0) {
+      ts.q = (int)(blockIdx.x % (unsigned)qc->nq);
+      ts.left = qc->nq;
     }
     int it = -1;
-    while (*left > 0) {
-      const int t = __hip_atomic_fetch_add(&hdr->ticket[*q].value, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (t < qc->count[*q]) {
-        it = qc->start[*q] + t;
+    while (ts.left > 0) {
+      const int t = __hip_atomic_fetch_add(&hdr->ticket[ts.q].value, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t < qc->count[ts.q]) {
+        it = qc->start[ts.q] + t;
         break;
       }
-      *q = *q + 1 == qc->nq ? 0 : *q + 1;
-      *left -= 1;
+      ts.q = ts.q + 1 == qc->nq ? 0 : ts.q + 1;
+      ts.left -= 1;
     }
     qc->item = it;
   }

@@ -55,14 +55,15 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
   lds_t* lds = (lds_t*)smem;
   __attribute__((address_space(3))) float* bias_lds = (__attribute__((address_space(3))) float*)(lds + C::BIAS_OFF);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave branches stay scalar
   const int H = a.H;
   const uint32_t gstride = (uint32_t)H * C::ROWB;  // bytes between consecutive tokens
   load_queues(a.hdr, &qcur);
-  int home_q = 0, queues_left = -1;
+  TicketState tk;
 
   for (;;) {
-    const int it = next_item(a.hdr, &qcur, &home_q, &queues_left);
+    const int it = next_item(a.hdr, &qcur, tk);
     if (it < 0) break;
     const int4 item = a.items[it];
     const int b = item.x, h = item.y, qt = item.z;
