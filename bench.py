@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--all] [--no-cpu-baseline]
 
 One step is the whole hot path over one synthetic batch already resident in
-HBM: jfa_fwd (work-list build + forward kernel) then jfa_bwd (two work lists,
-delta, dK/dV pass, dQ pass). Throughput counts valid (query, key) pairs only:
+HBM: jfa_fwd (work-list build + forward kernel) then jfa_bwd (three work
+lists, delta, dK/dV pass, dQ pass, and for sequences of at most 64 queries the
+short-query backward and its dQ sum). Throughput counts valid (query, key) pairs only:
 forward 4*D*H*pairs flops, backward 10*D*H*pairs flops (pairs = sum Lq*Lk, or
 sum_i min(i+1, Lk) with the causal mask).
 
@@ -32,11 +33,17 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0
+SHORT_Q_MAX = 64            # the backward owns sequences with at most this many queries whole
 
 
-def valid_pairs(q_lengths, kv_lengths, causal):
+def valid_pairs(q_lengths, kv_lengths, causal, which="all"):
+    """Valid (query, key) pairs per head. which: "all", "long" (sequences the
+    split backward handles) or "short" (at most SHORT_Q_MAX queries: the
+    short-query backward)."""
     total = 0
     for lq, lk in zip(q_lengths.tolist(), kv_lengths.tolist()):
+        if which == "long" and lq <= SHORT_Q_MAX or which == "short" and lq > SHORT_Q_MAX:
+            continue
         if causal:
             m = min(lq, lk)
             total += m * (m + 1) // 2 + (lq - m) * lk
@@ -79,7 +86,7 @@ def recorded_traffic(kernel_label: str, workload: int):
 # Algorithmic flops per valid pair per head, as multiples of D, for each kernel:
 # forward QK^T + PV; dK/dV pass recomputes QK^T and dO V^T and forms dV, dK;
 # dQ pass recomputes QK^T and dO V^T and forms dQ.
-KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "dkdv": 8, "dq": 6}
+KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "dkdv": 8, "dq": 6, "sq": 10}
 
 
 def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None):
@@ -127,7 +134,7 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None)
     # the plan kind covers one launch in forward and one in backward per step
     plan_ms = kt["plan"][0] / max(kt["plan"][1], 1)
     fwd_ms = kt["forward"][0] / steps + plan_ms
-    bwd_ms = (kt["delta"][0] + kt["dkdv"][0] + kt["dq"][0]) / steps + plan_ms
+    bwd_ms = (kt["delta"][0] + kt["dkdv"][0] + kt["dq"][0] + kt["sq"][0] + kt["sq_reduce"][0]) / steps + plan_ms
     res = {
         "workload": wl.name, "B": wl.B, "H": wl.H, "D": wl.D, "dtype": wl.dtype, "causal": wl.causal,
         "bias": wl.bias, "seed": wl.seed if seed is None else seed, "total_q": batch.total_q,
@@ -142,17 +149,26 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None)
     peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
     res["fwd_pct_peak"] = 100.0 * res["fwd_tflops"] / peak
     res["bwd_pct_peak"] = 100.0 * res["bwd_tflops"] / peak
-    # dominant kernel
-    share = {k_: kt[k_][0] for k_ in ("forward", "dkdv", "dq")}
+    # dominant kernel; its bound is the roofline its arithmetic intensity falls under
+    share = {k_: kt[k_][0] for k_ in ("forward", "dkdv", "dq", "sq")}
     dom = max(share, key=share.get)
     avg_ms = kt[dom][0] / kt[dom][1]
-    alg = KERNEL_FLOPS_PER_PAIR_D[dom] * wl.D * wl.H * pairs
-    achieved = alg / (avg_ms * 1e-3) / 1e12
+    kpairs = {"forward": pairs, "dkdv": valid_pairs(batch.q_lengths, batch.kv_lengths, wl.causal, "long"),
+              "dq": valid_pairs(batch.q_lengths, batch.kv_lengths, wl.causal, "long"),
+              "sq": valid_pairs(batch.q_lengths, batch.kv_lengths, wl.causal, "short")}[dom]
+    alg = KERNEL_FLOPS_PER_PAIR_D[dom] * wl.D * wl.H * kpairs
+    alg_bytes = algorithmic_bytes(dom, batch)
     label = f"jfa_{'fwd' if dom == 'forward' else dom}_kernel<{wl.dtype},D={wl.D}{',bias' if wl.bias else ''}>"
-    res["roofline"] = {"kernel": label, "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                       "frac": achieved / peak, "traffic": recorded_traffic(label, idx), "traffic_unit": "bytes/launch",
+    hbm = alg / max(alg_bytes, 1) < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm:
+        achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = alg / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
+    res["roofline"] = {"kernel": label, **roof, "traffic": recorded_traffic(label, idx), "traffic_unit": "bytes/launch",
                        "avg_launch_ms": avg_ms, "algorithmic_flops_per_launch": alg,
-                       "algorithmic_bytes_per_launch": algorithmic_bytes(dom, batch)}
+                       "algorithmic_bytes_per_launch": alg_bytes}
     res["_batch"] = batch
     return res
 
@@ -167,6 +183,8 @@ def algorithmic_bytes(kernel: str, batch) -> int:
         return tq + 2 * tk + tq + rows
     if kernel == "dkdv":         # q, k, v, dout, lse, delta in; dk, dv out
         return 2 * tq + 2 * tk + 2 * rows + 2 * tk
+    if kernel == "sq":           # q, k, v, dout, lse, delta in; dq, dk, dv out (whole sequences)
+        return 3 * tq + 4 * tk + 2 * rows
     return 2 * tq + 2 * tk + 2 * rows + tq   # dq: q, k, v, dout, lse, delta in; dq out
 
 

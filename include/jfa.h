@@ -71,6 +71,7 @@ typedef enum {
 #define JFA_KERNEL_FWD 0       /* forward: tiles of query rows            */
 #define JFA_KERNEL_BWD_DKDV 1  /* backward dK/dV pass: tiles of keys       */
 #define JFA_KERNEL_BWD_DQ 2    /* backward dQ pass: tiles of query rows    */
+#define JFA_KERNEL_BWD_SQ 3    /* backward of short-query sequences (Lq <= 64): chunks of keys */
 
 /* Element types for jfa_tile_config / jfa_build_plan. */
 #define JFA_DTYPE_BF16 0
@@ -97,7 +98,11 @@ jfa_status jfa_fwd(const void* q, const void* k, const void* v, const int32_t* q
 /* Backward pass (bf16). Takes the forward's out and lse and the upstream
  * gradient dout; writes dq, dk, dv (same layout and type as q, k, v). dK/dV
  * and dQ are computed in two passes with no atomics ("Jagged Flash Attention
- * (JFA)", section "Four generations", item 2). No gradient for the bias. */
+ * (JFA)", section "Four generations", item 2). A sequence with at most 64
+ * queries is instead owned whole by one workgroup per chunk of 1024 keys,
+ * which forms S and dP once and reads K, V once; its dQ is the sum, in a
+ * fixed order, of the chunks' partial results (asymmetric query/key lengths,
+ * section "Definition"). No gradient for the bias. */
 jfa_status jfa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
                    const void* dout, const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H,
                    int D, int64_t total_q, int64_t total_kv, const float* bias, int causal, void* dq,
@@ -135,8 +140,13 @@ jfa_status jfa_tile_config(int kernel, int D, int dtype, int* tile_m, int* tile_
  * 15 - g mod 16 (one queue per XCD; a workgroup drains its own queue, then
  * the others). Inside a queue groups follow their rank; inside a group items
  * follow cost descending, then tile ascending. Queue q holds items
- * [start[q], start[q] + qcount[q]). Exposed so that the lists can be checked
- * against an independent builder. */
+ * [start[q], start[q] + qcount[q]). The backward lists of JFA_KERNEL_BWD_DKDV
+ * and JFA_KERNEL_BWD_DQ skip sequences with at most 64 queries; the list of
+ * JFA_KERNEL_BWD_SQ has only those, one item per chunk of 1024 keys (at least
+ * one per sequence, cost = keys in the chunk), and the last
+ * align(B * H * 4, 256) bytes of the workspace then receive, per (b, h), the
+ * list position of its chunk 0 (-1 for other sequences). Exposed so that the
+ * lists can be checked against an independent builder. */
 jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D, int dtype,
                           int causal, int kernel, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -146,7 +156,7 @@ size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv,
 /* Launch timing, for benchmarks and profiling. While enabled, every kernel
  * launch of this library is bracketed by two HIP events recorded on its
  * stream (a few microseconds of host overhead per launch). */
-#define JFA_TIMING_KINDS 6 /* 0 plan, 1 forward, 2 delta, 3 dK/dV, 4 dQ, 5 offsets scan */
+#define JFA_TIMING_KINDS 8 /* 0 plan, 1 forward, 2 delta, 3 dK/dV, 4 dQ, 5 offsets scan, 6 short-query backward, 7 its dQ sum */
 jfa_status jfa_timing_enable(int enable);
 
 /* Waits for every recorded launch, writes the summed kernel milliseconds and

@@ -10,4 +10,5 @@ Modules:
   plan       the longest-first work list and the offsets scan, as integers
 """
 from .attention import forward, backward, valid_pairs  # noqa: F401
-from .plan import build_plan, build_plan_queues, q_tile_cost, kv_tile_cost, exclusive_scan, snake, N_QUEUES  # noqa: F401
+from .plan import (build_plan, build_plan_queues, q_tile_cost, kv_tile_cost, sq_chunk_cost, exclusive_scan,  # noqa: F401
+                   snake, N_QUEUES, SHORT_Q_MAX)

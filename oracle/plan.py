@@ -16,6 +16,13 @@ the reading used here:
     ceil(Lq/TM), or with the causal mask 0 if t*TN >= Lq else
     ceil(Lq/TM) - floor(t*TN/TM).
 
+  sq pass (the backward of short-query sequences, Lq <= QMAX = 64, which one
+    workgroup owns whole: no dQ pass and no recomputation for them): one item
+    per (b, h, c) with c a chunk of TN keys, c < max(1, ceil(Lk/TN)) (a
+    sequence without keys still gets one item, which writes its zero dQ). Its
+    cost is the number of keys in the chunk, min(TN, Lk - c*TN) (0 if none).
+    In the backward, the q and kv passes skip these sequences.
+
 Order, longest first at two levels. The items of one (b, h) form a group
 whose cost is the sum of its items' costs (the same for every h of a
 sequence). Groups are ranked by group cost descending, then b, then h. Group
@@ -33,6 +40,7 @@ from typing import List, Tuple
 import numpy as np
 
 N_QUEUES = 8
+SHORT_Q_MAX = 64  # backward: sequences with at most this many queries take the sq pass
 
 
 def _cdiv(a: int, b: int) -> int:
@@ -68,10 +76,22 @@ def snake(g: int, n_queues: int) -> int:
     return r if r < n_queues else 2 * n_queues - 1 - r
 
 
+def sq_chunk_cost(Lk: int, c: int, TN: int) -> int:
+    return max(0, min(TN, Lk - c * TN))
+
+
 def build_plan_queues(q_offsets, kv_offsets, H: int, TM: int, TN: int, causal: bool, kv_pass: bool = False,
-                      n_queues: int = N_QUEUES) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                      n_queues: int = N_QUEUES, kind: str = None, short_q: int = None,
+                      with_groups: bool = False):
     """Work lists as (items int32 [n, 4] of (b, h, tile, cost) with the queues
-    stored one after the other, starts int32 [n_queues], counts int32 [n_queues])."""
+    stored one after the other, starts int32 [n_queues], counts int32 [n_queues]).
+
+    kind: "q", "kv" or "sq" (default: "kv" if kv_pass else "q"). short_q: for
+    the backward's q and kv passes, sequences with Lq <= short_q get no items.
+    with_groups: also return, for the sq pass, int32 [B*H] with the list
+    position of chunk 0 of each (b, h) (-1 for sequences the pass skips)."""
+    if kind is None:
+        kind = "kv" if kv_pass else "q"
     qo = [int(x) for x in q_offsets]
     ko = [int(x) for x in kv_offsets]
     B = len(qo) - 1
@@ -79,11 +99,17 @@ def build_plan_queues(q_offsets, kv_offsets, H: int, TM: int, TN: int, causal: b
     seq_cost: List[int] = []
     for b in range(B):
         Lq, Lk = qo[b + 1] - qo[b], ko[b + 1] - ko[b]
-        if kv_pass:
-            n, costf = _cdiv(Lk, TN), kv_tile_cost
+        if kind == "sq":
+            n = max(1, _cdiv(Lk, TN)) if Lq <= SHORT_Q_MAX else 0
+            tiles = [(t, sq_chunk_cost(Lk, t, TN)) for t in range(n)]
         else:
-            n, costf = _cdiv(Lq, TM), q_tile_cost
-        tiles = [(t, costf(Lq, Lk, t, TM, TN, causal)) for t in range(n)]
+            if kind == "kv":
+                n, costf = _cdiv(Lk, TN), kv_tile_cost
+            else:
+                n, costf = _cdiv(Lq, TM), q_tile_cost
+            if short_q is not None and Lq <= short_q:
+                n = 0
+            tiles = [(t, costf(Lq, Lk, t, TM, TN, causal)) for t in range(n)]
         tiles.sort(key=lambda tc: (-tc[1], tc[0]))
         seq_items.append(tiles)
         seq_cost.append(sum(c for _, c in tiles))
@@ -97,7 +123,13 @@ def build_plan_queues(q_offsets, kv_offsets, H: int, TM: int, TN: int, causal: b
     counts = np.array([len(qu) for qu in queues], dtype=np.int32)
     starts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int32)
     items = np.array([it for qu in queues for it in qu], dtype=np.int32).reshape(-1, 4)
-    return items, starts, counts
+    if not with_groups:
+        return items, starts, counts
+    first = np.full(B * H, -1, dtype=np.int32)
+    for pos, (b, h, t, _) in enumerate(items.tolist()):
+        if t == 0:
+            first[b * H + h] = pos
+    return items, starts, counts, first
 
 
 def build_plan(q_offsets, kv_offsets, H: int, TM: int, TN: int, causal: bool, kv_pass: bool = False,

@@ -103,3 +103,39 @@ def test_exclusive_scan():
     lens = np.array([3, 0, 5, 1], dtype=np.int32)
     np.testing.assert_array_equal(oracle.exclusive_scan(lens), [0, 3, 3, 8, 9])
     assert oracle.exclusive_scan([]).tolist() == [0]
+
+
+@pytest.mark.parametrize("n_queues", [1, 8])
+def test_short_query_pass(n_queues):
+    """The sq pass: exactly the sequences with Lq <= 64, chunks covering their
+    keys once (one chunk when there are none), group table pointing at chunk 0,
+    and the q and kv passes of the backward skipping exactly those sequences."""
+    rng = np.random.default_rng(7 + n_queues)
+    B, H, KC = 40, 3, 1024
+    lq = rng.integers(0, 130, size=B)
+    lq[:4] = [0, 64, 65, 1]
+    lk = rng.integers(0, 5000, size=B)
+    lk[4:6] = [0, 1024]
+    qo, ko = oracle.exclusive_scan(lq), oracle.exclusive_scan(lk)
+    items, starts, counts, first = oracle.build_plan_queues(qo, ko, H, 64, KC, False, kind="sq", n_queues=n_queues,
+                                                            with_groups=True)
+    short = [b for b in range(B) if lq[b] <= oracle.SHORT_Q_MAX]
+    for b in range(B):
+        for h in range(H):
+            its = [(int(t), int(c)) for bb, hh, t, c in items if bb == b and hh == h]
+            if b not in short:
+                assert its == [] and first[b * H + h] == -1
+                continue
+            n = max(1, -(-int(lk[b]) // KC))
+            assert sorted(t for t, _ in its) == list(range(n))
+            assert sum(c for _, c in its) == lk[b]          # the chunks cover every key once
+            assert all(c == min(KC, int(lk[b]) - t * KC) for t, c in its)
+            pos = first[b * H + h]
+            assert tuple(items[pos][:3]) == (b, h, 0)
+            assert [tuple(x) for x in items[pos:pos + n, :3]] == [(b, h, t) for t in range(n)]  # contiguous, in order
+    for kind, TM, TN in (("q", 128, 64), ("kv", 64, 128)):
+        got, _, _ = oracle.build_plan_queues(qo, ko, H, TM, TN, True, kind=kind, short_q=oracle.SHORT_Q_MAX,
+                                             n_queues=n_queues)
+        full, _, _ = oracle.build_plan_queues(qo, ko, H, TM, TN, True, kind=kind, n_queues=n_queues)
+        assert {int(b) for b in got[:, 0]}.isdisjoint(short)
+        assert {tuple(x) for x in got.tolist()} == {tuple(x) for x in full.tolist() if x[0] not in short}

@@ -71,7 +71,8 @@ jfa_status device_info(DeviceInfo** out) {
 
 // Optional per-launch timing: HIP events recorded on the launch stream around
 // each kernel, read back on jfa_timing_collect().
-enum { kKindPlan = 0, kKindFwd = 1, kKindDelta = 2, kKindDkdv = 3, kKindDq = 4, kKindScan = 5 };
+enum { kKindPlan = 0, kKindFwd = 1, kKindDelta = 2, kKindDkdv = 3, kKindDq = 4, kKindScan = 5, kKindSq = 6, kKindSqReduce = 7 };
+static_assert(kKindSqReduce + 1 == JFA_TIMING_KINDS, "timing kinds published in the header");
 struct TimingRec {
   int kind;
   hipEvent_t a, b;
@@ -136,18 +137,27 @@ FwdLayout fwd_layout(int B, int H, int64_t tq) {
   return L;
 }
 
+// Backward workspace: three list headers (dK/dV, dQ, short-query passes), the
+// row constants [Tq, H] (lse * log2 e, Delta), the three item lists, the
+// short-query group table [B*H] and one [64, D] fp32 partial dQ per
+// short-query item.
 struct BwdLayout {
-  size_t hdr_kv = 0, hdr_q = sizeof(PlanHeader), rowc = 0, items_kv = 0, items_q = 0, total = 0;
-  int64_t cap_kv = 0, cap_q = 0;
+  size_t hdr_kv = 0, hdr_q = sizeof(PlanHeader), hdr_sq = 2 * sizeof(PlanHeader), rowc = 0, items_kv = 0,
+         items_q = 0, items_sq = 0, gfirst = 0, dqp = 0, total = 0;
+  int64_t cap_kv = 0, cap_q = 0, cap_sq = 0;
 };
-BwdLayout bwd_layout(int B, int H, int64_t tq, int64_t tk) {
+BwdLayout bwd_layout(int B, int H, int64_t tq, int64_t tk, int D) {
   BwdLayout L;
   L.cap_kv = max_items(B, H, tk, jfa::kDkvTN);
   L.cap_q = max_items(B, H, tq, jfa::kDqTM);
-  L.rowc = 2 * sizeof(PlanHeader);
+  L.cap_sq = max_items(B, H, tk, jfa::kSqKC);  // sum_b max(1, ceil(Lk_b / KC)) <= ceil(Tk / KC) + B
+  L.rowc = 3 * sizeof(PlanHeader);
   L.items_kv = L.rowc + align_up((size_t)tq * H * 8);
   L.items_q = L.items_kv + align_up((size_t)L.cap_kv * 16);
-  L.total = L.items_q + align_up((size_t)L.cap_q * 16);
+  L.items_sq = L.items_q + align_up((size_t)L.cap_q * 16);
+  L.gfirst = L.items_sq + align_up((size_t)L.cap_sq * 16);
+  L.dqp = L.gfirst + align_up((size_t)B * H * 4);
+  L.total = L.dqp + align_up((size_t)L.cap_sq * jfa::kSqQMax * D * 4);
   return L;
 }
 
@@ -192,8 +202,8 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.B = B;
   pa.H = H;
   pa.causal = causal ? 1 : 0;
-  pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::fwd_tile_rows(f32, D), jfa::kFwdTN, 0,
-                jfa::kPlanQueues};
+  pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::fwd_tile_rows(f32, D), jfa::kFwdTN,
+                jfa::kPassQ, jfa::kPlanQueues, -1, nullptr};
   hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 1, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
 
@@ -228,7 +238,7 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(lse, 4))
     return fail(JFA_ERR_INVALID_ARGUMENT, "out/dout/dq/dk/dv must be 16-byte aligned");
-  const BwdLayout L = bwd_layout(B, H, tq, tk);
+  const BwdLayout L = bwd_layout(B, H, tq, tk, D);
   if (ws_bytes < L.total)
     return fail(JFA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
   DeviceInfo* dev = nullptr;
@@ -243,9 +253,13 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.B = B;
   pa.H = H;
   pa.causal = causal ? 1 : 0;
-  pa.pass[0] = {(int4*)(w + L.items_kv), (PlanHeader*)(w + L.hdr_kv), (long)L.cap_kv, jfa::dkv_tile_rows(f32, D), jfa::kDkvTN, 1, jfa::kPlanQueues};
-  pa.pass[1] = {(int4*)(w + L.items_q), (PlanHeader*)(w + L.hdr_q), (long)L.cap_q, jfa::kDqTM, jfa::kDqTN, 0, jfa::kPlanQueues};
-  hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 2, st); });
+  pa.pass[0] = {(int4*)(w + L.items_kv), (PlanHeader*)(w + L.hdr_kv), (long)L.cap_kv, jfa::dkv_tile_rows(f32, D),
+                jfa::kDkvTN, jfa::kPassKV, jfa::kPlanQueues, jfa::kSqQMax, nullptr};
+  pa.pass[1] = {(int4*)(w + L.items_q), (PlanHeader*)(w + L.hdr_q), (long)L.cap_q, jfa::kDqTM, jfa::kDqTN,
+                jfa::kPassQ, jfa::kPlanQueues, jfa::kSqQMax, nullptr};
+  pa.pass[2] = {(int4*)(w + L.items_sq), (PlanHeader*)(w + L.hdr_sq), (long)L.cap_sq, jfa::kSqQMax, jfa::kSqKC,
+                jfa::kPassSQ, jfa::kPlanQueues, -1, (int*)(w + L.gfirst)};
+  hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 3, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
 
   jfa::BwdArgs a{};
@@ -267,17 +281,25 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a.scale = (float)(1.0 / std::sqrt((double)D));
   a.scale2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
   a.tq = (long)tq;
-  jfa::BwdArgs a_kv = a, a_q = a;
+  a.B = B;
+  a.gfirst = (int*)(w + L.gfirst);
+  a.dqp = (float*)(w + L.dqp);
+  jfa::BwdArgs a_kv = a, a_q = a, a_sq = a;
   a_kv.items = (const int4*)(w + L.items_kv);
   a_kv.hdr = (PlanHeader*)(w + L.hdr_kv);
   a_q.items = (const int4*)(w + L.items_q);
   a_q.hdr = (PlanHeader*)(w + L.hdr_q);
+  a_sq.items = (const int4*)(w + L.items_sq);
+  a_sq.hdr = (PlanHeader*)(w + L.hdr_sq);
   const bool has_bias = bias != nullptr;
   e = timed(kKindDelta, st, [&] { return jfa::launch_delta(f32, D, a_kv, st); });
   if (e == hipSuccess)
     e = timed(kKindDkdv, st, [&] { return jfa::launch_dkdv(f32, D, a_kv, has_bias, (long)L.cap_kv, dev->num_cus, st); });
   if (e == hipSuccess)
     e = timed(kKindDq, st, [&] { return jfa::launch_dq(f32, D, a_q, has_bias, (long)L.cap_q, dev->num_cus, st); });
+  if (e == hipSuccess)
+    e = timed(kKindSq, st, [&] { return jfa::launch_sq(f32, D, a_sq, has_bias, (long)L.cap_sq, dev->num_cus, st); });
+  if (e == hipSuccess) e = timed(kKindSqReduce, st, [&] { return jfa::launch_sq_reduce(f32, D, a_sq, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -287,6 +309,7 @@ bool tile_of(int kernel, int D, int dtype, int* tm, int* tn) {
     case JFA_KERNEL_FWD: *tm = jfa::fwd_tile_rows(dtype == JFA_DTYPE_F32, D); *tn = jfa::kFwdTN; return true;
     case JFA_KERNEL_BWD_DKDV: *tm = jfa::dkv_tile_rows(dtype == JFA_DTYPE_F32, D); *tn = jfa::kDkvTN; return true;
     case JFA_KERNEL_BWD_DQ: *tm = jfa::kDqTM; *tn = jfa::kDqTN; return true;
+    case JFA_KERNEL_BWD_SQ: *tm = jfa::kSqQMax; *tn = jfa::kSqKC; return true;
     default: return false;
   }
 }
@@ -304,7 +327,7 @@ size_t jfa_fwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, 
 size_t jfa_bwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, int D, int causal) {
   (void)causal;
   if (!valid_sizes(B, H, total_q, total_kv, D)) return 0;
-  return bwd_layout(B, H, total_q, total_kv).total;
+  return bwd_layout(B, H, total_q, total_kv, D).total;
 }
 
 jfa_status jfa_fwd(const void* q, const void* k, const void* v, const int32_t* q_offsets, const int32_t* kv_offsets,
@@ -362,8 +385,9 @@ size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv,
   if (!valid_sizes(B, H, total_q, total_kv, D) || (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_F32) ||
       !tile_of(kernel, D, dtype, &tm, &tn))
     return 0;
-  const int64_t cap = kernel == JFA_KERNEL_BWD_DKDV ? max_items(B, H, total_kv, tn) : max_items(B, H, total_q, tm);
-  return sizeof(PlanHeader) + align_up((size_t)cap * 16);
+  const int64_t cap = kernel == JFA_KERNEL_BWD_DKDV || kernel == JFA_KERNEL_BWD_SQ ? max_items(B, H, total_kv, tn)
+                                                                                  : max_items(B, H, total_q, tm);
+  return sizeof(PlanHeader) + align_up((size_t)cap * 16) + (kernel == JFA_KERNEL_BWD_SQ ? align_up((size_t)B * H * 4) : 0);
 }
 
 jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D, int dtype,
@@ -386,8 +410,15 @@ jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, i
   pa.B = B;
   pa.H = H;
   pa.causal = causal ? 1 : 0;
-  pa.pass[0] = {(int4*)(w + sizeof(PlanHeader)), (PlanHeader*)w, (long)((workspace_bytes - sizeof(PlanHeader)) / 16), tm, tn,
-                kernel == JFA_KERNEL_BWD_DKDV ? 1 : 0, jfa::kPlanQueues};
+  // Layout: header, items, and for the short-query pass the [B*H] group table
+  // after the largest list the sizes allow.
+  const size_t tail = kernel == JFA_KERNEL_BWD_SQ ? align_up((size_t)B * H * 4) : 0;
+  if (workspace_bytes < sizeof(PlanHeader) + tail) return fail(JFA_ERR_WORKSPACE, "workspace too small");
+  const int kind = kernel == JFA_KERNEL_BWD_DKDV ? jfa::kPassKV : (kernel == JFA_KERNEL_BWD_SQ ? jfa::kPassSQ : jfa::kPassQ);
+  const int short_q = (kernel == JFA_KERNEL_BWD_DKDV || kernel == JFA_KERNEL_BWD_DQ) ? jfa::kSqQMax : -1;
+  pa.pass[0] = {(int4*)(w + sizeof(PlanHeader)), (PlanHeader*)w,
+                (long)((workspace_bytes - sizeof(PlanHeader) - tail) / 16), tm, tn, kind, jfa::kPlanQueues, short_q,
+                tail ? (int*)(w + workspace_bytes - tail) : nullptr};
   hipError_t e = jfa::launch_plan(pa, 1, (hipStream_t)stream);
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
   return ok();

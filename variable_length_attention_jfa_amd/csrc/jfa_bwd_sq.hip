@@ -1,0 +1,356 @@
+// Backward pass for short-query sequences (at most 64 queries, e.g. a few
+// new events attending to a long history) on gfx950.
+//
+// The split backward ("Jagged Flash Attention (JFA)", section "Four
+// generations", item 2) computes dK/dV per key tile and dQ per query tile in
+// two passes, so K and V are read twice and S = QK^T, dP = dO V^T are formed
+// twice. When a sequence has at most 64 queries they fit one workgroup, which
+// can then own the whole sequence's backward: one item per (b, h, chunk of
+// 1024 keys) reads each K, V row once, forms S, P, dP, dS once, stores the
+// chunk's dK, dV directly and accumulates a partial dQ over its keys. The
+// partials of a sequence's chunks are summed in list order by a second small
+// kernel, so dQ is deterministic and no atomics are used. The same page
+// counts asymmetric query/key lengths among the method's targets (section
+// "Definition").
+//
+// Per 128-key tile, wave w owns keys 32w .. 32w+31 of the tile:
+//   S = Q K^T, dP = dO V^T   (Q, dO, K from LDS; V fragments in VGPRs)
+//   P = exp2(S * scale * log2(e) - lse2 (+ bias)), dS = P (dP - Delta),
+//   both written to LDS as [key][query] tiles (so no score block stays in
+//   registers across the phases)
+//   dV^T += dO^T P^T, dK^T += Q^T dS^T, stored once per tile
+//   dQ^T += K^T dS^T split over the waves by (query half, 32-column block of
+//   D), K and dS read transposed from LDS.
+// Rows past a sequence's end load as zeros; keys past the end and, with the
+// causal mask, keys after the query get P = 0.
+#include "jfa_common.h"
+#include "jfa_kernels.h"
+
+namespace jfa {
+
+template <typename T, int D>
+struct SqTiles {
+  static constexpr int QM = kSqQMax;  // query rows (two halves of 32)
+  static constexpr int KT = kSqKT;    // keys per tile (4 waves x 32)
+  static constexpr int KC = kSqKC;    // keys per item
+  static constexpr int THREADS = 256;
+  using TL = Tile<T, D>;   // Q, dO, K rows
+  using PL = Tile<T, QM>;  // P, dS: one row of QM queries per key
+  static constexpr int ROWB = TL::ROWB;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int NKBUF = sizeof(T) == 2 ? 2 : 1;  // K tile buffers (fp32 rows leave room for one)
+  static constexpr int QOFF = 0;
+  static constexpr int DOFF = QM * ROWB;
+  static constexpr int KOFF = 2 * QM * ROWB;
+  static constexpr int POFF = KOFF + NKBUF * KT * ROWB;
+  static constexpr int SOFF = POFF + KT * PL::ROWB;
+  static constexpr int RCOFF = SOFF + KT * PL::ROWB;   // (lse2, Delta) per query row
+  static constexpr int BIAS_OFF = RCOFF + QM * 8;
+  static constexpr int LDS = BIAS_OFF + 1040;
+  static constexpr int KCPT = KT * CPR / THREADS;       // K tile pieces per thread
+  static constexpr int QCPT = (2 * QM * CPR + THREADS - 1) / THREADS;  // Q and dO pieces per thread
+  static constexpr int NDQ = 2 * (D / 32);              // 32x32 dQ blocks
+  static_assert((KT * CPR) % THREADS == 0, "tile pieces divide the workgroup");
+  static_assert(KC % KT == 0, "chunks are whole tiles");
+};
+
+// Fragment from one row of a [key][query] tile for a 32x32x16 MFMA operand
+// whose k runs over queries: k-slots = queries 16c + {4g .. 4g+3, 8+4g ..
+// 8+4g+3}, the order of the transposed fragment on the other side.
+__device__ __forceinline__ Frag<bf16> pfrag(const lds_t* tile, int row, int c, int g, bf16*) {
+  using PL = Tile<bf16, kSqQMax>;
+  const i32x2 x = *(const __attribute__((address_space(3))) i32x2*)(tile + PL::byte(row, (16 * c + 4 * g) * 2));
+  const i32x2 y = *(const __attribute__((address_space(3))) i32x2*)(tile + PL::byte(row, (16 * c + 8 + 4 * g) * 2));
+  const bf16x4 x4 = __builtin_bit_cast(bf16x4, x), y4 = __builtin_bit_cast(bf16x4, y);
+  Frag<bf16> f;
+  f.v = (bf16x8){x4[0], x4[1], x4[2], x4[3], y4[0], y4[1], y4[2], y4[3]};
+  return f;
+}
+__device__ __forceinline__ Frag<float> pfrag(const lds_t* tile, int row, int c, int g, float*) {
+  using PL = Tile<float, kSqQMax>;
+  Frag<float> f;
+  f.lo = *(const __attribute__((address_space(3))) f32x4*)(tile + PL::byte(row, (16 * c + 4 * g) * 4));
+  f.hi = *(const __attribute__((address_space(3))) f32x4*)(tile + PL::byte(row, (16 * c + 8 + 4 * g) * 4));
+  return f;
+}
+
+// Four consecutive values of one row of a [key][query] tile (elements 4a ..
+// 4a+3 of a 32x32 result held by a lane of half g are queries 8a+4g .. +3).
+__device__ __forceinline__ void put4(lds_t* tile, int row, int q, float a, float b, float c, float d, bf16*) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  bf16x2 lo = {(bf16)a, (bf16)b}, hi = {(bf16)c, (bf16)d};
+  *(__attribute__((address_space(3))) i32x2*)(tile + Tile<bf16, kSqQMax>::byte(row, q * 2)) =
+      (i32x2){__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+}
+__device__ __forceinline__ void put4(lds_t* tile, int row, int q, float a, float b, float c, float d, float*) {
+  *(__attribute__((address_space(3))) f32x4*)(tile + Tile<float, kSqQMax>::byte(row, q * 4)) = (f32x4){a, b, c, d};
+}
+
+template <typename T, int D, bool BIAS>
+__global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
+  using C = SqTiles<T, D>;
+  constexpr int QM = C::QM, KT = C::KT, KC = C::KC, ES = (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ QueueCursor qcur;
+  lds_t* lds = (lds_t*)smem;
+  lds_t* qt = lds + C::QOFF;
+  lds_t* dot = lds + C::DOFF;
+  lds_t* pt = lds + C::POFF;  // P   [key][query]
+  lds_t* st = lds + C::SOFF;  // dS  [key][query]
+  __attribute__((address_space(3))) float* rc = (__attribute__((address_space(3))) float*)(lds + C::RCOFF);
+  __attribute__((address_space(3))) float* bias_lds = (__attribute__((address_space(3))) float*)(lds + C::BIAS_OFF);
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.H;
+  const uint32_t gstride = (uint32_t)H * C::ROWB;
+  load_queues(a.hdr, &qcur);
+  TicketState tk;
+
+  for (;;) {
+    const int it = next_item(a.hdr, &qcur, tk);
+    if (it < 0) break;
+    const int4 item = a.items[it];
+    const int b = uni(item.x), h = uni(item.y), chunk = uni(item.z);
+    const int q0 = uni(a.q_off[b]), Lq = uni(a.q_off[b + 1]) - q0;
+    const int k0 = uni(a.kv_off[b]), Lk = uni(a.kv_off[b + 1]) - k0;
+    const int key_c0 = chunk * KC;                                   // first key of the chunk
+    const int nt = Lk > key_c0 ? cdiv(min(KC, Lk - key_c0), KT) : 0;  // key tiles in the chunk
+    const int nqs = cdiv(min(Lq, QM), 32);                           // query halves in use
+
+    const size_t qrow = ((size_t)q0 * H + h) * C::ROWB, krow = ((size_t)k0 * H + h) * C::ROWB;
+    const View qv = seq_view((const char*)a.q + qrow, Lq, gstride, C::ROWB);
+    const View dov = seq_view((const char*)a.dout + qrow, Lq, gstride, C::ROWB);
+    const View rcv = seq_view(a.rowc + (size_t)q0 * H + h, Lq, 8 * H, 8);
+
+    if (BIAS) {
+      for (int i = tid; i < kBiasLen; i += C::THREADS) bias_lds[i] = a.bias[h * kBiasLen + i] * kLog2e;
+    }
+    // Q, dO (rows past Lq read as zeros) and the row constants into LDS.
+    {
+      i32x4 r[C::QCPT];
+#pragma unroll
+      for (int c = 0; c < C::QCPT; ++c) {
+        const int x = tid + C::THREADS * c;
+        if (x < 2 * QM * C::CPR) {
+          const int y = x % (QM * C::CPR), row = y / C::CPR, col = y % C::CPR;
+          r[c] = ld16(x < QM * C::CPR ? qv : dov, (uint32_t)row * gstride + col * 16);
+        }
+      }
+      i32x2 rr = {};
+      if (tid < QM) rr = ld8(rcv, (uint32_t)tid * 8 * H);
+#pragma unroll
+      for (int c = 0; c < C::QCPT; ++c) {
+        const int x = tid + C::THREADS * c;
+        if (x < 2 * QM * C::CPR) {
+          const int y = x % (QM * C::CPR), row = y / C::CPR, col = y % C::CPR;
+          *(__attribute__((address_space(3))) i32x4*)((x < QM * C::CPR ? qt : dot) + C::TL::chunk(row, col)) = r[c];
+        }
+      }
+      if (tid < QM) *(__attribute__((address_space(3))) i32x2*)((lds_t*)rc + 8 * tid) = rr;
+    }
+
+    // K tiles through registers into two LDS buffers; V fragments in VGPRs.
+    auto kview = [&](int t) {
+      const int r0 = key_c0 + t * KT;
+      return seq_view((const char*)a.k + krow + (size_t)r0 * gstride, min(KT, Lk - r0), gstride, C::ROWB);
+    };
+    auto kload = [&](int t, i32x4* r) {
+      const View kv = kview(t);
+#pragma unroll
+      for (int c = 0; c < C::KCPT; ++c) {
+        const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
+        r[c] = ld16(kv, (uint32_t)row * gstride + col * 16);
+      }
+    };
+    auto kstore = [&](int t, const i32x4* r) {
+      lds_t* kt = lds + C::KOFF + (t % C::NKBUF) * KT * C::ROWB;
+#pragma unroll
+      for (int c = 0; c < C::KCPT; ++c) {
+        const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
+        *(__attribute__((address_space(3))) i32x4*)(kt + C::TL::chunk(row, col)) = r[c];
+      }
+    };
+    auto vload = [&](int t, Frag<T>* vf) {
+      const int kw0 = key_c0 + t * KT + 32 * w;
+      const View vv = seq_view((const char*)a.v + krow + (size_t)kw0 * gstride, max(0, min(32, Lk - kw0)), gstride, C::ROWB);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) vf[kk] = gfrag(vv, (uint32_t)l32 * gstride + (16 * kk + 8 * g) * ES, (T*)0);
+    };
+
+    i32x4 kr[C::KCPT];
+    Frag<T> vf[D / 16];
+    if (nt > 0) {
+      kload(0, kr);
+      vload(0, vf);
+      kstore(0, kr);
+    }
+    wait_vmem();
+    __syncthreads();
+
+    f32x16 dq[(C::NDQ + 3) / 4];
+#pragma unroll
+    for (int x = 0; x < (C::NDQ + 3) / 4; ++x) dq[x] = (f32x16){};
+
+    for (int t = 0; t < nt; ++t) {
+      if (t + 1 < nt) kload(t + 1, kr);
+      const lds_t* kt = lds + C::KOFF + (t % C::NKBUF) * KT * C::ROWB;
+      const int kw0 = key_c0 + t * KT + 32 * w;  // first key of this wave
+      const int kj = kw0 + l32;                  // this lane's key
+      const int krow_t = 32 * w + l32;           // its row in the tile
+      // S, dP of each query half (lane = key, element i = query res_row(i, g))
+      // -> P, dS into LDS, row = key.
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        if (qs < nqs) {
+          f32x16 sc = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) {
+            mma(sc, lfrag<D>(qt, 32 * qs + l32, 16 * kk + 8 * g, (T*)0), lfrag<D>(kt, krow_t, 16 * kk + 8 * g, (T*)0));
+            mma(dp, lfrag<D>(dot, 32 * qs + l32, 16 * kk + 8 * g, (T*)0), vf[kk]);
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qi = 32 * qs + res_row(i, g);
+            float x = sc[i] * a.scale2 - rc[2 * qi];
+            if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+            float p = __builtin_amdgcn_exp2f(x);
+            if (kj >= Lk || (a.causal && kj > qi)) p = 0.f;
+            sc[i] = p;
+            dp[i] = p * (dp[i] - rc[2 * qi + 1]);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int q = 32 * qs + 8 * r + 4 * g;
+            put4(pt, krow_t, q, sc[4 * r], sc[4 * r + 1], sc[4 * r + 2], sc[4 * r + 3], (T*)0);
+            put4(st, krow_t, q, dp[4 * r], dp[4 * r + 1], dp[4 * r + 2], dp[4 * r + 3], (T*)0);
+          }
+        }
+      }
+      // V of this tile is no longer needed: its registers take the next
+      // tile's V, whose load then overlaps the rest of this tile.
+      if (t + 1 < nt) vload(t + 1, vf);
+      __syncthreads();
+      // dV^T, dK^T of this wave's 32 keys (rows it wrote itself): lane holds
+      // rows d = 32db + res_row(i,g) of key kj.
+      {
+        const int nk = max(0, min(32, Lk - kw0));
+        const View dvv = seq_view((char*)a.dv + krow + (size_t)kw0 * gstride, nk, gstride, C::ROWB);
+        const View dkv = seq_view((char*)a.dk + krow + (size_t)kw0 * gstride, nk, gstride, C::ROWB);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          f32x16 av = (f32x16){}, ak = (f32x16){};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if (c < 2 * nqs) {
+              mma(av, tfrag<D>(dot, 16 * c, 32 * db, lane, (T*)0), pfrag(pt, krow_t, c, g, (T*)0));
+              mma(ak, tfrag<D>(qt, 16 * c, 32 * db, lane, (T*)0), pfrag(st, krow_t, c, g, (T*)0));
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int d = 32 * db + 8 * r + 4 * g;
+            const uint32_t off = (uint32_t)l32 * gstride + d * ES;
+            store4(dvv, off, av[4 * r], av[4 * r + 1], av[4 * r + 2], av[4 * r + 3], (T*)0);
+            store4(dkv, off, ak[4 * r] * a.scale, ak[4 * r + 1] * a.scale, ak[4 * r + 2] * a.scale,
+                   ak[4 * r + 3] * a.scale, (T*)0);
+          }
+        }
+      }
+      // dQ^T += K^T dS^T over the tile's keys; block x of this wave is
+      // (query half x % 2, column block x / 2), x = w, w + 4, ...
+#pragma unroll
+      for (int xi = 0; xi < (C::NDQ + 3) / 4; ++xi) {
+        const int x = w + 4 * xi;
+        if (x < C::NDQ && (x % 2) < nqs) {
+          const int qs = x % 2, db = x / 2;
+#pragma unroll
+          for (int kc = 0; kc < KT / 16; ++kc)
+            mma(dq[xi], tfrag<D>(kt, 16 * kc, 32 * db, lane, (T*)0), tfrag<QM>(st, 16 * kc, 32 * qs, lane, (T*)0));
+        }
+      }
+      if (C::NKBUF == 1) __syncthreads();  // the only K buffer is refilled next
+      if (t + 1 < nt) kstore(t + 1, kr);
+      __syncthreads();
+    }
+
+    // Partial dQ of this chunk (unscaled), [64 rows][D] fp32 at item slot it.
+    float* part = a.dqp + (size_t)it * QM * D;
+#pragma unroll
+    for (int xi = 0; xi < (C::NDQ + 3) / 4; ++xi) {
+      const int x = w + 4 * xi;
+      if (x < C::NDQ) {
+        const int qs = x % 2, db = x / 2, q = 32 * qs + l32;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = 32 * db + 8 * r + 4 * g;
+          *(f32x4*)(part + (size_t)q * D + d) = (f32x4){dq[xi][4 * r], dq[xi][4 * r + 1], dq[xi][4 * r + 2], dq[xi][4 * r + 3]};
+        }
+      }
+    }
+  }
+}
+
+// dQ of each short-query sequence: the sum, in list order, of its chunks'
+// partials, times the softmax scale. One workgroup per (b, h).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void jfa_sq_reduce_kernel(BwdArgs a) {
+  constexpr int QM = kSqQMax;
+  const int gi = blockIdx.x, b = gi / a.H, h = gi % a.H;
+  const int first = a.gfirst[gi];
+  if (first < 0) return;
+  const int q0 = a.q_off[b], Lq = min(a.q_off[b + 1] - q0, QM);
+  const int Lk = a.kv_off[b + 1] - a.kv_off[b];
+  const int n = max(1, cdiv(Lk, kSqKC));
+  const size_t qstride = (size_t)a.H * D;  // elements between consecutive tokens
+  for (int e = threadIdx.x * 4; e < Lq * D; e += 256 * 4) {
+    const int q = e / D, d = e % D;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < n; ++t) s += *(const f32x4*)(a.dqp + (size_t)(first + t) * QM * D + e);
+    T* dst = (T*)a.dq + ((size_t)(q0 + q) * a.H + h) * D + d;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[k] = (T)(s[k] * a.scale);
+  }
+}
+
+template <typename T, int D, bool BIAS>
+static hipError_t launch_sq_t(const BwdArgs& a, long max_items, int num_cus, hipStream_t st) {
+  static int occ = 0;
+  if (occ == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, jfa_sq_kernel<T, D, BIAS>, 256, 0) != hipSuccess || occ < 1)
+      occ = 1;
+  }
+  const long g = max(1L, min(max_items, (long)num_cus * occ));
+  hipLaunchKernelGGL((jfa_sq_kernel<T, D, BIAS>), dim3((unsigned)g), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_sq_reduce_t(const BwdArgs& a, hipStream_t st) {
+  const long n = (long)a.B * a.H;
+  if (n > 0) hipLaunchKernelGGL((jfa_sq_reduce_kernel<T, D>), dim3((unsigned)n), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+#define JFA_SQ_DISPATCH(F32, D, CALL)                                            \
+  do {                                                                           \
+    if (F32) {                                                                   \
+      if ((D) == 32) { using T = float; constexpr int DD = 32; return CALL; }    \
+      if ((D) == 64) { using T = float; constexpr int DD = 64; return CALL; }    \
+      return hipErrorInvalidValue; /* fp32 with D = 128 is rejected on the host */ \
+    }                                                                            \
+    if ((D) == 32) { using T = bf16; constexpr int DD = 32; return CALL; }       \
+    if ((D) == 64) { using T = bf16; constexpr int DD = 64; return CALL; }       \
+    { using T = bf16; constexpr int DD = 128; return CALL; }                     \
+  } while (0)
+
+hipError_t launch_sq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
+  if (bias) JFA_SQ_DISPATCH(f32, D, (launch_sq_t<T, DD, true>(a, max_items, num_cus, st)));
+  JFA_SQ_DISPATCH(f32, D, (launch_sq_t<T, DD, false>(a, max_items, num_cus, st)));
+}
+
+hipError_t launch_sq_reduce(bool f32, int D, const BwdArgs& a, hipStream_t st) {
+  JFA_SQ_DISPATCH(f32, D, (launch_sq_reduce_t<T, DD>(a, st)));
+}
+
+}  // namespace jfa

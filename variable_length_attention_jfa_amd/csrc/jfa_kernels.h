@@ -44,15 +44,23 @@ struct BwdArgs {
   float scale;         // 1/sqrt(D)
   float scale2;        // scale * log2(e)
   long tq;             // query tokens (rows of rowc per head)
+  int B;
+  int* gfirst;         // short-query pass: [B*H] list position of chunk 0 of each (b, h), -1 if none
+  float* dqp;          // short-query pass: per item, a [64, D] fp32 partial dQ
 };
+
+// Pass kinds of the work lists.
+enum PlanKind { kPassQ = 0, kPassKV = 1, kPassSQ = 2 };
 
 struct PlanPass {
   int4* items;
   PlanHeader* hdr;
   long capacity;  // items that fit the workspace
-  int TM, TN;     // query rows / keys per tile and per visited block
-  int kv_pass;
+  int TM, TN;     // query rows / keys per tile and per visited block (sq: keys per chunk)
+  int kind;       // PlanKind
   int nq;         // queues (one per XCD)
+  int short_q;    // q and kv passes: sequences with Lq <= short_q get no items (-1: none)
+  int* gfirst;    // sq pass: [B*H] list position of chunk 0 of each (b, h), -1 if none
 };
 
 constexpr int kPlanQueues = 8;  // MI355X: 8 XCDs
@@ -61,8 +69,12 @@ struct PlanArgs {
   const int* q_off;
   const int* kv_off;
   int B, H, causal;
-  PlanPass pass[2];
+  PlanPass pass[3];
 };
+
+// Short-query backward: sequences with at most kSqQMax queries are owned whole
+// by one workgroup per chunk of kSqKC keys.
+constexpr int kSqQMax = 64, kSqKC = 1024, kSqKT = 128;
 
 // Tile shapes (query rows x keys) of each kernel. The forward's waves per
 // workgroup (32 query rows each) depend on the element type and D.
@@ -82,6 +94,8 @@ hipError_t launch_fwd(bool f32, int D, const FwdArgs& a, bool bias, long max_ite
 hipError_t launch_delta(bool f32, int D, const BwdArgs& a, hipStream_t st);
 hipError_t launch_dkdv(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
 hipError_t launch_dq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
+hipError_t launch_sq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
+hipError_t launch_sq_reduce(bool f32, int D, const BwdArgs& a, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, int npass, hipStream_t st);
 hipError_t launch_scan(const int* lengths, int B, int* offsets, hipStream_t st);
 

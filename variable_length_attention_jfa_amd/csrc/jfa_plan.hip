@@ -8,7 +8,11 @@
 //
 //   tiles  : q pass  -> (b, t) with t < ceil(Lq_b / TM)
 //            kv pass -> (b, t) with t < ceil(Lk_b / TN)
-//   cost   : key blocks (q pass) or query blocks (kv pass) the tile visits
+//            sq pass -> (b, c) with c < max(1, ceil(Lk_b / TN)), only for
+//                       sequences with Lq_b <= 64 (which the backward's q and
+//                       kv passes then skip)
+//   cost   : key blocks (q pass) or query blocks (kv pass) the tile visits;
+//            keys in the chunk (sq pass)
 //   groups : the tiles of one (b, h); group cost = sum of its tile costs
 //   order  : groups by cost descending, then b, then h; group rank g is dealt
 //            to queue snake(g) (0..Q-1, Q-1..0, ...), one queue per XCD, so
@@ -32,11 +36,14 @@ constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanMaxB = 8192;
 
 __device__ __forceinline__ int plan_tiles(int Lq, int Lk, const PlanPass& p) {
-  return p.kv_pass ? cdiv(Lk, p.TN) : cdiv(Lq, p.TM);
+  if (p.kind == kPassSQ) return Lq <= kSqQMax ? max(1, cdiv(Lk, p.TN)) : 0;
+  if (Lq <= p.short_q) return 0;
+  return p.kind == kPassKV ? cdiv(Lk, p.TN) : cdiv(Lq, p.TM);
 }
 
 __device__ __forceinline__ int plan_cost(int Lq, int Lk, int t, const PlanPass& p, int causal) {
-  if (!p.kv_pass) {
+  if (p.kind == kPassSQ) return max(0, min(p.TN, Lk - t * p.TN));
+  if (p.kind == kPassQ) {
     if (!causal) return cdiv(Lk, p.TN);
     return cdiv(min(min((t + 1) * p.TM, Lq), Lk), p.TN);
   }
@@ -56,7 +63,7 @@ __device__ __forceinline__ int plan_cost(int Lq, int Lk, int t, const PlanPass& 
 // the n - t1 tiles of larger cost and the t - t0 tiles of equal cost before it.
 __device__ __forceinline__ int plan_pos(int Lq, int Lk, int t, int n, const PlanPass& p, int causal) {
   const int lmin = min(Lq, Lk);
-  if (!causal || p.kv_pass || lmin == 0) return t;
+  if (!causal || p.kind != kPassQ || lmin == 0) return t;
   const int c = plan_cost(Lq, Lk, t, p, causal);
   const int t0 = ((c - 1) * p.TN) / p.TM;
   const int t1 = lmin > c * p.TN ? min((c * p.TN) / p.TM, n) : n;
@@ -128,6 +135,8 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
     qtotal[tid] = 0;
     qcarry[tid] = 0;
   }
+  if (p.gfirst)
+    for (int x = tid; x < B * H; x += kPlanThreads) p.gfirst[x] = -1;
   __syncthreads();
 
   // 2. bitonic sort of the P keys (ascending: cost descending, then b)
@@ -196,6 +205,7 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
     const int pos = ex - excl[x * per_q];
     gbase[tid] = qstart[x] + qcarry[x] + pos;  // first item of this group in the list
     gbh[tid] = make_int2(b, g < G ? g % H : 0);
+    if (p.gfirst && n > 0) p.gfirst[b * H + g % H] = gbase[tid];  // chunk 0 is first (costs non-increasing)
     __syncthreads();
     if (i == per_q - 1) qcarry[x] += pos + n;  // last group of queue x in this chunk
     for (int f = tid; f < tot; f += kPlanThreads) {
