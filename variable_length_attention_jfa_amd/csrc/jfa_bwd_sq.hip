@@ -13,14 +13,23 @@
 // counts asymmetric query/key lengths among the method's targets (section
 // "Definition").
 //
-// Per 128-key tile, wave w owns keys 32w .. 32w+31 of the tile:
-//   S = Q K^T, dP = dO V^T   (Q, dO, K from LDS; V fragments in VGPRs)
+// Per 64-key tile, the four waves split the 64 x 64 (key, query) block into
+// 32 x 32 quarters, wave w taking key half w & 1 and query half w >> 1:
+//   S = Q K^T, dP = dO V^T   (Q, dO, K, V all from LDS)
 //   P = exp2(S * scale * log2(e) - lse2 (+ bias)), dS = P (dP - Delta),
-//   both written to LDS as [key][query] tiles (so no score block stays in
-//   registers across the phases)
-//   dV^T += dO^T P^T, dK^T += Q^T dS^T, stored once per tile
-//   dQ^T += K^T dS^T split over the waves by (query half, 32-column block of
-//   D), K and dS read transposed from LDS.
+//   both written as [key][query] tiles into the LDS that held V
+//   dV^T += dO^T P^T, dK^T += Q^T dS^T for the key half, the two waves of a
+//   key half taking alternate 32-column blocks of D
+//   dQ^T += K^T dS^T per (query half, column block), K and dS read
+//   transposed from LDS.
+// The tile's dV and dK are then staged in the LDS of V and K and leave as
+// whole rows, 16 bytes per lane: written straight from the MFMA result
+// layout each store instruction would touch 32 rows with a few bytes each,
+// and the memory system runs out of requests long before it runs out of
+// bytes. K and V arrive the same way, in whole rows, one tile ahead, through
+// registers. The LDS of one workgroup (Q, dO, K, V or P and dS, row
+// constants, bias) stays under 80 KB at D = 128 in bf16, so two workgroups
+// share a CU.
 // Rows past a sequence's end load as zeros; keys past the end and, with the
 // causal mask, keys after the query get P = 0.
 #include "jfa_common.h"
@@ -31,26 +40,30 @@ namespace jfa {
 template <typename T, int D>
 struct SqTiles {
   static constexpr int QM = kSqQMax;  // query rows (two halves of 32)
-  static constexpr int KT = kSqKT;    // keys per tile (4 waves x 32)
+  static constexpr int KT = kSqKT;    // keys per tile (two halves of 32)
   static constexpr int KC = kSqKC;    // keys per item
   static constexpr int THREADS = 256;
   using TL = Tile<T, D>;   // Q, dO, K rows
   using PL = Tile<T, QM>;  // P, dS: one row of QM queries per key
   static constexpr int ROWB = TL::ROWB;
   static constexpr int CPR = ROWB / 16;
-  static constexpr int NKBUF = sizeof(T) == 2 ? 2 : 1;  // K tile buffers (fp32 rows leave room for one)
   static constexpr int QOFF = 0;
   static constexpr int DOFF = QM * ROWB;
   static constexpr int KOFF = 2 * QM * ROWB;
-  static constexpr int POFF = KOFF + NKBUF * KT * ROWB;
-  static constexpr int SOFF = POFF + KT * PL::ROWB;
-  static constexpr int RCOFF = SOFF + KT * PL::ROWB;   // (lse2, Delta) per query row
+  static constexpr int VOFF = KOFF + KT * ROWB;         // V, then P and dS, then staged dV
+  static constexpr int VREG = KT * ROWB > 2 * KT * PL::ROWB ? KT * ROWB : 2 * KT * PL::ROWB;
+  static constexpr int POFF = VOFF;
+  static constexpr int SOFF = VOFF + KT * PL::ROWB;
+  static constexpr int RCOFF = VOFF + VREG;            // (lse2, Delta) per query row
   static constexpr int BIAS_OFF = RCOFF + QM * 8;
   static constexpr int LDS = BIAS_OFF + 1040;
-  static constexpr int KCPT = KT * CPR / THREADS;       // K tile pieces per thread
+  static constexpr int KCPT = KT * CPR / THREADS;       // K (or V) tile pieces per thread
   static constexpr int QCPT = (2 * QM * CPR + THREADS - 1) / THREADS;  // Q and dO pieces per thread
-  static constexpr int NDQ = 2 * (D / 32);              // 32x32 dQ blocks
+  static constexpr int NDB = D / 32;                    // 32-column blocks of D
+  static constexpr int NDB2 = (NDB + 1) / 2;            // column blocks per wave
+  static constexpr int NDQ = 2 * NDB;                   // 32x32 dQ blocks
   static_assert((KT * CPR) % THREADS == 0, "tile pieces divide the workgroup");
+  static_assert((QM * CPR) % THREADS == 0, "Q and dO pieces fill whole passes of the workgroup");
   static_assert(KC % KT == 0, "chunks are whole tiles");
 };
 
@@ -74,16 +87,19 @@ __device__ __forceinline__ Frag<float> pfrag(const lds_t* tile, int row, int c, 
   return f;
 }
 
-// Four consecutive values of one row of a [key][query] tile (elements 4a ..
-// 4a+3 of a 32x32 result held by a lane of half g are queries 8a+4g .. +3).
-__device__ __forceinline__ void put4(lds_t* tile, int row, int q, float a, float b, float c, float d, bf16*) {
+// Four consecutive values (columns col .. col+3) of one row of a tile of W
+// columns. In a 32x32 result held by a lane of half g, elements 4a .. 4a+3
+// are columns 8a+4g .. +3 of the lane's row.
+template <int W>
+__device__ __forceinline__ void put4(lds_t* tile, int row, int col, float a, float b, float c, float d, bf16*) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   bf16x2 lo = {(bf16)a, (bf16)b}, hi = {(bf16)c, (bf16)d};
-  *(__attribute__((address_space(3))) i32x2*)(tile + Tile<bf16, kSqQMax>::byte(row, q * 2)) =
+  *(__attribute__((address_space(3))) i32x2*)(tile + Tile<bf16, W>::byte(row, col * 2)) =
       (i32x2){__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
 }
-__device__ __forceinline__ void put4(lds_t* tile, int row, int q, float a, float b, float c, float d, float*) {
-  *(__attribute__((address_space(3))) f32x4*)(tile + Tile<float, kSqQMax>::byte(row, q * 4)) = (f32x4){a, b, c, d};
+template <int W>
+__device__ __forceinline__ void put4(lds_t* tile, int row, int col, float a, float b, float c, float d, float*) {
+  *(__attribute__((address_space(3))) f32x4*)(tile + Tile<float, W>::byte(row, col * 4)) = (f32x4){a, b, c, d};
 }
 
 template <typename T, int D, bool BIAS>
@@ -95,6 +111,8 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
   lds_t* lds = (lds_t*)smem;
   lds_t* qt = lds + C::QOFF;
   lds_t* dot = lds + C::DOFF;
+  lds_t* kt = lds + C::KOFF;  // K tile, then staged dK
+  lds_t* vt = lds + C::VOFF;  // V tile, then P and dS, then staged dV
   lds_t* pt = lds + C::POFF;  // P   [key][query]
   lds_t* st = lds + C::SOFF;  // dS  [key][query]
   __attribute__((address_space(3))) float* rc = (__attribute__((address_space(3))) float*)(lds + C::RCOFF);
@@ -134,7 +152,8 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
         const int x = tid + C::THREADS * c;
         if (x < 2 * QM * C::CPR) {
           const int y = x % (QM * C::CPR), row = y / C::CPR, col = y % C::CPR;
-          r[c] = ld16(x < QM * C::CPR ? qv : dov, (uint32_t)row * gstride + col * 16);
+          // pieces c * THREADS .. are all Q or all dO (a whole number of passes per tile)
+          r[c] = ld16(c * C::THREADS < QM * C::CPR ? qv : dov, (uint32_t)row * gstride + col * 16);
         }
       }
       i32x2 rr = {};
@@ -144,46 +163,48 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
         const int x = tid + C::THREADS * c;
         if (x < 2 * QM * C::CPR) {
           const int y = x % (QM * C::CPR), row = y / C::CPR, col = y % C::CPR;
-          *(__attribute__((address_space(3))) i32x4*)((x < QM * C::CPR ? qt : dot) + C::TL::chunk(row, col)) = r[c];
+          *(__attribute__((address_space(3))) i32x4*)((c * C::THREADS < QM * C::CPR ? qt : dot) + C::TL::chunk(row, col)) = r[c];
         }
       }
       if (tid < QM) *(__attribute__((address_space(3))) i32x2*)((lds_t*)rc + 8 * tid) = rr;
     }
 
-    // K tiles through registers into two LDS buffers; V fragments in VGPRs.
-    auto kview = [&](int t) {
+    // K and V tiles: whole rows, 16 bytes per lane, through registers into LDS.
+    auto tview = [&](const void* base, int t) {
       const int r0 = key_c0 + t * KT;
-      return seq_view((const char*)a.k + krow + (size_t)r0 * gstride, min(KT, Lk - r0), gstride, C::ROWB);
+      return seq_view((const char*)base + krow + (size_t)r0 * gstride, min(KT, Lk - r0), gstride, C::ROWB);
     };
-    auto kload = [&](int t, i32x4* r) {
-      const View kv = kview(t);
+    auto tload = [&](const void* base, int t, i32x4* r) {
+      const View tv = tview(base, t);
 #pragma unroll
       for (int c = 0; c < C::KCPT; ++c) {
         const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
-        r[c] = ld16(kv, (uint32_t)row * gstride + col * 16);
+        r[c] = ld16(tv, (uint32_t)row * gstride + col * 16);
       }
     };
-    auto kstore = [&](int t, const i32x4* r) {
-      lds_t* kt = lds + C::KOFF + (t % C::NKBUF) * KT * C::ROWB;
+    auto tstore = [&](lds_t* dst, const i32x4* r) {
 #pragma unroll
       for (int c = 0; c < C::KCPT; ++c) {
         const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
-        *(__attribute__((address_space(3))) i32x4*)(kt + C::TL::chunk(row, col)) = r[c];
+        *(__attribute__((address_space(3))) i32x4*)(dst + C::TL::chunk(row, col)) = r[c];
       }
     };
-    auto vload = [&](int t, Frag<T>* vf) {
-      const int kw0 = key_c0 + t * KT + 32 * w;
-      const View vv = seq_view((const char*)a.v + krow + (size_t)kw0 * gstride, max(0, min(32, Lk - kw0)), gstride, C::ROWB);
+    auto tout = [&](void* base, int t, const lds_t* src) {  // staged tile -> global rows
+      const View tv = tview(base, t);
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) vf[kk] = gfrag(vv, (uint32_t)l32 * gstride + (16 * kk + 8 * g) * ES, (T*)0);
+      for (int c = 0; c < C::KCPT; ++c) {
+        const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
+        st16(tv, (uint32_t)row * gstride + col * 16,
+             *(const __attribute__((address_space(3))) i32x4*)(src + C::TL::chunk(row, col)));
+      }
     };
 
-    i32x4 kr[C::KCPT];
-    Frag<T> vf[D / 16];
+    i32x4 kr[C::KCPT], vr[C::KCPT];
     if (nt > 0) {
-      kload(0, kr);
-      vload(0, vf);
-      kstore(0, kr);
+      tload(a.k, 0, kr);
+      tload(a.v, 0, vr);
+      tstore(kt, kr);
+      tstore(vt, vr);
     }
     wait_vmem();
     __syncthreads();
@@ -192,68 +213,58 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
 #pragma unroll
     for (int x = 0; x < (C::NDQ + 3) / 4; ++x) dq[x] = (f32x16){};
 
+    const int kh = w & 1, qh = w >> 1;  // key half and query half of this wave
+    const int krow_t = 32 * kh + l32;   // this lane's key row in the tile
     for (int t = 0; t < nt; ++t) {
-      if (t + 1 < nt) kload(t + 1, kr);
-      const lds_t* kt = lds + C::KOFF + (t % C::NKBUF) * KT * C::ROWB;
-      const int kw0 = key_c0 + t * KT + 32 * w;  // first key of this wave
-      const int kj = kw0 + l32;                  // this lane's key
-      const int krow_t = 32 * w + l32;           // its row in the tile
-      // S, dP of each query half (lane = key, element i = query res_row(i, g))
-      // -> P, dS into LDS, row = key.
+      if (t + 1 < nt) {
+        tload(a.k, t + 1, kr);
+        tload(a.v, t + 1, vr);
+      }
+      const int kj = key_c0 + t * KT + krow_t;  // this lane's key
+      // S, dP of (key half kh, query half qh).
+      f32x16 sc = (f32x16){}, dp = (f32x16){};
+      if (qh < nqs) {
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        if (qs < nqs) {
-          f32x16 sc = (f32x16){}, dp = (f32x16){};
-#pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk) {
-            mma(sc, lfrag<D>(qt, 32 * qs + l32, 16 * kk + 8 * g, (T*)0), lfrag<D>(kt, krow_t, 16 * kk + 8 * g, (T*)0));
-            mma(dp, lfrag<D>(dot, 32 * qs + l32, 16 * kk + 8 * g, (T*)0), vf[kk]);
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int qi = 32 * qs + res_row(i, g);
-            float x = sc[i] * a.scale2 - rc[2 * qi];
-            if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
-            float p = __builtin_amdgcn_exp2f(x);
-            if (kj >= Lk || (a.causal && kj > qi)) p = 0.f;
-            sc[i] = p;
-            dp[i] = p * (dp[i] - rc[2 * qi + 1]);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int q = 32 * qs + 8 * r + 4 * g;
-            put4(pt, krow_t, q, sc[4 * r], sc[4 * r + 1], sc[4 * r + 2], sc[4 * r + 3], (T*)0);
-            put4(st, krow_t, q, dp[4 * r], dp[4 * r + 1], dp[4 * r + 2], dp[4 * r + 3], (T*)0);
-          }
+        for (int kk = 0; kk < D / 16; ++kk) {
+          mma(sc, lfrag<D>(qt, 32 * qh + l32, 16 * kk + 8 * g, (T*)0), lfrag<D>(kt, krow_t, 16 * kk + 8 * g, (T*)0));
+          mma(dp, lfrag<D>(dot, 32 * qh + l32, 16 * kk + 8 * g, (T*)0), lfrag<D>(vt, krow_t, 16 * kk + 8 * g, (T*)0));
         }
       }
-      // V of this tile is no longer needed: its registers take the next
-      // tile's V, whose load then overlaps the rest of this tile.
-      if (t + 1 < nt) vload(t + 1, vf);
-      __syncthreads();
-      // dV^T, dK^T of this wave's 32 keys (rows it wrote itself): lane holds
-      // rows d = 32db + res_row(i,g) of key kj.
-      {
-        const int nk = max(0, min(32, Lk - kw0));
-        const View dvv = seq_view((char*)a.dv + krow + (size_t)kw0 * gstride, nk, gstride, C::ROWB);
-        const View dkv = seq_view((char*)a.dk + krow + (size_t)kw0 * gstride, nk, gstride, C::ROWB);
+      __syncthreads();  // V is consumed: P and dS take its place
+      if (qh < nqs) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          f32x16 av = (f32x16){}, ak = (f32x16){};
+        for (int i = 0; i < 16; ++i) {
+          const int qi = 32 * qh + res_row(i, g);
+          float x = sc[i] * a.scale2 - rc[2 * qi];
+          if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+          float p = __builtin_amdgcn_exp2f(x);
+          if (kj >= Lk || (a.causal && kj > qi)) p = 0.f;
+          sc[i] = p;
+          dp[i] = p * (dp[i] - rc[2 * qi + 1]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int q = 32 * qh + 8 * r + 4 * g;
+          put4<QM>(pt, krow_t, q, sc[4 * r], sc[4 * r + 1], sc[4 * r + 2], sc[4 * r + 3], (T*)0);
+          put4<QM>(st, krow_t, q, dp[4 * r], dp[4 * r + 1], dp[4 * r + 2], dp[4 * r + 3], (T*)0);
+        }
+      }
+      __syncthreads();
+      // dV^T, dK^T of key half kh, column blocks qh, qh + 2, ...: lane holds
+      // rows d = 32db + res_row(i,g) of key kj.
+      f32x16 av[C::NDB2], ak[C::NDB2];
+#pragma unroll
+      for (int j = 0; j < C::NDB2; ++j) {
+        const int db = qh + 2 * j;
+        av[j] = (f32x16){};
+        ak[j] = (f32x16){};
+        if (db < C::NDB) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             if (c < 2 * nqs) {
-              mma(av, tfrag<D>(dot, 16 * c, 32 * db, lane, (T*)0), pfrag(pt, krow_t, c, g, (T*)0));
-              mma(ak, tfrag<D>(qt, 16 * c, 32 * db, lane, (T*)0), pfrag(st, krow_t, c, g, (T*)0));
+              mma(av[j], tfrag<D>(dot, 16 * c, 32 * db, lane, (T*)0), pfrag(pt, krow_t, c, g, (T*)0));
+              mma(ak[j], tfrag<D>(qt, 16 * c, 32 * db, lane, (T*)0), pfrag(st, krow_t, c, g, (T*)0));
             }
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int d = 32 * db + 8 * r + 4 * g;
-            const uint32_t off = (uint32_t)l32 * gstride + d * ES;
-            store4(dvv, off, av[4 * r], av[4 * r + 1], av[4 * r + 2], av[4 * r + 3], (T*)0);
-            store4(dkv, off, ak[4 * r] * a.scale, ak[4 * r + 1] * a.scale, ak[4 * r + 2] * a.scale,
-                   ak[4 * r + 3] * a.scale, (T*)0);
           }
         }
       }
@@ -269,9 +280,29 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
             mma(dq[xi], tfrag<D>(kt, 16 * kc, 32 * db, lane, (T*)0), tfrag<QM>(st, 16 * kc, 32 * qs, lane, (T*)0));
         }
       }
-      if (C::NKBUF == 1) __syncthreads();  // the only K buffer is refilled next
-      if (t + 1 < nt) kstore(t + 1, kr);
+      __syncthreads();  // K, P and dS are consumed: stage dV over V, dK over K
+#pragma unroll
+      for (int j = 0; j < C::NDB2; ++j) {
+        const int db = qh + 2 * j;
+        if (db < C::NDB) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int d = 32 * db + 8 * r + 4 * g;
+            put4<D>(vt, krow_t, d, av[j][4 * r], av[j][4 * r + 1], av[j][4 * r + 2], av[j][4 * r + 3], (T*)0);
+            put4<D>(kt, krow_t, d, ak[j][4 * r] * a.scale, ak[j][4 * r + 1] * a.scale, ak[j][4 * r + 2] * a.scale,
+                    ak[j][4 * r + 3] * a.scale, (T*)0);
+          }
+        }
+      }
       __syncthreads();
+      tout(a.dv, t, vt);
+      tout(a.dk, t, kt);
+      __syncthreads();  // staging read: the next tile's K and V may land
+      if (t + 1 < nt) {
+        tstore(kt, kr);
+        tstore(vt, vr);
+        __syncthreads();
+      }
     }
 
     // Partial dQ of this chunk (unscaled), [64 rows][D] fp32 at item slot it.

@@ -74,7 +74,7 @@ struct PlanArgs {
 
 // Short-query backward: sequences with at most kSqQMax queries are owned whole
 // by one workgroup per chunk of kSqKC keys.
-constexpr int kSqQMax = 64, kSqKC = 1024, kSqKT = 128;
+constexpr int kSqQMax = 64, kSqKC = 1024, kSqKT = 64;
 
 // Tile shapes (query rows x keys) of each kernel. The forward's waves per
 // workgroup (32 query rows each) depend on the element type and D.
