@@ -33,13 +33,13 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0
-SHORT_Q_MAX = 64            # the backward owns sequences with at most this many queries whole
+SHORT_Q_MAX = 64            # sequences with at most this many queries take the short-query passes
 
 
 def valid_pairs(q_lengths, kv_lengths, causal, which="all"):
     """Valid (query, key) pairs per head. which: "all", "long" (sequences the
-    split backward handles) or "short" (at most SHORT_Q_MAX queries: the
-    short-query backward)."""
+    query-tile forward and the split backward handle) or "short" (at most
+    SHORT_Q_MAX queries: the short-query forward and backward)."""
     total = 0
     for lq, lk in zip(q_lengths.tolist(), kv_lengths.tolist()):
         if which == "long" and lq <= SHORT_Q_MAX or which == "short" and lq > SHORT_Q_MAX:
@@ -86,7 +86,8 @@ def recorded_traffic(kernel_label: str, workload: int):
 # Algorithmic flops per valid pair per head, as multiples of D, for each kernel:
 # forward QK^T + PV; dK/dV pass recomputes QK^T and dO V^T and forms dV, dK;
 # dQ pass recomputes QK^T and dO V^T and forms dQ.
-KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "dkdv": 8, "dq": 6, "sq": 10}
+KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "fsq": 4, "dkdv": 8, "dq": 6, "sq": 10}
+KERNEL_SEQS = {"forward": "long", "fsq": "short", "dkdv": "long", "dq": "long", "sq": "short"}
 
 
 def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None):
@@ -133,7 +134,7 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None)
     per = {k_: (ms / max(n, 1), n) for k_, (ms, n) in kt.items()}
     # the plan kind covers one launch in forward and one in backward per step
     plan_ms = kt["plan"][0] / max(kt["plan"][1], 1)
-    fwd_ms = kt["forward"][0] / steps + plan_ms
+    fwd_ms = (kt["forward"][0] + kt["fsq"][0] + kt["fsq_merge"][0]) / steps + plan_ms
     bwd_ms = (kt["delta"][0] + kt["dkdv"][0] + kt["dq"][0] + kt["sq"][0] + kt["sq_reduce"][0]) / steps + plan_ms
     res = {
         "workload": wl.name, "B": wl.B, "H": wl.H, "D": wl.D, "dtype": wl.dtype, "causal": wl.causal,
@@ -150,12 +151,10 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None)
     res["fwd_pct_peak"] = 100.0 * res["fwd_tflops"] / peak
     res["bwd_pct_peak"] = 100.0 * res["bwd_tflops"] / peak
     # dominant kernel; its bound is the roofline its arithmetic intensity falls under
-    share = {k_: kt[k_][0] for k_ in ("forward", "dkdv", "dq", "sq")}
+    share = {k_: kt[k_][0] for k_ in ("forward", "fsq", "dkdv", "dq", "sq")}
     dom = max(share, key=share.get)
     avg_ms = kt[dom][0] / kt[dom][1]
-    kpairs = {"forward": pairs, "dkdv": valid_pairs(batch.q_lengths, batch.kv_lengths, wl.causal, "long"),
-              "dq": valid_pairs(batch.q_lengths, batch.kv_lengths, wl.causal, "long"),
-              "sq": valid_pairs(batch.q_lengths, batch.kv_lengths, wl.causal, "short")}[dom]
+    kpairs = valid_pairs(batch.q_lengths, batch.kv_lengths, wl.causal, KERNEL_SEQS[dom])
     alg = KERNEL_FLOPS_PER_PAIR_D[dom] * wl.D * wl.H * kpairs
     alg_bytes = algorithmic_bytes(dom, batch)
     label = f"jfa_{'fwd' if dom == 'forward' else dom}_kernel<{wl.dtype},D={wl.D}{',bias' if wl.bias else ''}>"
@@ -174,12 +173,16 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None)
 
 
 def algorithmic_bytes(kernel: str, batch) -> int:
-    """Bytes the kernel must move at least once: its inputs read, its outputs written."""
+    """Bytes the kernel must move at least once over the sequences it handles:
+    its inputs read, its outputs written."""
     wl = batch.wl
     e = 2 if wl.dtype == "bf16" else 4
-    tq, tk = batch.total_q * wl.H * wl.D * e, batch.total_kv * wl.H * wl.D * e
-    rows = batch.total_q * wl.H * 4
-    if kernel == "forward":      # q, k, v in; out, lse out
+    short = batch.q_lengths <= SHORT_Q_MAX
+    sel = short if KERNEL_SEQS[kernel] == "short" else ~short
+    nq, nk = int(batch.q_lengths[sel].sum()), int(batch.kv_lengths[sel].sum())
+    tq, tk = nq * wl.H * wl.D * e, nk * wl.H * wl.D * e
+    rows = nq * wl.H * 4
+    if kernel in ("forward", "fsq"):  # q, k, v in; out, lse out
         return tq + 2 * tk + tq + rows
     if kernel == "dkdv":         # q, k, v, dout, lse, delta in; dk, dv out
         return 2 * tq + 2 * tk + 2 * rows + 2 * tk

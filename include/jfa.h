@@ -72,6 +72,7 @@ typedef enum {
 #define JFA_KERNEL_BWD_DKDV 1  /* backward dK/dV pass: tiles of keys       */
 #define JFA_KERNEL_BWD_DQ 2    /* backward dQ pass: tiles of query rows    */
 #define JFA_KERNEL_BWD_SQ 3    /* backward of short-query sequences (Lq <= 64): chunks of keys */
+#define JFA_KERNEL_FWD_SQ 4    /* forward of short-query sequences (Lq <= 64): chunks of keys  */
 
 /* Element types for jfa_tile_config / jfa_build_plan. */
 #define JFA_DTYPE_BF16 0
@@ -89,7 +90,11 @@ size_t jfa_bwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, 
  * 1/sqrt(D). Jagged edges are handled by zero-filled loads and a subtraction
  * of the extra exponent terms ("Jagged Flash Attention (JFA)", section "Four
  * generations", item 1); work is scheduled longest-first over persistent
- * workgroups (same section, item 3). */
+ * workgroups (same section, item 3). A sequence with at most 64 queries is
+ * split over its keys instead, one workgroup per chunk of 1024 keys; each
+ * chunk's rows, normalised over its keys, and their log-sum-exp are combined
+ * per (b, h) in a fixed order, so the result is deterministic (asymmetric
+ * query/key lengths, section "Definition"). */
 jfa_status jfa_fwd(const void* q, const void* k, const void* v, const int32_t* q_offsets,
                    const int32_t* kv_offsets, int B, int H, int D, int64_t total_q, int64_t total_kv,
                    const float* bias, int causal, void* out, float* lse, void* workspace,
@@ -127,7 +132,9 @@ jfa_status jfa_offsets_from_lengths(const int32_t* lengths, int B, int32_t* offs
 /* Tile shape of a kernel: *tile_m query rows and *tile_n keys. For
  * JFA_KERNEL_FWD and JFA_KERNEL_BWD_DQ an item is one tile of tile_m query
  * rows and its cost counts tile_n-key blocks; for JFA_KERNEL_BWD_DKDV an item
- * is one tile of tile_n keys and its cost counts tile_m-row query blocks. */
+ * is one tile of tile_n keys and its cost counts tile_m-row query blocks; for
+ * JFA_KERNEL_BWD_SQ and JFA_KERNEL_FWD_SQ an item is one chunk of tile_n keys
+ * of a sequence with at most tile_m queries. */
 jfa_status jfa_tile_config(int kernel, int D, int dtype, int* tile_m, int* tile_n);
 
 /* Builds the longest-first work lists the given kernel runs on, into
@@ -140,10 +147,11 @@ jfa_status jfa_tile_config(int kernel, int D, int dtype, int* tile_m, int* tile_
  * 15 - g mod 16 (one queue per XCD; a workgroup drains its own queue, then
  * the others). Inside a queue groups follow their rank; inside a group items
  * follow cost descending, then tile ascending. Queue q holds items
- * [start[q], start[q] + qcount[q]). The backward lists of JFA_KERNEL_BWD_DKDV
- * and JFA_KERNEL_BWD_DQ skip sequences with at most 64 queries; the list of
- * JFA_KERNEL_BWD_SQ has only those, one item per chunk of 1024 keys (at least
- * one per sequence, cost = keys in the chunk), and the last
+ * [start[q], start[q] + qcount[q]). The lists of JFA_KERNEL_FWD,
+ * JFA_KERNEL_BWD_DKDV and JFA_KERNEL_BWD_DQ skip sequences with at most 64
+ * queries; the lists of JFA_KERNEL_BWD_SQ and JFA_KERNEL_FWD_SQ (the same
+ * list) have only those, one item per chunk of 1024 keys (at least one per
+ * sequence, cost = keys in the chunk, causal or not), and the last
  * align(B * H * 4, 256) bytes of the workspace then receive, per (b, h), the
  * list position of its chunk 0 (-1 for other sequences). Exposed so that the
  * lists can be checked against an independent builder. */
@@ -156,7 +164,8 @@ size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv,
 /* Launch timing, for benchmarks and profiling. While enabled, every kernel
  * launch of this library is bracketed by two HIP events recorded on its
  * stream (a few microseconds of host overhead per launch). */
-#define JFA_TIMING_KINDS 8 /* 0 plan, 1 forward, 2 delta, 3 dK/dV, 4 dQ, 5 offsets scan, 6 short-query backward, 7 its dQ sum */
+#define JFA_TIMING_KINDS 10 /* 0 plan, 1 forward, 2 delta, 3 dK/dV, 4 dQ, 5 offsets scan, 6 short-query backward, \
+                              7 its dQ sum, 8 short-query forward, 9 its chunk merge */
 jfa_status jfa_timing_enable(int enable);
 
 /* Waits for every recorded launch, writes the summed kernel milliseconds and

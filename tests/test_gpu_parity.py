@@ -90,10 +90,11 @@ def test_edge_lengths(lengths, causal, bias):
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("f32", 32), ("f32", 64)])
 @pytest.mark.parametrize("causal,bias", [(False, False), (True, False), (False, True), (True, True)])
-def test_short_query_backward(dtype, D, causal, bias):
-    """Sequences with at most 64 queries take the single-owner backward: key
-    counts across several 1024-key chunks and ragged tiles, the 64/65 boundary
-    in one batch with the split backward, and empty query or key sides."""
+def test_short_query_passes(dtype, D, causal, bias):
+    """Sequences with at most 64 queries take the key-split forward and the
+    single-owner backward: key counts across several 1024-key chunks and
+    ragged tiles, the 64/65 boundary in one batch with the query-tile forward
+    and the split backward, and empty query or key sides."""
     ql = [64, 65, 1, 33, 0, 17, 40]
     kl = [2500, 70, 1024, 1025, 300, 0, 131]
     wl = gen.Workload("sq", len(ql), 2, D, dtype, causal, bias, gen.LengthDist("fixed", 1, 1), seed=61)
@@ -143,7 +144,8 @@ def test_outputs_outside_sequences_untouched():
     assert e_o <= BF16_TOL["out"] and e_l <= BF16_TOL["lse"]
 
 
-@pytest.mark.parametrize("kernel", [jfa.KERNEL_FWD, jfa.KERNEL_BWD_DKDV, jfa.KERNEL_BWD_DQ, jfa.KERNEL_BWD_SQ])
+@pytest.mark.parametrize("kernel", [jfa.KERNEL_FWD, jfa.KERNEL_BWD_DKDV, jfa.KERNEL_BWD_DQ, jfa.KERNEL_BWD_SQ,
+                                    jfa.KERNEL_FWD_SQ])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_plan_bit_exact(kernel, causal, cfg):
@@ -155,8 +157,9 @@ def test_plan_bit_exact(kernel, causal, cfg):
     _check_plan(qo, ko, wl.H, wl.D, causal, kernel)
 
 
-_PLAN_KIND = {jfa.KERNEL_FWD: ("q", None), jfa.KERNEL_BWD_DKDV: ("kv", oracle.SHORT_Q_MAX),
-              jfa.KERNEL_BWD_DQ: ("q", oracle.SHORT_Q_MAX), jfa.KERNEL_BWD_SQ: ("sq", None)}
+_PLAN_KIND = {jfa.KERNEL_FWD: ("q", oracle.SHORT_Q_MAX), jfa.KERNEL_BWD_DKDV: ("kv", oracle.SHORT_Q_MAX),
+              jfa.KERNEL_BWD_DQ: ("q", oracle.SHORT_Q_MAX), jfa.KERNEL_BWD_SQ: ("sq", None),
+              jfa.KERNEL_FWD_SQ: ("sq", None)}
 
 
 def _check_plan(qo, ko, H, D, causal, kernel):
@@ -168,7 +171,7 @@ def _check_plan(qo, ko, H, D, causal, kernel):
                          int(qo[-1]), int(ko[-1]))
     hdr, items = got[0], got[1]
     torch.cuda.synchronize()
-    if kernel == jfa.KERNEL_BWD_SQ:
+    if kernel in jfa.SQ_KERNELS:
         np.testing.assert_array_equal(got[2].cpu().numpy(), first)
     h = hdr.cpu().numpy()
     assert h[0] == len(ref) and h[1] == 0 and h[2] == jfa.PLAN_QUEUES
@@ -186,7 +189,7 @@ def test_plan_bit_exact_random(seed):
     kl = rng.integers(0, 5000, size=B) * (rng.random(B) < 0.9)
     qo, ko = gen.offsets_from_lengths(ql), gen.offsets_from_lengths(kl)
     H = int(rng.integers(1, 9))
-    for kernel in (jfa.KERNEL_FWD, jfa.KERNEL_BWD_DKDV, jfa.KERNEL_BWD_DQ, jfa.KERNEL_BWD_SQ):
+    for kernel in (jfa.KERNEL_FWD, jfa.KERNEL_BWD_DKDV, jfa.KERNEL_BWD_DQ, jfa.KERNEL_BWD_SQ, jfa.KERNEL_FWD_SQ):
         for causal in (False, True):
             _check_plan(qo, ko, H, 128, causal, kernel)
 

@@ -38,10 +38,13 @@ def test_host_only_queries(L):
     assert L.jfa_fwd_workspace_bytes(4, 65535, 10, 10, 64, 0) > 0
     assert L.jfa_fwd_workspace_bytes(4, 65536, 10, 10, 64, 0) == 0  # beyond JFA_MAX_HEADS
     assert L.jfa_bwd_workspace_bytes(4, 0, 10, 10, 64, 0) == 0
-    for kernel in (jfa.KERNEL_FWD, jfa.KERNEL_BWD_DKDV, jfa.KERNEL_BWD_DQ, jfa.KERNEL_BWD_SQ):
+    for kernel in (jfa.KERNEL_FWD, jfa.KERNEL_BWD_DKDV, jfa.KERNEL_BWD_DQ, jfa.KERNEL_BWD_SQ, jfa.KERNEL_FWD_SQ):
         tm, tn = jfa.tile_config(kernel, 128)
         assert tm % 32 == 0 and tn % 32 == 0 and tm > 0 and tn > 0
-    assert jfa.tile_config(jfa.KERNEL_BWD_SQ, 64) == (64, 1024)  # short-query rows, keys per chunk
+    for kernel in jfa.SQ_KERNELS:
+        assert jfa.tile_config(kernel, 64) == (64, 1024)  # short-query rows, keys per chunk
+    # the forward workspace holds the short-query partials: [64, D] fp32 rows per chunk of 1024 keys
+    assert L.jfa_fwd_workspace_bytes(128, 8, 4281, 617399, 128, 0) > (617399 // 1024) * 8 * 64 * 128 * 4
     with pytest.raises(jfa.JFAError):
         jfa.tile_config(7, 128)
     assert L.jfa_status_string(2) == b"workspace missing, misaligned or too small"

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libjfa.so")
-SOURCES = ["jfa_plan.hip", "jfa_fwd.hip", "jfa_bwd.hip", "jfa_bwd_sq.hip", "jfa_api.hip"]
+SOURCES = ["jfa_plan.hip", "jfa_fwd.hip", "jfa_fwd_sq.hip", "jfa_bwd.hip", "jfa_bwd_sq.hip", "jfa_api.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

@@ -71,8 +71,9 @@ jfa_status device_info(DeviceInfo** out) {
 
 // Optional per-launch timing: HIP events recorded on the launch stream around
 // each kernel, read back on jfa_timing_collect().
-enum { kKindPlan = 0, kKindFwd = 1, kKindDelta = 2, kKindDkdv = 3, kKindDq = 4, kKindScan = 5, kKindSq = 6, kKindSqReduce = 7 };
-static_assert(kKindSqReduce + 1 == JFA_TIMING_KINDS, "timing kinds published in the header");
+enum { kKindPlan = 0, kKindFwd = 1, kKindDelta = 2, kKindDkdv = 3, kKindDq = 4, kKindScan = 5, kKindSq = 6, kKindSqReduce = 7,
+       kKindFsq = 8, kKindFsqMerge = 9 };
+static_assert(kKindFsqMerge + 1 == JFA_TIMING_KINDS, "timing kinds published in the header");
 struct TimingRec {
   int kind;
   hipEvent_t a, b;
@@ -124,16 +125,23 @@ bool valid_sizes(int B, int H, int64_t tq, int64_t tk, int D) {
 // Upper bound on the work items of one pass: sum_b ceil(L_b / tile) <= ceil(T / tile) + B.
 int64_t max_items(int B, int H, int64_t total, int tile) { return (int64_t)H * (cdiv64(total, tile) + B); }
 
+// Forward workspace: two list headers (query tiles, short-query chunks), the
+// two item lists, the short-query group table [B*H] and per short-query item
+// its [64, D] fp32 rows and [64] log2 row sums.
 struct FwdLayout {
-  size_t hdr = 0, items = 0, total = 0;
-  int64_t cap = 0;
+  size_t hdr = 0, hdr_sq = sizeof(PlanHeader), items = 0, items_sq = 0, gfirst = 0, op = 0, lsep = 0, total = 0;
+  int64_t cap = 0, cap_sq = 0;
 };
-FwdLayout fwd_layout(int B, int H, int64_t tq) {
+FwdLayout fwd_layout(int B, int H, int64_t tq, int64_t tk, int D) {
   FwdLayout L;
   L.cap = max_items(B, H, tq, 128);  // smallest forward tile: an upper bound for every variant
-  L.hdr = 0;
-  L.items = sizeof(PlanHeader);
-  L.total = L.items + align_up((size_t)L.cap * 16);
+  L.cap_sq = max_items(B, H, tk, jfa::kSqKC);
+  L.items = 2 * sizeof(PlanHeader);
+  L.items_sq = L.items + align_up((size_t)L.cap * 16);
+  L.gfirst = L.items_sq + align_up((size_t)L.cap_sq * 16);
+  L.op = L.gfirst + align_up((size_t)B * H * 4);
+  L.lsep = L.op + align_up((size_t)L.cap_sq * jfa::kSqQMax * D * 4);
+  L.total = L.lsep + align_up((size_t)L.cap_sq * jfa::kSqQMax * 4);
   return L;
 }
 
@@ -187,7 +195,7 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   if (f32 && D > 64) return fail(JFA_ERR_UNSUPPORTED, "fp32 tensors support D = 32 or 64");
   if ((tq > 0 && (!out || !lse))) return fail(JFA_ERR_INVALID_ARGUMENT, "out/lse must not be NULL");
   if (!aligned(out, 16) || !aligned(lse, 4)) return fail(JFA_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
-  const FwdLayout L = fwd_layout(B, H, tq);
+  const FwdLayout L = fwd_layout(B, H, tq, tk, D);
   if (ws_bytes < L.total)
     return fail(JFA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
   DeviceInfo* dev = nullptr;
@@ -203,8 +211,10 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.H = H;
   pa.causal = causal ? 1 : 0;
   pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::fwd_tile_rows(f32, D), jfa::kFwdTN,
-                jfa::kPassQ, jfa::kPlanQueues, -1, nullptr};
-  hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 1, st); });
+                jfa::kPassQ, jfa::kPlanQueues, jfa::kSqQMax, nullptr};
+  pa.pass[1] = {(int4*)(w + L.items_sq), (PlanHeader*)(w + L.hdr_sq), (long)L.cap_sq, jfa::kSqQMax, jfa::kSqKC,
+                jfa::kPassSQ, jfa::kPlanQueues, -1, (int*)(w + L.gfirst)};
+  hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 2, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
 
   jfa::FwdArgs a{};
@@ -221,7 +231,18 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a.H = H;
   a.causal = causal ? 1 : 0;
   a.scale2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
-  e = timed(kKindFwd, st, [&] { return jfa::launch_fwd(f32, D, a, bias != nullptr, (long)L.cap, dev->num_cus, st); });
+  a.B = B;
+  a.gfirst = (int*)(w + L.gfirst);
+  a.op = (float*)(w + L.op);
+  a.lsep = (float*)(w + L.lsep);
+  jfa::FwdArgs a_sq = a;
+  a_sq.items = (const int4*)(w + L.items_sq);
+  a_sq.hdr = (PlanHeader*)(w + L.hdr_sq);
+  const bool has_bias = bias != nullptr;
+  e = timed(kKindFwd, st, [&] { return jfa::launch_fwd(f32, D, a, has_bias, (long)L.cap, dev->num_cus, st); });
+  if (e == hipSuccess)
+    e = timed(kKindFsq, st, [&] { return jfa::launch_fsq(f32, D, a_sq, has_bias, (long)L.cap_sq, dev->num_cus, st); });
+  if (e == hipSuccess) e = timed(kKindFsqMerge, st, [&] { return jfa::launch_fsq_merge(f32, D, a_sq, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -309,7 +330,8 @@ bool tile_of(int kernel, int D, int dtype, int* tm, int* tn) {
     case JFA_KERNEL_FWD: *tm = jfa::fwd_tile_rows(dtype == JFA_DTYPE_F32, D); *tn = jfa::kFwdTN; return true;
     case JFA_KERNEL_BWD_DKDV: *tm = jfa::dkv_tile_rows(dtype == JFA_DTYPE_F32, D); *tn = jfa::kDkvTN; return true;
     case JFA_KERNEL_BWD_DQ: *tm = jfa::kDqTM; *tn = jfa::kDqTN; return true;
-    case JFA_KERNEL_BWD_SQ: *tm = jfa::kSqQMax; *tn = jfa::kSqKC; return true;
+    case JFA_KERNEL_BWD_SQ:
+    case JFA_KERNEL_FWD_SQ: *tm = jfa::kSqQMax; *tn = jfa::kSqKC; return true;
     default: return false;
   }
 }
@@ -321,7 +343,7 @@ extern "C" {
 size_t jfa_fwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, int D, int causal) {
   (void)causal;
   if (!valid_sizes(B, H, total_q, total_kv, D)) return 0;
-  return fwd_layout(B, H, total_q).total;
+  return fwd_layout(B, H, total_q, total_kv, D).total;
 }
 
 size_t jfa_bwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, int D, int causal) {
@@ -385,9 +407,9 @@ size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv,
   if (!valid_sizes(B, H, total_q, total_kv, D) || (dtype != JFA_DTYPE_BF16 && dtype != JFA_DTYPE_F32) ||
       !tile_of(kernel, D, dtype, &tm, &tn))
     return 0;
-  const int64_t cap = kernel == JFA_KERNEL_BWD_DKDV || kernel == JFA_KERNEL_BWD_SQ ? max_items(B, H, total_kv, tn)
-                                                                                  : max_items(B, H, total_q, tm);
-  return sizeof(PlanHeader) + align_up((size_t)cap * 16) + (kernel == JFA_KERNEL_BWD_SQ ? align_up((size_t)B * H * 4) : 0);
+  const bool sq = kernel == JFA_KERNEL_BWD_SQ || kernel == JFA_KERNEL_FWD_SQ;
+  const int64_t cap = kernel == JFA_KERNEL_BWD_DKDV || sq ? max_items(B, H, total_kv, tn) : max_items(B, H, total_q, tm);
+  return sizeof(PlanHeader) + align_up((size_t)cap * 16) + (sq ? align_up((size_t)B * H * 4) : 0);
 }
 
 jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D, int dtype,
@@ -412,10 +434,11 @@ jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, i
   pa.causal = causal ? 1 : 0;
   // Layout: header, items, and for the short-query pass the [B*H] group table
   // after the largest list the sizes allow.
-  const size_t tail = kernel == JFA_KERNEL_BWD_SQ ? align_up((size_t)B * H * 4) : 0;
+  const bool sq = kernel == JFA_KERNEL_BWD_SQ || kernel == JFA_KERNEL_FWD_SQ;
+  const size_t tail = sq ? align_up((size_t)B * H * 4) : 0;
   if (workspace_bytes < sizeof(PlanHeader) + tail) return fail(JFA_ERR_WORKSPACE, "workspace too small");
-  const int kind = kernel == JFA_KERNEL_BWD_DKDV ? jfa::kPassKV : (kernel == JFA_KERNEL_BWD_SQ ? jfa::kPassSQ : jfa::kPassQ);
-  const int short_q = (kernel == JFA_KERNEL_BWD_DKDV || kernel == JFA_KERNEL_BWD_DQ) ? jfa::kSqQMax : -1;
+  const int kind = kernel == JFA_KERNEL_BWD_DKDV ? jfa::kPassKV : (sq ? jfa::kPassSQ : jfa::kPassQ);
+  const int short_q = sq ? -1 : jfa::kSqQMax;
   pa.pass[0] = {(int4*)(w + sizeof(PlanHeader)), (PlanHeader*)w,
                 (long)((workspace_bytes - sizeof(PlanHeader) - tail) / 16), tm, tn, kind, jfa::kPlanQueues, short_q,
                 tail ? (int*)(w + workspace_bytes - tail) : nullptr};

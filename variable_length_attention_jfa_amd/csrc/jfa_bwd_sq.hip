@@ -305,8 +305,10 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
       }
     }
 
-    // Partial dQ of this chunk (unscaled), [64 rows][D] fp32 at item slot it.
-    float* part = a.dqp + (size_t)it * QM * D;
+    // dQ of this chunk, staged in LDS as [64 rows][D] fp32 and written as
+    // whole rows: a sequence with a single chunk stores its dQ (times the
+    // scale) itself; otherwise the unscaled partial goes to item slot it and
+    // the reduce sums the chunks. LDS is free: the last tile ended on a barrier.
 #pragma unroll
     for (int xi = 0; xi < (C::NDQ + 3) / 4; ++xi) {
       const int x = w + 4 * xi;
@@ -315,29 +317,41 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int d = 32 * db + 8 * r + 4 * g;
-          *(f32x4*)(part + (size_t)q * D + d) = (f32x4){dq[xi][4 * r], dq[xi][4 * r + 1], dq[xi][4 * r + 2], dq[xi][4 * r + 3]};
+          *(__attribute__((address_space(3))) f32x4*)(lds + Tile<float, D>::byte(q, d * 4)) =
+              (f32x4){dq[xi][4 * r], dq[xi][4 * r + 1], dq[xi][4 * r + 2], dq[xi][4 * r + 3]};
         }
       }
+    }
+    __syncthreads();
+    if (Lk <= KC) {
+      const View dqv = seq_view((char*)a.dq + qrow, Lq, gstride, C::ROWB);
+      rows_out<T, D, QM, C::THREADS>(lds, dqv, gstride, a.scale, tid);
+    } else {
+      const View pv = seq_view(a.dqp + (size_t)it * QM * D, Lq, D * 4, D * 4);
+      rows_out<float, D, QM, C::THREADS>(lds, pv, D * 4, 1.0f, tid);
     }
   }
 }
 
-// dQ of each short-query sequence: the sum, in list order, of its chunks'
-// partials, times the softmax scale. One workgroup per (b, h).
+// dQ of each short-query sequence with more than one chunk: the sum, in
+// list order, of its chunks' partials, times the softmax scale. One
+// workgroup per (b, h); four columns per thread, chunks unrolled so that
+// their loads overlap.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void jfa_sq_reduce_kernel(BwdArgs a) {
   constexpr int QM = kSqQMax;
   const int gi = blockIdx.x, b = gi / a.H, h = gi % a.H;
   const int first = a.gfirst[gi];
-  if (first < 0) return;
-  const int q0 = a.q_off[b], Lq = min(a.q_off[b + 1] - q0, QM);
   const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-  const int n = max(1, cdiv(Lk, kSqKC));
-  const size_t qstride = (size_t)a.H * D;  // elements between consecutive tokens
+  if (first < 0 || Lk <= kSqKC) return;  // one chunk: the chunk stored dQ itself
+  const int q0 = a.q_off[b], Lq = min(a.q_off[b + 1] - q0, QM);
+  const int n = cdiv(Lk, kSqKC);
+  const float* part = a.dqp + (size_t)first * QM * D;
   for (int e = threadIdx.x * 4; e < Lq * D; e += 256 * 4) {
     const int q = e / D, d = e % D;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int t = 0; t < n; ++t) s += *(const f32x4*)(a.dqp + (size_t)(first + t) * QM * D + e);
+#pragma unroll 4
+    for (int t = 0; t < n; ++t) s += *(const f32x4*)(part + (size_t)t * QM * D + e);
     T* dst = (T*)a.dq + ((size_t)(q0 + q) * a.H + h) * D + d;
 #pragma unroll
     for (int k = 0; k < 4; ++k) dst[k] = (T)(s[k] * a.scale);

@@ -33,6 +33,7 @@ constexpr int kBiasLen = 2 * kBiasRadius + 1;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInit = -1.0e30f;  // running-max start value (finite: keeps exp2(m_old - m_new) at 0)
+constexpr float kRescaleSlack = 8.0f;  // log2 units: the running max lags the true max by at most this, so P <= 256
 
 // ---------------------------------------------------------------------------
 // Buffer views with hardware range checks.
@@ -252,6 +253,23 @@ __device__ __forceinline__ void store4(const View& v, uint32_t off, float a, flo
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// ROWS rows of D fp32 values staged in LDS (Tile<float, D> layout) out to
+// global memory as whole rows, each value times `mul` and rounded to T; row
+// r goes to byte offset r * stride of `dst`, whose range drops rows past the
+// sequence end.
+template <typename T, int D, int ROWS, int THREADS>
+__device__ __forceinline__ void rows_out(const lds_t* src, const View& dst, uint32_t stride, float mul, int tid) {
+  using OL = Tile<float, D>;
+  static_assert((ROWS * OL::CPR) % THREADS == 0, "row pieces divide the workgroup");
+#pragma unroll
+  for (int c = 0; c < ROWS * OL::CPR / THREADS; ++c) {
+    const int x = tid + THREADS * c, row = x / OL::CPR, col = x % OL::CPR;
+    const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(src + OL::chunk(row, col));
+    store4(dst, (uint32_t)row * stride + col * 4 * (int)sizeof(T), v[0] * mul, v[1] * mul, v[2] * mul, v[3] * mul,
+           (T*)0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Direct global -> LDS tile loads. One wave instruction moves 64 x 16 bytes
 // into 1 KB of LDS, lane l landing at byte 16*l (gfx950 buffer_load_dwordx4
@@ -394,8 +412,10 @@ struct TicketState {
 // queue (the one its XCD drains) and, once that is empty, from the others in
 // turn. Tickets are taken one at a time, when the previous item is done: a
 // workgroup never holds a claim on an item it is not working on, so the
-// longest-first order decides which items start first. Returns -1 when every
-// queue is empty.
+// longest-first order decides which items start first. Queues the plan left
+// empty are passed over without touching their ticket, so a pass with no
+// items (a batch without short-query sequences, say) ends at once. Returns
+// -1 when every queue is empty.
 __device__ __forceinline__ int next_item(PlanHeader* hdr, QueueCursor* qc, TicketState& ts) {
   __syncthreads();  // queue bounds loaded; every wave is done with the previous item's slot
   if (threadIdx.x == 0) {
@@ -405,10 +425,12 @@ __device__ __forceinline__ int next_item(PlanHeader* hdr, QueueCursor* qc, Ticke
     }
     int it = -1;
     while (ts.left > 0) {
-      const int t = __hip_atomic_fetch_add(&hdr->ticket[ts.q].value, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (t < qc->count[ts.q]) {
-        it = qc->start[ts.q] + t;
-        break;
+      if (qc->count[ts.q] > 0) {
+        const int t = __hip_atomic_fetch_add(&hdr->ticket[ts.q].value, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t < qc->count[ts.q]) {
+          it = qc->start[ts.q] + t;
+          break;
+        }
       }
       ts.q = ts.q + 1 == qc->nq ? 0 : ts.q + 1;
       ts.left -= 1;

@@ -27,8 +27,6 @@
 
 namespace jfa {
 
-constexpr float kRescaleSlack = 8.0f;  // log2 units: P never exceeds 256
-
 template <typename T, int D>
 struct FwdTiles {
   static constexpr int BM = 128;  // query rows per item (4 waves x 32)

@@ -16,11 +16,15 @@ struct FwdArgs {
   const float* bias;  // [H][257] or null
   void* out;
   float* lse;
-  const int4* items;
+  const int4* items;   // work list of this pass
   PlanHeader* hdr;
   int H;
   int causal;
-  float scale2;  // softmax scale * log2(e)
+  float scale2;        // softmax scale * log2(e)
+  int B;
+  int* gfirst;         // short-query pass: [B*H] list position of chunk 0 of each (b, h), -1 if none
+  float* op;           // short-query pass: per item, [64, D] fp32 rows normalised over the chunk's keys
+  float* lsep;         // short-query pass: per item, [64] log2 of each row's sum over the chunk's keys
 };
 
 struct BwdArgs {
@@ -72,8 +76,10 @@ struct PlanArgs {
   PlanPass pass[3];
 };
 
-// Short-query backward: sequences with at most kSqQMax queries are owned whole
-// by one workgroup per chunk of kSqKC keys.
+// Short-query passes: sequences with at most kSqQMax queries are cut into
+// chunks of kSqKC keys, one workgroup per (b, h, chunk), in the forward
+// (split over the keys, chunks merged per (b, h)) and in the backward (one
+// pass over K/V, dQ partials summed per (b, h)).
 constexpr int kSqQMax = 64, kSqKC = 1024, kSqKT = 64;
 
 // Tile shapes (query rows x keys) of each kernel. The forward's waves per
@@ -91,6 +97,8 @@ constexpr int kDqTM = 128, kDqTN = 64;
 
 // Persistent launches: grid = min(max_items, CUs x resident workgroups per CU).
 hipError_t launch_fwd(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
+hipError_t launch_fsq(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
+hipError_t launch_fsq_merge(bool f32, int D, const FwdArgs& a, hipStream_t st);
 hipError_t launch_delta(bool f32, int D, const BwdArgs& a, hipStream_t st);
 hipError_t launch_dkdv(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
 hipError_t launch_dq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);

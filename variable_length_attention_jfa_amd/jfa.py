@@ -24,7 +24,8 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libjfa.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "jfa.h")
 
-KERNEL_FWD, KERNEL_BWD_DKDV, KERNEL_BWD_DQ, KERNEL_BWD_SQ = 0, 1, 2, 3
+KERNEL_FWD, KERNEL_BWD_DKDV, KERNEL_BWD_DQ, KERNEL_BWD_SQ, KERNEL_FWD_SQ = 0, 1, 2, 3, 4
+SQ_KERNELS = (KERNEL_BWD_SQ, KERNEL_FWD_SQ)  # short-query chunk lists (one list, two passes)
 DTYPE_BF16, DTYPE_F32 = 0, 1
 BIAS_RADIUS = 128
 WORKSPACE_ALIGN = 256
@@ -191,7 +192,8 @@ def tile_config(kernel: int, D: int, dtype: int = DTYPE_BF16) -> Tuple[int, int]
 def build_plan(q_offsets: torch.Tensor, kv_offsets: torch.Tensor, H: int, D: int, causal: bool, kernel: int,
                total_q: int, total_kv: int, dtype: int = DTYPE_BF16) -> Tuple[torch.Tensor, torch.Tensor]:
     """Runs the on-device work-list builder; returns (header int32[512], items int32[n, 4]) on the device,
-    and for KERNEL_BWD_SQ also the per-(b, h) position of chunk 0 (int32[B*H], -1 if none)."""
+    and for the short-query lists (KERNEL_BWD_SQ, KERNEL_FWD_SQ) also the per-(b, h) position of chunk 0
+    (int32[B*H], -1 if none)."""
     _check_tensor("q_offsets", q_offsets, torch.int32, 1)
     _check_tensor("kv_offsets", kv_offsets, torch.int32, 1)
     B = q_offsets.numel() - 1
@@ -204,15 +206,15 @@ def build_plan(q_offsets: torch.Tensor, kv_offsets: torch.Tensor, H: int, D: int
                           nbytes, _stream())
     _check("jfa_build_plan", st)
     off = wp - ws.data_ptr()
-    tail = (B * H * 4 + 255) // 256 * 256 if kernel == KERNEL_BWD_SQ else 0
+    tail = (B * H * 4 + 255) // 256 * 256 if kernel in SQ_KERNELS else 0
     header = ws[off:off + PLAN_HEADER_BYTES].view(torch.int32)
     items = ws[off + PLAN_HEADER_BYTES:off + nbytes - tail].view(torch.int32).view(-1, 4)
-    if kernel != KERNEL_BWD_SQ:
+    if kernel not in SQ_KERNELS:
         return header, items
     return header, items, ws[off + nbytes - tail:off + nbytes - tail + B * H * 4].view(torch.int32)
 
 
-TIMING_KINDS = ("plan", "forward", "delta", "dkdv", "dq", "scan", "sq", "sq_reduce")
+TIMING_KINDS = ("plan", "forward", "delta", "dkdv", "dq", "scan", "sq", "sq_reduce", "fsq", "fsq_merge")
 
 
 def timing_enable(enable: bool = True) -> None:
