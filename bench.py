@@ -33,16 +33,19 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0
-SHORT_Q_MAX = 64            # sequences with at most this many queries take the short-query passes
+SHORT_Q_MAX = 64            # sequences with at most this many queries ...
+SHORT_KV_MIN = 1024         # ... and more than this many keys take the short-query passes
 
 
 def valid_pairs(q_lengths, kv_lengths, causal, which="all"):
     """Valid (query, key) pairs per head. which: "all", "long" (sequences the
     query-tile forward and the split backward handle) or "short" (at most
-    SHORT_Q_MAX queries: the short-query forward and backward)."""
+    SHORT_Q_MAX queries and more than SHORT_KV_MIN keys: the short-query
+    forward and backward)."""
     total = 0
     for lq, lk in zip(q_lengths.tolist(), kv_lengths.tolist()):
-        if which == "long" and lq <= SHORT_Q_MAX or which == "short" and lq > SHORT_Q_MAX:
+        short = lq <= SHORT_Q_MAX and lk > SHORT_KV_MIN
+        if which == "long" and short or which == "short" and not short:
             continue
         if causal:
             m = min(lq, lk)
@@ -116,14 +119,19 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    jfa.timing_collect()  # drop anything recorded before
-    jfa.timing_enable(True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # Per-kernel durations: the same steps again, with the library's HIP
+    # events recorded on the launch stream around every kernel (kept out of
+    # the wall-clock pass above, whose launches they would space out).
+    jfa.timing_collect()  # drop anything recorded before
+    jfa.timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
     jfa.timing_enable(False)
     kt = jfa.timing_collect()
 
@@ -134,8 +142,8 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None)
     per = {k_: (ms / max(n, 1), n) for k_, (ms, n) in kt.items()}
     # the plan kind covers one launch in forward and one in backward per step
     plan_ms = kt["plan"][0] / max(kt["plan"][1], 1)
-    fwd_ms = (kt["forward"][0] + kt["fsq"][0] + kt["fsq_merge"][0]) / steps + plan_ms
-    bwd_ms = (kt["delta"][0] + kt["dkdv"][0] + kt["dq"][0] + kt["sq"][0] + kt["sq_reduce"][0]) / steps + plan_ms
+    fwd_ms = (kt["forward"][0] + kt["fsq"][0]) / steps + plan_ms
+    bwd_ms = (kt["delta"][0] + kt["dkdv"][0] + kt["dq"][0] + kt["sq"][0]) / steps + plan_ms
     res = {
         "workload": wl.name, "B": wl.B, "H": wl.H, "D": wl.D, "dtype": wl.dtype, "causal": wl.causal,
         "bias": wl.bias, "seed": wl.seed if seed is None else seed, "total_q": batch.total_q,
@@ -177,7 +185,7 @@ def algorithmic_bytes(kernel: str, batch) -> int:
     its inputs read, its outputs written."""
     wl = batch.wl
     e = 2 if wl.dtype == "bf16" else 4
-    short = batch.q_lengths <= SHORT_Q_MAX
+    short = (batch.q_lengths <= SHORT_Q_MAX) & (batch.kv_lengths > SHORT_KV_MIN)
     sel = short if KERNEL_SEQS[kernel] == "short" else ~short
     nq, nk = int(batch.q_lengths[sel].sum()), int(batch.kv_lengths[sel].sum())
     tq, tk = nq * wl.H * wl.D * e, nk * wl.H * wl.D * e

@@ -71,8 +71,8 @@ typedef enum {
 #define JFA_KERNEL_FWD 0       /* forward: tiles of query rows            */
 #define JFA_KERNEL_BWD_DKDV 1  /* backward dK/dV pass: tiles of keys       */
 #define JFA_KERNEL_BWD_DQ 2    /* backward dQ pass: tiles of query rows    */
-#define JFA_KERNEL_BWD_SQ 3    /* backward of short-query sequences (Lq <= 64): chunks of keys */
-#define JFA_KERNEL_FWD_SQ 4    /* forward of short-query sequences (Lq <= 64): chunks of keys  */
+#define JFA_KERNEL_BWD_SQ 3    /* backward of short-query sequences (Lq <= 64 < 1024 < Lk): chunks of keys */
+#define JFA_KERNEL_FWD_SQ 4    /* forward of short-query sequences (Lq <= 64 < 1024 < Lk): chunks of keys  */
 
 /* Element types for jfa_tile_config / jfa_build_plan. */
 #define JFA_DTYPE_BF16 0
@@ -90,11 +90,11 @@ size_t jfa_bwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, 
  * 1/sqrt(D). Jagged edges are handled by zero-filled loads and a subtraction
  * of the extra exponent terms ("Jagged Flash Attention (JFA)", section "Four
  * generations", item 1); work is scheduled longest-first over persistent
- * workgroups (same section, item 3). A sequence with at most 64 queries is
- * split over its keys instead, one workgroup per chunk of 1024 keys; each
- * chunk's rows, normalised over its keys, and their log-sum-exp are combined
- * per (b, h) in a fixed order, so the result is deterministic (asymmetric
- * query/key lengths, section "Definition"). */
+ * workgroups (same section, item 3). A sequence with at most 64 queries and
+ * more than 1024 keys is split over its keys instead, one workgroup per
+ * chunk of 1024 keys; each chunk's rows, normalised over its keys, and their
+ * log-sum-exp are combined per (b, h) in a fixed order, so the result is
+ * deterministic (asymmetric query/key lengths, section "Definition"). */
 jfa_status jfa_fwd(const void* q, const void* k, const void* v, const int32_t* q_offsets,
                    const int32_t* kv_offsets, int B, int H, int D, int64_t total_q, int64_t total_kv,
                    const float* bias, int causal, void* out, float* lse, void* workspace,
@@ -104,10 +104,11 @@ jfa_status jfa_fwd(const void* q, const void* k, const void* v, const int32_t* q
  * gradient dout; writes dq, dk, dv (same layout and type as q, k, v). dK/dV
  * and dQ are computed in two passes with no atomics ("Jagged Flash Attention
  * (JFA)", section "Four generations", item 2). A sequence with at most 64
- * queries is instead owned whole by one workgroup per chunk of 1024 keys,
- * which forms S and dP once and reads K, V once; its dQ is the sum, in a
- * fixed order, of the chunks' partial results (asymmetric query/key lengths,
- * section "Definition"). No gradient for the bias. */
+ * queries and more than 1024 keys is instead owned whole by one workgroup
+ * per chunk of 1024 keys, which forms S and dP once and reads K, V once; its
+ * dQ is the sum, in a fixed order, of the chunks' partial results
+ * (asymmetric query/key lengths, section "Definition"). No gradient for the
+ * bias. */
 jfa_status jfa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
                    const void* dout, const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H,
                    int D, int64_t total_q, int64_t total_kv, const float* bias, int causal, void* dq,
@@ -149,9 +150,9 @@ jfa_status jfa_tile_config(int kernel, int D, int dtype, int* tile_m, int* tile_
  * follow cost descending, then tile ascending. Queue q holds items
  * [start[q], start[q] + qcount[q]). The lists of JFA_KERNEL_FWD,
  * JFA_KERNEL_BWD_DKDV and JFA_KERNEL_BWD_DQ skip sequences with at most 64
- * queries; the lists of JFA_KERNEL_BWD_SQ and JFA_KERNEL_FWD_SQ (the same
- * list) have only those, one item per chunk of 1024 keys (at least one per
- * sequence, cost = keys in the chunk, causal or not), and the last
+ * queries and more than 1024 keys; the lists of JFA_KERNEL_BWD_SQ and
+ * JFA_KERNEL_FWD_SQ (the same list) have only those, one item per chunk of
+ * 1024 keys (cost = keys in the chunk, causal or not), and the last
  * align(B * H * 4, 256) bytes of the workspace then receive, per (b, h), the
  * list position of its chunk 0 (-1 for other sequences). Exposed so that the
  * lists can be checked against an independent builder. */
@@ -164,8 +165,9 @@ size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv,
 /* Launch timing, for benchmarks and profiling. While enabled, every kernel
  * launch of this library is bracketed by two HIP events recorded on its
  * stream (a few microseconds of host overhead per launch). */
-#define JFA_TIMING_KINDS 10 /* 0 plan, 1 forward, 2 delta, 3 dK/dV, 4 dQ, 5 offsets scan, 6 short-query backward, \
-                              7 its dQ sum, 8 short-query forward, 9 its chunk merge */
+#define JFA_TIMING_KINDS 8 /* 0 plan, 1 forward (with the short-query chunk merge), 2 delta, 3 dK/dV, \
+                             4 dQ (with the short-query dQ sum), 5 offsets scan, 6 short-query backward chunks, \
+                             7 short-query forward chunks */
 jfa_status jfa_timing_enable(int enable);
 
 /* Waits for every recorded launch, writes the summed kernel milliseconds and

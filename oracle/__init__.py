@@ -11,4 +11,4 @@ Modules:
 """
 from .attention import forward, backward, valid_pairs  # noqa: F401
 from .plan import (build_plan, build_plan_queues, q_tile_cost, kv_tile_cost, sq_chunk_cost, exclusive_scan,  # noqa: F401
-                   snake, N_QUEUES, SHORT_Q_MAX)
+                   snake, short_query, N_QUEUES, SHORT_Q_MAX, SHORT_KV_MIN)

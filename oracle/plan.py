@@ -40,7 +40,13 @@ from typing import List, Tuple
 import numpy as np
 
 N_QUEUES = 8
-SHORT_Q_MAX = 64  # backward: sequences with at most this many queries take the sq pass
+SHORT_Q_MAX = 64     # short-query sequences: at most this many queries ...
+SHORT_KV_MIN = 1024  # ... and more than this many keys (one chunk of the sq pass)
+
+
+def short_query(Lq: int, Lk: int) -> bool:
+    """Sequences the short-query passes own, split into chunks of keys."""
+    return Lq <= SHORT_Q_MAX and Lk > SHORT_KV_MIN
 
 
 def _cdiv(a: int, b: int) -> int:
@@ -87,7 +93,8 @@ def build_plan_queues(q_offsets, kv_offsets, H: int, TM: int, TN: int, causal: b
     stored one after the other, starts int32 [n_queues], counts int32 [n_queues]).
 
     kind: "q", "kv" or "sq" (default: "kv" if kv_pass else "q"). short_q: for
-    the backward's q and kv passes, sequences with Lq <= short_q get no items.
+    the q and kv passes, sequences with Lq <= short_q and more than
+    SHORT_KV_MIN keys get no items (the sq pass has them).
     with_groups: also return, for the sq pass, int32 [B*H] with the list
     position of chunk 0 of each (b, h) (-1 for sequences the pass skips)."""
     if kind is None:
@@ -100,14 +107,14 @@ def build_plan_queues(q_offsets, kv_offsets, H: int, TM: int, TN: int, causal: b
     for b in range(B):
         Lq, Lk = qo[b + 1] - qo[b], ko[b + 1] - ko[b]
         if kind == "sq":
-            n = max(1, _cdiv(Lk, TN)) if Lq <= SHORT_Q_MAX else 0
+            n = _cdiv(Lk, TN) if short_query(Lq, Lk) else 0
             tiles = [(t, sq_chunk_cost(Lk, t, TN)) for t in range(n)]
         else:
             if kind == "kv":
                 n, costf = _cdiv(Lk, TN), kv_tile_cost
             else:
                 n, costf = _cdiv(Lq, TM), q_tile_cost
-            if short_q is not None and Lq <= short_q:
+            if short_q is not None and Lq <= short_q and Lk > SHORT_KV_MIN:
                 n = 0
             tiles = [(t, costf(Lq, Lk, t, TM, TN, causal)) for t in range(n)]
         tiles.sort(key=lambda tc: (-tc[1], tc[0]))

@@ -91,12 +91,13 @@ def test_edge_lengths(lengths, causal, bias):
 @pytest.mark.parametrize("dtype,D", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("f32", 32), ("f32", 64)])
 @pytest.mark.parametrize("causal,bias", [(False, False), (True, False), (False, True), (True, True)])
 def test_short_query_passes(dtype, D, causal, bias):
-    """Sequences with at most 64 queries take the key-split forward and the
-    single-owner backward: key counts across several 1024-key chunks and
-    ragged tiles, the 64/65 boundary in one batch with the query-tile forward
-    and the split backward, and empty query or key sides."""
-    ql = [64, 65, 1, 33, 0, 17, 40]
-    kl = [2500, 70, 1024, 1025, 300, 0, 131]
+    """Sequences with at most 64 queries and more than 1024 keys take the
+    key-split forward and the single-owner backward: key counts across
+    several 1024-key chunks and ragged tiles, the 64/65 and 1024/1025
+    boundaries in one batch with the query-tile forward and the split
+    backward, and empty query or key sides."""
+    ql = [64, 65, 1, 33, 0, 17, 40, 0, 5, 64]
+    kl = [2500, 70, 1024, 1025, 300, 0, 131, 3000, 4097, 1024]
     wl = gen.Workload("sq", len(ql), 2, D, dtype, causal, bias, gen.LengthDist("fixed", 1, 1), seed=61)
     _check(gen.make_batch(wl, q_lengths=ql, kv_lengths=kl), label=f"short-query {dtype} D={D} causal={causal} bias={bias}")
 

@@ -107,26 +107,28 @@ def test_exclusive_scan():
 
 @pytest.mark.parametrize("n_queues", [1, 8])
 def test_short_query_pass(n_queues):
-    """The sq pass: exactly the sequences with Lq <= 64, chunks covering their
-    keys once (one chunk when there are none), group table pointing at chunk 0,
-    and the q and kv passes of the backward skipping exactly those sequences."""
+    """The sq pass: exactly the sequences with Lq <= 64 and more than 1024
+    keys, chunks covering their keys once, group table pointing at chunk 0,
+    and the q and kv passes skipping exactly those sequences."""
     rng = np.random.default_rng(7 + n_queues)
     B, H, KC = 40, 3, 1024
     lq = rng.integers(0, 130, size=B)
-    lq[:4] = [0, 64, 65, 1]
+    lq[:8] = [0, 64, 65, 1, 64, 64, 0, 3]
     lk = rng.integers(0, 5000, size=B)
-    lk[4:6] = [0, 1024]
+    lk[:8] = [2000, 1025, 3000, 4096, 1024, 0, 1024, 1025]
     qo, ko = oracle.exclusive_scan(lq), oracle.exclusive_scan(lk)
     items, starts, counts, first = oracle.build_plan_queues(qo, ko, H, 64, KC, False, kind="sq", n_queues=n_queues,
                                                             with_groups=True)
-    short = [b for b in range(B) if lq[b] <= oracle.SHORT_Q_MAX]
+    short = [b for b in range(B) if lq[b] <= 64 and lk[b] > 1024]
+    assert {0, 1, 3, 7}.issubset(short) and not {2, 4, 5, 6} & set(short)
     for b in range(B):
         for h in range(H):
             its = [(int(t), int(c)) for bb, hh, t, c in items if bb == b and hh == h]
             if b not in short:
                 assert its == [] and first[b * H + h] == -1
                 continue
-            n = max(1, -(-int(lk[b]) // KC))
+            n = -(-int(lk[b]) // KC)
+            assert n >= 2
             assert sorted(t for t, _ in its) == list(range(n))
             assert sum(c for _, c in its) == lk[b]          # the chunks cover every key once
             assert all(c == min(KC, int(lk[b]) - t * KC) for t, c in its)

@@ -71,9 +71,8 @@ jfa_status device_info(DeviceInfo** out) {
 
 // Optional per-launch timing: HIP events recorded on the launch stream around
 // each kernel, read back on jfa_timing_collect().
-enum { kKindPlan = 0, kKindFwd = 1, kKindDelta = 2, kKindDkdv = 3, kKindDq = 4, kKindScan = 5, kKindSq = 6, kKindSqReduce = 7,
-       kKindFsq = 8, kKindFsqMerge = 9 };
-static_assert(kKindFsqMerge + 1 == JFA_TIMING_KINDS, "timing kinds published in the header");
+enum { kKindPlan = 0, kKindFwd = 1, kKindDelta = 2, kKindDkdv = 3, kKindDq = 4, kKindScan = 5, kKindSq = 6, kKindFsq = 7 };
+static_assert(kKindFsq + 1 == JFA_TIMING_KINDS, "timing kinds published in the header");
 struct TimingRec {
   int kind;
   hipEvent_t a, b;
@@ -239,10 +238,10 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a_sq.items = (const int4*)(w + L.items_sq);
   a_sq.hdr = (PlanHeader*)(w + L.hdr_sq);
   const bool has_bias = bias != nullptr;
-  e = timed(kKindFwd, st, [&] { return jfa::launch_fwd(f32, D, a, has_bias, (long)L.cap, dev->num_cus, st); });
+  // Short-query chunks first: the query-tile launch then combines them.
+  e = timed(kKindFsq, st, [&] { return jfa::launch_fsq(f32, D, a_sq, has_bias, (long)L.cap_sq, dev->num_cus, st); });
   if (e == hipSuccess)
-    e = timed(kKindFsq, st, [&] { return jfa::launch_fsq(f32, D, a_sq, has_bias, (long)L.cap_sq, dev->num_cus, st); });
-  if (e == hipSuccess) e = timed(kKindFsqMerge, st, [&] { return jfa::launch_fsq_merge(f32, D, a_sq, st); });
+    e = timed(kKindFwd, st, [&] { return jfa::launch_fwd(f32, D, a, has_bias, (long)L.cap, dev->num_cus, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -313,14 +312,15 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a_sq.items = (const int4*)(w + L.items_sq);
   a_sq.hdr = (PlanHeader*)(w + L.hdr_sq);
   const bool has_bias = bias != nullptr;
+  // Delta, then the short-query chunks (their partial dQ is summed at the
+  // start of the dQ launch), then the split passes.
   e = timed(kKindDelta, st, [&] { return jfa::launch_delta(f32, D, a_kv, st); });
+  if (e == hipSuccess)
+    e = timed(kKindSq, st, [&] { return jfa::launch_sq(f32, D, a_sq, has_bias, (long)L.cap_sq, dev->num_cus, st); });
   if (e == hipSuccess)
     e = timed(kKindDkdv, st, [&] { return jfa::launch_dkdv(f32, D, a_kv, has_bias, (long)L.cap_kv, dev->num_cus, st); });
   if (e == hipSuccess)
     e = timed(kKindDq, st, [&] { return jfa::launch_dq(f32, D, a_q, has_bias, (long)L.cap_q, dev->num_cus, st); });
-  if (e == hipSuccess)
-    e = timed(kKindSq, st, [&] { return jfa::launch_sq(f32, D, a_sq, has_bias, (long)L.cap_sq, dev->num_cus, st); });
-  if (e == hipSuccess) e = timed(kKindSqReduce, st, [&] { return jfa::launch_sq_reduce(f32, D, a_sq, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -29,6 +29,7 @@
 // blocks that straddle it.
 #include "jfa_common.h"
 #include "jfa_kernels.h"
+#include "jfa_short.h"
 
 namespace jfa {
 
@@ -588,6 +589,10 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave branches stay scalar
   const int H = a.H;
   const uint32_t gstride = (uint32_t)H * C::ROWB;
+  // First, the short-query sequences: dQ is the sum of their chunks'
+  // partials (previous launch).
+  static_assert(kShortLds <= C::LDS, "combining step fits the LDS");
+  for_short_groups(a.gfirst, a.B * H, lds, [&](int gi) { sq_reduce<T, D>(a, gi); });
   load_queues(a.hdr, &qcur);
   TicketState tk;
 

@@ -1,5 +1,5 @@
-// Backward pass for short-query sequences (at most 64 queries, e.g. a few
-// new events attending to a long history) on gfx950.
+// Backward pass for short-query sequences (at most 64 queries and more than
+// 1024 keys, e.g. a few new events attending to a long history) on gfx950.
 //
 // The split backward ("Jagged Flash Attention (JFA)", section "Four
 // generations", item 2) computes dK/dV per key tile and dQ per query tile in
@@ -7,9 +7,10 @@
 // twice. When a sequence has at most 64 queries they fit one workgroup, which
 // can then own the whole sequence's backward: one item per (b, h, chunk of
 // 1024 keys) reads each K, V row once, forms S, P, dP, dS once, stores the
-// chunk's dK, dV directly and accumulates a partial dQ over its keys. The
-// partials of a sequence's chunks are summed in list order by a second small
-// kernel, so dQ is deterministic and no atomics are used. The same page
+// chunk's dK, dV directly and accumulates a partial dQ over its keys. This
+// pass runs before the dQ pass, whose launch first sums the partials of each
+// sequence's chunks in list order (jfa_short.h), so dQ is deterministic and
+// is never accumulated across workgroups. The same page
 // counts asymmetric query/key lengths among the method's targets (section
 // "Definition").
 //
@@ -305,10 +306,9 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
       }
     }
 
-    // dQ of this chunk, staged in LDS as [64 rows][D] fp32 and written as
-    // whole rows: a sequence with a single chunk stores its dQ (times the
-    // scale) itself; otherwise the unscaled partial goes to item slot it and
-    // the reduce sums the chunks. LDS is free: the last tile ended on a barrier.
+    // Partial dQ of this chunk (unscaled), staged in LDS as [64 rows][D] fp32
+    // and written as whole rows of valid queries to item slot it; the dQ
+    // launch sums the chunks. LDS is free: the last tile ended on a barrier.
 #pragma unroll
     for (int xi = 0; xi < (C::NDQ + 3) / 4; ++xi) {
       const int x = w + 4 * xi;
@@ -323,38 +323,8 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    if (Lk <= KC) {
-      const View dqv = seq_view((char*)a.dq + qrow, Lq, gstride, C::ROWB);
-      rows_out<T, D, QM, C::THREADS>(lds, dqv, gstride, a.scale, tid);
-    } else {
-      const View pv = seq_view(a.dqp + (size_t)it * QM * D, Lq, D * 4, D * 4);
-      rows_out<float, D, QM, C::THREADS>(lds, pv, D * 4, 1.0f, tid);
-    }
-  }
-}
-
-// dQ of each short-query sequence with more than one chunk: the sum, in
-// list order, of its chunks' partials, times the softmax scale. One
-// workgroup per (b, h); four columns per thread, chunks unrolled so that
-// their loads overlap.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void jfa_sq_reduce_kernel(BwdArgs a) {
-  constexpr int QM = kSqQMax;
-  const int gi = blockIdx.x, b = gi / a.H, h = gi % a.H;
-  const int first = a.gfirst[gi];
-  const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-  if (first < 0 || Lk <= kSqKC) return;  // one chunk: the chunk stored dQ itself
-  const int q0 = a.q_off[b], Lq = min(a.q_off[b + 1] - q0, QM);
-  const int n = cdiv(Lk, kSqKC);
-  const float* part = a.dqp + (size_t)first * QM * D;
-  for (int e = threadIdx.x * 4; e < Lq * D; e += 256 * 4) {
-    const int q = e / D, d = e % D;
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int t = 0; t < n; ++t) s += *(const f32x4*)(part + (size_t)t * QM * D + e);
-    T* dst = (T*)a.dq + ((size_t)(q0 + q) * a.H + h) * D + d;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) dst[k] = (T)(s[k] * a.scale);
+    const View pv = seq_view(a.dqp + (size_t)it * QM * D, Lq, D * 4, D * 4);
+    rows_out<float, D, QM, C::THREADS>(lds, pv, D * 4, 1.0f, tid);
   }
 }
 
@@ -367,13 +337,6 @@ static hipError_t launch_sq_t(const BwdArgs& a, long max_items, int num_cus, hip
   }
   const long g = max(1L, min(max_items, (long)num_cus * occ));
   hipLaunchKernelGGL((jfa_sq_kernel<T, D, BIAS>), dim3((unsigned)g), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-template <typename T, int D>
-static hipError_t launch_sq_reduce_t(const BwdArgs& a, hipStream_t st) {
-  const long n = (long)a.B * a.H;
-  if (n > 0) hipLaunchKernelGGL((jfa_sq_reduce_kernel<T, D>), dim3((unsigned)n), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -392,10 +355,6 @@ static hipError_t launch_sq_reduce_t(const BwdArgs& a, hipStream_t st) {
 hipError_t launch_sq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
   if (bias) JFA_SQ_DISPATCH(f32, D, (launch_sq_t<T, DD, true>(a, max_items, num_cus, st)));
   JFA_SQ_DISPATCH(f32, D, (launch_sq_t<T, DD, false>(a, max_items, num_cus, st)));
-}
-
-hipError_t launch_sq_reduce(bool f32, int D, const BwdArgs& a, hipStream_t st) {
-  JFA_SQ_DISPATCH(f32, D, (launch_sq_reduce_t<T, DD>(a, st)));
 }
 
 }  // namespace jfa

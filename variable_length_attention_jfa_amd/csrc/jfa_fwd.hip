@@ -24,6 +24,7 @@
 // element mask (which then also drops keys past the end).
 #include "jfa_common.h"
 #include "jfa_kernels.h"
+#include "jfa_short.h"
 
 namespace jfa {
 
@@ -57,6 +58,10 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave branches stay scalar
   const int H = a.H;
   const uint32_t gstride = (uint32_t)H * C::ROWB;  // bytes between consecutive tokens
+  // First, the short-query sequences: their chunks (previous launch) are
+  // combined into O and lse.
+  static_assert(kShortLds <= C::LDS, "combining step fits the LDS");
+  for_short_groups(a.gfirst, a.B * H, lds, [&](int gi) { fsq_merge<T, D>(a, gi, lds); });
   load_queues(a.hdr, &qcur);
   TicketState tk;
 

@@ -1,21 +1,21 @@
-// Forward pass for short-query sequences (at most 64 queries, e.g. a few new
-// events against a long history) on gfx950, split over the keys.
+// Forward pass for short-query sequences (at most 64 queries and more than
+// 1024 keys, e.g. a few new events against a long history) on gfx950, split
+// over the keys.
 //
 // The regular forward gives one workgroup a whole (b, h, query tile) and walks
 // all its keys. With few queries and many keys that is a long serial stream
 // per item: the grid holds too few bytes in flight, and one long sequence
-// outlasts the rest of the batch. Here a sequence with at most 64 queries is
-// cut into chunks of 1024 keys, one item per (b, h, chunk), placed in the
-// same longest-first list as the other passes. Asymmetric query/key lengths
-// are among the method's targets ("Jagged Flash Attention (JFA)", section
-// "Definition"); its work list and persistent workgroups are item 3 of
-// "Four generations".
+// outlasts the rest of the batch. Here such a sequence is cut into chunks of
+// 1024 keys, one item per (b, h, chunk), placed in a longest-first list like
+// the other passes. Asymmetric query/key lengths are among the method's
+// targets ("Jagged Flash Attention (JFA)", section "Definition"); its work
+// list and persistent workgroups are item 3 of "Four generations".
 //
 // An item computes, for its keys only, the exact softmax-weighted sum of V
 // for each query row, normalised by its own sum, and log2 of that sum (the
-// running max plus log2 of the running sum). A sequence with a single chunk
-// (at most 1024 keys) is then done: the item writes O and lse. Otherwise a
-// second kernel combines the chunks of each (b, h) in list order:
+// running max plus log2 of the running sum). This pass runs before the
+// query-tile forward, whose launch then combines the chunks of each (b, h)
+// in list order (jfa_short.h):
 //   M = max_c lse2_c,  w_c = 2^(lse2_c - M),  O = sum_c w_c O_c / sum_c w_c,
 //   lse = (M + log2 sum_c w_c) * ln 2,
 // which is the softmax over all keys regrouped by chunk (the same identity
@@ -89,7 +89,6 @@ __global__ __launch_bounds__(256, 2) void jfa_fsq_kernel(FwdArgs a) {
     const int q0 = uni(a.q_off[b]), Lq = uni(a.q_off[b + 1]) - q0;
     const int k0 = uni(a.kv_off[b]), Lk = uni(a.kv_off[b + 1]) - k0;
     const int kc0 = chunk * KC;  // first key of the chunk
-    const bool single = Lk <= KC;  // the sequence's only chunk: write O and lse directly
     // Keys of the chunk that some query may see (top-left causal: key j is
     // visible to query i iff j <= i, and i < Lq).
     int kend = min(Lk, kc0 + KC);
@@ -271,88 +270,12 @@ __global__ __launch_bounds__(256, 2) void jfa_fsq_kernel(FwdArgs a) {
           *p = (f32x4){x[0] + o[db][4 * r] * f, x[1] + o[db][4 * r + 1] * f, x[2] + o[db][4 * r + 2] * f,
                        x[3] + o[db][4 * r + 3] * f};
         }
-      if (g == 0) {
-        const float lse2 = L > 0.f ? M + __builtin_amdgcn_logf(L) : -INFINITY;
-        if (single) {
-          if (qi < Lq) a.lse[(size_t)(q0 + qi) * H + h] = lse2 * kLn2;
-        } else {
-          a.lsep[(size_t)it * QM + qi] = lse2;
-        }
-      }
+      if (g == 0) a.lsep[(size_t)it * QM + qi] = L > 0.f ? M + __builtin_amdgcn_logf(L) : -INFINITY;
     }
     __syncthreads();
-    // The chunk's normalised rows, whole rows out (rows past Lq are dropped):
-    // the final O when the sequence has a single chunk, else the partial.
-    if (single) {
-      const View ov = seq_view((char*)a.out + qrow, Lq, gstride, C::ROWB);
-      rows_out<T, D, QM, C::THREADS>(lds, ov, gstride, 1.0f, tid);
-    } else {
-      const View pv = seq_view(a.op + (size_t)it * QM * D, Lq, D * 4, D * 4);
-      rows_out<float, D, QM, C::THREADS>(lds, pv, D * 4, 1.0f, tid);
-    }
-  }
-}
-
-// O and lse of each short-query sequence with more than one chunk, from its
-// chunks combined in list order. One workgroup per (b, h): the first 64
-// threads find each row's max and sum of the chunk weights, then chunk
-// weights go through LDS in batches and every thread accumulates four
-// columns of its rows, the chunk loop unrolled so that loads overlap.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void jfa_fsq_merge_kernel(FwdArgs a) {
-  constexpr int QM = kSqQMax, DV = D / 4, NB = 16, EPT = QM * DV / 256;
-  static_assert(QM * DV % 256 == 0, "row quads divide the workgroup");
-  __shared__ float wl[NB][QM];
-  __shared__ float mrow[QM], srow[QM];
-  const int gi = blockIdx.x, b = gi / a.H, h = gi % a.H, tid = threadIdx.x;
-  const int first = a.gfirst[gi];
-  const int Lk = a.kv_off[b + 1] - a.kv_off[b];
-  if (first < 0 || Lk <= kSqKC) return;  // one chunk: the chunk wrote O and lse itself
-  const int q0 = a.q_off[b], Lq = min(a.q_off[b + 1] - q0, QM);
-  const int n = cdiv(Lk, kSqKC);
-  const float* lp = a.lsep + (size_t)first * QM;  // chunk c, row q at lp[c * QM + q]
-  if (tid < Lq) {
-    float M = -INFINITY, S = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < n; ++c) M = fmaxf(M, lp[c * QM + tid]);
-    if (M > -INFINITY) {
-#pragma unroll 4
-      for (int c = 0; c < n; ++c) S += __builtin_amdgcn_exp2f(lp[c * QM + tid] - M);
-    }
-    mrow[tid] = M;
-    srow[tid] = S;
-    a.lse[(size_t)(q0 + tid) * a.H + h] = S > 0.f ? (M + __builtin_amdgcn_logf(S)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
-  f32x4 acc[EPT];
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < n; c0 += NB) {
-    const int nb = min(NB, n - c0);
-    for (int i = tid; i < nb * QM; i += 256) {
-      const int c = i / QM, q = i % QM;
-      wl[c][q] = q < Lq && srow[q] > 0.f ? __builtin_amdgcn_exp2f(lp[(c0 + c) * QM + q] - mrow[q]) / srow[q] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const int e = tid + 256 * j, q = e / DV, d = (e % DV) * 4;
-      if (q < Lq) {
-        const float* src = a.op + ((size_t)(first + c0) * QM + q) * D + d;
-#pragma unroll 4
-        for (int c = 0; c < nb; ++c) acc[j] += wl[c][q] * *(const f32x4*)(src + (size_t)c * QM * D);
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int e = tid + 256 * j, q = e / DV, d = (e % DV) * 4;
-    if (q < Lq) {
-      T* dst = (T*)a.out + ((size_t)(q0 + q) * a.H + h) * D + d;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) dst[k] = (T)acc[j][k];
-    }
+    // The chunk's normalised rows, whole rows out (rows past Lq are dropped).
+    const View pv = seq_view(a.op + (size_t)it * QM * D, Lq, D * 4, D * 4);
+    rows_out<float, D, QM, C::THREADS>(lds, pv, D * 4, 1.0f, tid);
   }
 }
 
@@ -365,13 +288,6 @@ static hipError_t launch_fsq_t(const FwdArgs& a, long max_items, int num_cus, hi
   }
   const long g = max(1L, min(max_items, (long)num_cus * occ));
   hipLaunchKernelGGL((jfa_fsq_kernel<T, D, BIAS>), dim3((unsigned)g), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-template <typename T, int D>
-static hipError_t launch_fsq_merge_t(const FwdArgs& a, hipStream_t st) {
-  const long n = (long)a.B * a.H;
-  if (n > 0) hipLaunchKernelGGL((jfa_fsq_merge_kernel<T, D>), dim3((unsigned)n), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -390,10 +306,6 @@ static hipError_t launch_fsq_merge_t(const FwdArgs& a, hipStream_t st) {
 hipError_t launch_fsq(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
   if (bias) JFA_FSQ_DISPATCH(f32, D, (launch_fsq_t<T, DD, true>(a, max_items, num_cus, st)));
   JFA_FSQ_DISPATCH(f32, D, (launch_fsq_t<T, DD, false>(a, max_items, num_cus, st)));
-}
-
-hipError_t launch_fsq_merge(bool f32, int D, const FwdArgs& a, hipStream_t st) {
-  JFA_FSQ_DISPATCH(f32, D, (launch_fsq_merge_t<T, DD>(a, st)));
 }
 
 }  // namespace jfa

@@ -63,7 +63,7 @@ struct PlanPass {
   int TM, TN;     // query rows / keys per tile and per visited block (sq: keys per chunk)
   int kind;       // PlanKind
   int nq;         // queues (one per XCD)
-  int short_q;    // q and kv passes: sequences with Lq <= short_q get no items (-1: none)
+  int short_q;    // q and kv passes: sequences with Lq <= short_q and more than kSqKC keys get no items (-1: none)
   int* gfirst;    // sq pass: [B*H] list position of chunk 0 of each (b, h), -1 if none
 };
 
@@ -76,11 +76,13 @@ struct PlanArgs {
   PlanPass pass[3];
 };
 
-// Short-query passes: sequences with at most kSqQMax queries are cut into
-// chunks of kSqKC keys, one workgroup per (b, h, chunk), in the forward
-// (split over the keys, chunks merged per (b, h)) and in the backward (one
-// pass over K/V, dQ partials summed per (b, h)).
+// Short-query passes: sequences with at most kSqQMax queries and more than
+// kSqKC keys are cut into chunks of kSqKC keys, one workgroup per (b, h,
+// chunk), in the forward (split over the keys, chunks merged per (b, h)) and
+// in the backward (one pass over K/V, dQ partials summed per (b, h)). The
+// other passes skip them.
 constexpr int kSqQMax = 64, kSqKC = 1024, kSqKT = 64;
+__host__ __device__ inline bool short_query(int Lq, int Lk) { return Lq <= kSqQMax && Lk > kSqKC; }
 
 // Tile shapes (query rows x keys) of each kernel. The forward's waves per
 // workgroup (32 query rows each) depend on the element type and D.
@@ -96,14 +98,14 @@ int dkv_tile_rows(bool f32, int D);
 constexpr int kDqTM = 128, kDqTN = 64;
 
 // Persistent launches: grid = min(max_items, CUs x resident workgroups per CU).
+// The short-query chunk passes run first; the forward launch then merges the
+// chunks of each sequence and the dQ launch sums its partial dQ.
 hipError_t launch_fwd(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
 hipError_t launch_fsq(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
-hipError_t launch_fsq_merge(bool f32, int D, const FwdArgs& a, hipStream_t st);
 hipError_t launch_delta(bool f32, int D, const BwdArgs& a, hipStream_t st);
 hipError_t launch_dkdv(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
 hipError_t launch_dq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
 hipError_t launch_sq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
-hipError_t launch_sq_reduce(bool f32, int D, const BwdArgs& a, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, int npass, hipStream_t st);
 hipError_t launch_scan(const int* lengths, int B, int* offsets, hipStream_t st);
 

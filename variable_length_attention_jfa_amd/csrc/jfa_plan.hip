@@ -36,8 +36,8 @@ constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanMaxB = 8192;
 
 __device__ __forceinline__ int plan_tiles(int Lq, int Lk, const PlanPass& p) {
-  if (p.kind == kPassSQ) return Lq <= kSqQMax ? max(1, cdiv(Lk, p.TN)) : 0;
-  if (Lq <= p.short_q) return 0;
+  if (p.kind == kPassSQ) return short_query(Lq, Lk) ? cdiv(Lk, p.TN) : 0;
+  if (Lq <= p.short_q && Lk > kSqKC) return 0;
   return p.kind == kPassKV ? cdiv(Lk, p.TN) : cdiv(Lq, p.TM);
 }
 
