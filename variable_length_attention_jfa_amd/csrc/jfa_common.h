@@ -412,11 +412,9 @@ struct TicketState {
 // queue (the one its XCD drains) and, once that is empty, from the others in
 // turn. Tickets are taken one at a time, when the previous item is done: a
 // workgroup never holds a claim on an item it is not working on, so the
-// longest-first order decides which items start first. Queues the plan left
-// empty are passed over without touching their ticket, so a pass with no
-// items (a batch without short-query sequences, say) ends at once, and a
-// queue is read before a ticket is taken from it, so the workgroups that
-// arrive after a short list is drained do not queue up on its counter.
+// longest-first order decides which items start first. Queues the plan
+// left empty are passed over without touching their ticket, so a pass with
+// no items (a batch without short-query sequences, say) ends at once.
 // Returns -1 when every queue is empty.
 __device__ __forceinline__ int next_item(PlanHeader* hdr, QueueCursor* qc, TicketState& ts) {
   __syncthreads();  // queue bounds loaded; every wave is done with the previous item's slot
@@ -427,8 +425,7 @@ __device__ __forceinline__ int next_item(PlanHeader* hdr, QueueCursor* qc, Ticke
     }
     int it = -1;
     while (ts.left > 0) {
-      if (qc->count[ts.q] > 0 &&
-          __hip_atomic_load(&hdr->ticket[ts.q].value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < qc->count[ts.q]) {
+      if (qc->count[ts.q] > 0) {
         const int t = __hip_atomic_fetch_add(&hdr->ticket[ts.q].value, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (t < qc->count[ts.q]) {
           it = qc->start[ts.q] + t;

@@ -108,8 +108,6 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
   __shared__ int wsum[2 * kPlanWaves];
   __shared__ int qtotal[kMaxQueues], qstart[kMaxQueues], qcarry[kMaxQueues];
   __shared__ int excl[kPlanThreads];
-  __shared__ int gbase[kPlanThreads];
-  __shared__ int2 gbh[kPlanThreads];
 
   const PlanPass p = a.pass[blockIdx.x];
   const int tid = threadIdx.x;
@@ -139,9 +137,14 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
     for (int x = tid; x < B * H; x += kPlanThreads) p.gfirst[x] = -1;
   __syncthreads();
 
-  // 2. bitonic sort of the P keys (ascending: cost descending, then b)
+  // 2. bitonic sort of the P keys (ascending: cost descending, then b).
+  //    Compare-exchange steps of stride 64 and more go through LDS, one
+  //    barrier each; the steps of smaller stride pair lanes of one wave and
+  //    run in registers with cross-lane shuffles (1024 is a multiple of 64,
+  //    so element i sits in lane i mod 64 of its wave).
   for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
+    int j = k >> 1;
+    for (; j >= 64; j >>= 1) {
       for (int i = tid; i < P; i += kPlanThreads) {
         const int ixj = i ^ j;
         if (ixj > i) {
@@ -155,6 +158,19 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
       }
       __syncthreads();
     }
+    for (int base = 0; base < P; base += kPlanThreads) {  // uniform bound: whole waves take part in the shuffles
+      const int i = base + tid;
+      unsigned long long x = i < P ? key[i] : ~0ull;
+      const bool up = (i & k) == 0;
+      for (int jj = j; jj > 0; jj >>= 1) {
+        const unsigned lo = __shfl_xor((unsigned)x, jj), hi = __shfl_xor((unsigned)(x >> 32), jj);
+        const unsigned long long y = ((unsigned long long)hi << 32) | lo;
+        const bool keep_min = ((i & jj) == 0) == up;  // lower element of an ascending pair keeps the min
+        x = keep_min ? (x < y ? x : y) : (x < y ? y : x);
+      }
+      if (i < P) key[i] = x;
+    }
+    __syncthreads();
   }
 
   // 3. queue sizes (group g = rank * H + h goes to queue snake(g))
@@ -187,8 +203,8 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
 
   // 4. positions inside each queue, chunk by chunk. Thread tid of a chunk
   //    handles the i-th group of queue x in that chunk, so that each queue's
-  //    groups are contiguous in one block scan; then all threads write the
-  //    chunk's items, one item per thread at a time.
+  //    groups are contiguous in one block scan, and writes that group's
+  //    items.
   const int per_q = kPlanThreads / NQ;  // groups of one queue in a chunk of kPlanThreads groups
   const int x = tid / per_q, i = tid % per_q;
   for (int c0 = 0; c0 < G; c0 += kPlanThreads) {
@@ -203,25 +219,19 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
     excl[tid] = ex;
     __syncthreads();
     const int pos = ex - excl[x * per_q];
-    gbase[tid] = qstart[x] + qcarry[x] + pos;  // first item of this group in the list
-    gbh[tid] = make_int2(b, g < G ? g % H : 0);
-    if (p.gfirst && n > 0) p.gfirst[b * H + g % H] = gbase[tid];  // chunk 0 is first (costs non-increasing)
+    const long gbase = (long)qstart[x] + qcarry[x] + pos;  // first item of this group in the list
+    if (p.gfirst && n > 0) p.gfirst[b * H + g % H] = (int)gbase;  // chunk 0 is first (costs non-increasing)
     __syncthreads();
     if (i == per_q - 1) qcarry[x] += pos + n;  // last group of queue x in this chunk
-    for (int f = tid; f < tot; f += kPlanThreads) {
-      int lo = 0, hi = kPlanThreads - 1;  // last thread slot with excl <= f
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (excl[mid] <= f) lo = mid; else hi = mid - 1;
+    // The thread writes its group's items.
+    if (n > 0) {
+      const int h = g % H, Lq = lq_s[b], Lk = lk_s[b];
+      for (int t = 0; t < n; ++t) {
+        const long at = gbase + plan_pos(Lq, Lk, t, n, p, a.causal);
+        if (at >= 0 && at < p.capacity) p.items[at] = make_int4(b, h, t, plan_cost(Lq, Lk, t, p, a.causal));
       }
-      const int gb = gbh[lo].x, gh = gbh[lo].y;
-      const int t = f - excl[lo];
-      const int Lq = lq_s[gb], Lk = lk_s[gb];
-      const int nt = plan_tiles(Lq, Lk, p);
-      const long at = (long)gbase[lo] + plan_pos(Lq, Lk, t, nt, p, a.causal);
-      if (at >= 0 && at < p.capacity) p.items[at] = make_int4(gb, gh, t, plan_cost(Lq, Lk, t, p, a.causal));
     }
-    __syncthreads();
+    __syncthreads();  // qcarry of the next chunk
   }
 }
 
