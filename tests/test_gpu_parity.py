@@ -3,6 +3,8 @@
 Sizes here let the oracle finish in seconds while still spanning several
 tiles and a ragged tail; full-size workloads are in test_gpu_full.py.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -236,3 +238,22 @@ def test_invalid_arguments_raise():
 def ctypes_offset(t, nbytes):
     import ctypes
     return ctypes.c_void_p(t.data_ptr() + nbytes)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_masking_study_variants(mode, cfg):
+    """The -inf masking variants of the instruction-mix study compute the same
+    forward as the subtraction (the oracle decides)."""
+    from variable_length_attention_jfa_amd import mask_study
+    path = mask_study.lib_path(mode)
+    if not os.path.exists(path):
+        pytest.skip("study variants not built (python -m variable_length_attention_jfa_amd.mask_study --build)")
+    saved = jfa.LIB_PATH
+    try:
+        jfa._LIB = None
+        jfa.LIB_PATH = path
+        _check(gen.make_batch(SMALL[cfg]), with_bwd=False, label=f"masking mode {mode} cfg{cfg}")
+    finally:
+        jfa._LIB = None
+        jfa.LIB_PATH = saved

@@ -26,32 +26,36 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-ta
          "-packed-fp32-ops", "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src: str, save_temps: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, save_temps: bool, objdir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     if save_temps:
         cmd.insert(1, "--save-temps")
-    r = subprocess.run(cmd, cwd=BUILD, capture_output=True, text=True)
+    r = subprocess.run(cmd, cwd=objdir, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n" + "\n".join(msgs))
     return obj
 
 
-def build(jobs: int = 4, save_temps: bool = False, verbose: bool = True) -> str:
+def build(jobs: int = 4, save_temps: bool = False, verbose: bool = True, defines=(), out: str = LIB,
+          objdir: str = BUILD) -> str:
+    """Compiles every source and links `out` (the library by default; other
+    `defines` and paths build study variants next to it)."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(objdir, exist_ok=True)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, save_temps), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, save_temps, objdir, defines), SOURCES))
+    tmp = out + ".tmp"
     r = subprocess.run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 def main(argv=None) -> int:

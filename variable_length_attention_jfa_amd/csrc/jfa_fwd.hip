@@ -26,7 +26,19 @@
 #include "jfa_kernels.h"
 #include "jfa_short.h"
 
+// How keys past a sequence's end leave the softmax. 0: they load as zeros and
+// their exp terms are subtracted once in the epilogue (the method). 1 and 2
+// exist only for an instruction-mix study against -inf masking: 1 masks them
+// with -inf in the block that holds them, 2 bounds-checks every key of every
+// block as a padded kernel would.
+#ifndef JFA_FWD_MASK_MODE
+#define JFA_FWD_MASK_MODE 0
+#endif
+
 namespace jfa {
+
+constexpr int kFwdMaskMode = JFA_FWD_MASK_MODE;
+static_assert(kFwdMaskMode >= 0 && kFwdMaskMode <= 2, "mask mode");
 
 template <typename T, int D>
 struct FwdTiles {
@@ -130,7 +142,9 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
       const int key0 = j * BN;
       const bool active = wave_on && (!a.causal || key0 <= wr0 + 31);
       if (active) {
-        const bool masked = a.causal && (key0 + BN - 1 > wr0);
+        const bool masked = (a.causal && (key0 + BN - 1 > wr0)) || kFwdMaskMode == 2 ||
+                            (kFwdMaskMode == 1 && key0 + BN > Lk);
+        const bool cmask = kFwdMaskMode == 0 || a.causal;  // with the subtraction, masked blocks are causal ones
         last_tile = j;
         last_masked = masked;
         const lds_t* kt = lds + s * C::STAGE;
@@ -161,7 +175,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
               const int kj = key0 + 32 * kb + res_row(i, g);
               float x = sc[kb][i] * a.scale2;
               if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
-              if (masked && (kj > qi || kj >= Lk)) x = -INFINITY;
+              if (masked && ((cmask && kj > qi) || kj >= Lk)) x = -INFINITY;
               sc[kb][i] = x;
               mx = fmaxf(mx, x);
             }
