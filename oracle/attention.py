@@ -22,6 +22,8 @@ Sources:
     calculus of the definition above:
       dV = P^T dO;  dP = dO V^T;  Delta_i = sum_d dO_id O_id = sum_j P_ij dP_ij
       dS = P * (dP - Delta);  dQ = dS K / sqrt(D);  dK = dS^T Q / sqrt(D)
+    and, as beta[h, r] is added to every score with clip(i - j) + R = r,
+      dbeta[h, r] = sum over b and visible (i, j) of that bin of dS_ij
 
 This is the plain definition evaluated sequence by sequence in fp64, with the
 query rows cut into blocks only to bound memory (each block is exact: causal
@@ -161,3 +163,47 @@ def backward(q, k, v, dout, q_offsets, kv_offsets, bias=None, causal: bool = Fal
         dk[ks:ke, h] = dK
         dv[ks:ke, h] = dV
     return dq, dk, dv
+
+
+def bias_grad(q, k, v, dout, q_offsets, kv_offsets, bias, causal: bool = False,
+              scale: Optional[float] = None, pairs=None, row_block: int = 512, out=None, lse=None):
+    """Gradient of sum(dout * O) with respect to the bias table (fp64, [H, 2R+1]).
+
+    beta[h, r] enters every score S_ij of head h whose relative position falls
+    in bin r = clip(i - j, -R, R) + R, so its gradient is the sum of dS_ij
+    (the gradient with respect to S_ij) over those pairs, over all sequences.
+    Pairs the causal mask hides have P = 0, hence dS = 0.
+    """
+    Tq, H, D = q.shape
+    qo = np.asarray(q_offsets, dtype=np.int64)
+    ko = np.asarray(kv_offsets, dtype=np.int64)
+    B = len(qo) - 1
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None or lse is None:
+        out, lse = forward(q, k, v, qo, ko, bias, causal, scale, pairs, row_block)
+    nbins = 2 * BIAS_RADIUS + 1
+    dbias = np.zeros((H, nbins), dtype=np.float64)
+    for b, h in _selected(B, H, pairs):
+        qs, qe, ks, ke = int(qo[b]), int(qo[b + 1]), int(ko[b]), int(ko[b + 1])
+        Lq, Lk = qe - qs, ke - ks
+        if Lq == 0 or Lk == 0:
+            continue
+        Q = q[qs:qe, h].astype(np.float64)
+        K = k[ks:ke, h].astype(np.float64)
+        V = v[ks:ke, h].astype(np.float64)
+        dO = dout[qs:qe, h].astype(np.float64)
+        O = np.asarray(out[qs:qe, h], dtype=np.float64)
+        L = np.asarray(lse[qs:qe, h], dtype=np.float64)
+        for r0 in range(0, Lq, row_block):
+            r1 = min(r0 + row_block, Lq)
+            ncol = min(Lk, r1) if causal else Lk
+            S = _scores(Q[r0:r1], K, h, r0, r1, ncol, scale, bias, causal)
+            P = np.exp(S - L[r0:r1, None])
+            dP = dO[r0:r1] @ V[:ncol].T
+            delta = (dO[r0:r1] * O[r0:r1]).sum(axis=1)
+            dS = P * (dP - delta[:, None])
+            i = np.arange(r0, r1)[:, None]
+            j = np.arange(ncol)[None, :]
+            bins = np.clip(i - j, -BIAS_RADIUS, BIAS_RADIUS) + BIAS_RADIUS
+            dbias[h] += np.bincount(bins.ravel(), weights=dS.ravel(), minlength=nbins)
+    return dbias

@@ -252,3 +252,78 @@ def test_pairs_subset_matches_full():
     for a, s in zip(full, sub):
         np.testing.assert_array_equal(a[qo[2]:qo[3], 1] if a.shape[0] == q.shape[0] else a[ko[2]:ko[3], 1],
                                       s[qo[2]:qo[3], 1] if s.shape[0] == q.shape[0] else s[ko[2]:ko[3], 1])
+
+
+def _sdpa_padded_dbias(qo, ko, q, k, v, do, bt, causal):
+    """Gradient of sum(dO * O) with respect to the bias table through torch
+    autograd (fp64): the padded additive mask is gathered from a leaf tensor."""
+    B = len(qo) - 1
+    H, D = q.shape[1], q.shape[2]
+    lq, lk = np.diff(qo), np.diff(ko)
+    Mq, Mk = max(int(lq.max()), 1), max(int(lk.max()), 1)
+    Qp = torch.zeros(B, H, Mq, D, dtype=torch.float64)
+    Kp = torch.zeros(B, H, Mk, D, dtype=torch.float64)
+    Vp = torch.zeros(B, H, Mk, D, dtype=torch.float64)
+    dOp = torch.zeros(B, H, Mq, D, dtype=torch.float64)
+    ok = torch.zeros(B, Mq, Mk, dtype=torch.bool)
+    i = torch.arange(Mq)[:, None]
+    j = torch.arange(Mk)[None, :]
+    for b in range(B):
+        a, e, c, f = int(qo[b]), int(qo[b + 1]), int(ko[b]), int(ko[b + 1])
+        Qp[b, :, :e - a] = torch.from_numpy(q[a:e]).transpose(0, 1)
+        Kp[b, :, :f - c] = torch.from_numpy(k[c:f]).transpose(0, 1)
+        Vp[b, :, :f - c] = torch.from_numpy(v[c:f]).transpose(0, 1)
+        dOp[b, :, :e - a] = torch.from_numpy(do[a:e]).transpose(0, 1)
+        vis = (j < f - c) & ((j <= i) if causal else torch.ones_like(j <= i))
+        vis = torch.where(i < e - a, vis, j == 0)  # padded query rows: any finite row, discarded later
+        ok[b] = vis
+    beta = torch.from_numpy(bt.copy()).requires_grad_(True)
+    idx = (torch.clamp(i - j, -R, R) + R).expand(Mq, Mk)
+    mask = torch.where(ok[:, None], beta[:, idx][None], torch.tensor(-math.inf, dtype=torch.float64))
+    O = F.scaled_dot_product_attention(Qp, Kp, Vp, attn_mask=mask)
+    (O * dOp).sum().backward()
+    return beta.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("asym", [False, True])
+def test_bias_grad_matches_autograd(causal, asym):
+    """The bias gradient against torch autograd through a padded dense
+    attention whose mask is gathered from the bias table; lengths reach past
+    the clipping radius so the end bins collect many distances."""
+    rng = np.random.default_rng(31 + causal + 2 * asym)
+    qo, ko, q, k, v, do, bt = _rand_batch(rng, 3, 2, 8, (1, 150), (1, 300) if asym else None, True)
+    got = oracle.bias_grad(q, k, v, do, qo, ko, bt, causal, row_block=37)
+    ref = _sdpa_padded_dbias(qo, ko, q, k, v, do, bt, causal)
+    np.testing.assert_allclose(got, ref, atol=1e-10, rtol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bias_grad_sums_to_zero_and_single_key(causal):
+    """Every row of dS sums to zero, so do the bins of each head; one key per
+    sequence gives P = 1 and dS = 0 everywhere."""
+    rng = np.random.default_rng(41 + causal)
+    qo, ko, q, k, v, do, bt = _rand_batch(rng, 4, 3, 8, (1, 200), None if causal else (1, 260), True)
+    g = oracle.bias_grad(q, k, v, do, qo, ko, bt, causal)
+    np.testing.assert_allclose(g.sum(axis=1), 0.0, atol=1e-10)
+    assert np.abs(g).max() > 1e-3
+    qo1, ko1, q1, k1, v1, do1, bt1 = _rand_batch(rng, 3, 2, 8, (1, 9), (1, 1), True)
+    np.testing.assert_allclose(oracle.bias_grad(q1, k1, v1, do1, qo1, ko1, bt1, False), 0.0, atol=1e-12)
+
+
+def test_bias_grad_finite_differences():
+    rng = np.random.default_rng(43)
+    qo, ko, q, k, v, do, bt = _rand_batch(rng, 2, 2, 4, (2, 9), (2, 11), True)
+    g = oracle.bias_grad(q, k, v, do, qo, ko, bt, False)
+
+    def loss(b_):
+        o, _ = oracle.forward(q, k, v, qo, ko, b_, False)
+        return float((o * do).sum())
+
+    eps = 1e-6
+    for h, r in ((0, R), (1, R - 3), (0, R + 5), (1, R + 1)):
+        plus, minus = bt.copy(), bt.copy()
+        plus[h, r] += eps
+        minus[h, r] -= eps
+        fd = (loss(plus) - loss(minus)) / (2 * eps)
+        assert abs(fd - g[h, r]) <= 1e-7 * max(1.0, abs(g[h, r])), (h, r, fd, g[h, r])
