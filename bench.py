@@ -93,7 +93,7 @@ KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "fsq": 4, "dkdv": 8, "dq": 6, "sq": 10}
 KERNEL_SEQS = {"forward": "long", "fsq": "short", "dkdv": "long", "dq": "long", "sq": "short"}
 
 
-def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None):
+def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None, bias_grad=False):
     wl = gen.WORKLOADS[idx]
     batch = gen.make_batch(wl, seed=seed)
     dev = torch.device("cuda")
@@ -114,7 +114,7 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None)
 
     def step():
         jfa.forward(q, k, v, qo, ko, bias, wl.causal, out=out, lse=lse)
-        jfa.backward(q, k, v, out, lse, do, qo, ko, bias, wl.causal, dq=dq, dk=dk, dv=dv)
+        jfa.backward(q, k, v, out, lse, do, qo, ko, bias, wl.causal, dq=dq, dk=dk, dv=dv, bias_grad=bias_grad)
 
     for _ in range(warmup):
         step()
@@ -143,7 +143,7 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None)
     # the plan kind covers one launch in forward and one in backward per step
     plan_ms = kt["plan"][0] / max(kt["plan"][1], 1)
     fwd_ms = (kt["forward"][0] + kt["fsq"][0]) / steps + plan_ms
-    bwd_ms = (kt["delta"][0] + kt["dkdv"][0] + kt["dq"][0] + kt["sq"][0]) / steps + plan_ms
+    bwd_ms = (kt["delta"][0] + kt["dkdv"][0] + kt["dq"][0] + kt["sq"][0] + kt["dbias"][0]) / steps + plan_ms
     res = {
         "workload": wl.name, "B": wl.B, "H": wl.H, "D": wl.D, "dtype": wl.dtype, "causal": wl.causal,
         "bias": wl.bias, "seed": wl.seed if seed is None else seed, "total_q": batch.total_q,
@@ -238,6 +238,8 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="also report workloads 1..5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--bias-grad", action="store_true",
+                    help="the backward also returns the bias-table gradient (workloads with a bias)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="also run a plain device copy of MB mebibytes (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -265,7 +267,10 @@ def main(argv=None):
         del src, dst
         torch.cuda.empty_cache()
 
-    main_res = run_workload(args.workload, args.steps, args.warmup, torch, jfa, gen)
+    if args.bias_grad and not gen.WORKLOADS[args.workload].bias:
+        print(f"bench.py: workload {args.workload} has no bias; --bias-grad needs one", file=sys.stderr)
+        return 2
+    main_res = run_workload(args.workload, args.steps, args.warmup, torch, jfa, gen, bias_grad=args.bias_grad)
     print(f"[bench] workload {args.workload}: {main_res['tflops_step']:.1f} TFLOP/s fwd+bwd, "
           f"fwd {main_res['fwd_tflops']:.1f} bwd {main_res['bwd_tflops']:.1f}", file=sys.stderr, flush=True)
     extra_ids = list(range(1, 6)) if args.all else [int(x) for x in args.also.split(",") if x.strip()]
@@ -301,7 +306,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={wl.B}, lengths U[{wl.q_len.lo},{wl.q_len.hi}], H={wl.H}, "
                                f"D={wl.D}, {wl.dtype}, causal={wl.causal}, bias={wl.bias}",
-                   "B": wl.B, "H": wl.H, "D": wl.D, "seed": main_res["seed"], "total_tokens": main_res["total_q"],
+                   "B": wl.B, "H": wl.H, "D": wl.D, "bias_grad": args.bias_grad, "seed": main_res["seed"],
+                   "total_tokens": main_res["total_q"],
                    "valid_pairs_per_head": main_res["valid_pairs_per_head"]},
         "pct_mfma_peak": 100.0 * main_res["tflops_step"] / PEAK_BF16_TFLOPS,
         "fwd_tflops": main_res["fwd_tflops"], "fwd_pct_peak": main_res["fwd_pct_peak"],

@@ -62,6 +62,7 @@ typedef enum {
 } jfa_status;
 
 #define JFA_BIAS_RADIUS 128 /* bias table is [H][2 * JFA_BIAS_RADIUS + 1] */
+#define JFA_BIAS_LEN (2 * JFA_BIAS_RADIUS + 1)
 #define JFA_MAX_BATCH 8192  /* largest B accepted by one call */
 #define JFA_MAX_HEADS 65535 /* largest H accepted by one call */
 #define JFA_PLAN_QUEUES 8   /* work-list queues, one per XCD */
@@ -107,12 +108,20 @@ jfa_status jfa_fwd(const void* q, const void* k, const void* v, const int32_t* q
  * queries and more than 1024 keys is instead owned whole by one workgroup
  * per chunk of 1024 keys, which forms S and dP once and reads K, V once; its
  * dQ is the sum, in a fixed order, of the chunks' partial results
- * (asymmetric query/key lengths, section "Definition"). No gradient for the
- * bias. */
+ * (asymmetric query/key lengths, section "Definition").
+ *
+ * dbias: NULL, or an fp32 [H][JFA_BIAS_LEN] array (caller-owned, device
+ * memory) that receives the gradient of sum(dout * out) with respect to the
+ * bias table: dbias[h][r] is the sum, over every sequence and visible
+ * (query i, key j) pair of head h with clip(i - j) + JFA_BIAS_RADIUS = r, of
+ * the gradient with respect to that pair's score, dS = P * (dP - Delta)
+ * (the bias is one of the custom attention biases of "Definition"). Needs
+ * `bias` (JFA_ERR_INVALID_ARGUMENT otherwise). Computed in a fixed order,
+ * so it is bit-identical run to run. */
 jfa_status jfa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
                    const void* dout, const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H,
                    int D, int64_t total_q, int64_t total_kv, const float* bias, int causal, void* dq,
-                   void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+                   void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
 /* fp32 twins: identical parameters, every tensor of element type fp32;
  * D must be 32 or 64 (JFA_ERR_UNSUPPORTED for 128). */
@@ -123,7 +132,7 @@ jfa_status jfa_fwd_f32(const void* q, const void* k, const void* v, const int32_
 jfa_status jfa_bwd_f32(const void* q, const void* k, const void* v, const void* out, const float* lse,
                        const void* dout, const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H,
                        int D, int64_t total_q, int64_t total_kv, const float* bias, int causal, void* dq,
-                       void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+                       void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
 /* offsets[0] = 0, offsets[b+1] = offsets[b] + lengths[b] for b < B (device
  * int32 arrays, lengths [B], offsets [B+1]); the prefix-sum addressing of
@@ -165,9 +174,9 @@ size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv,
 /* Launch timing, for benchmarks and profiling. While enabled, every kernel
  * launch of this library is bracketed by two HIP events recorded on its
  * stream (a few microseconds of host overhead per launch). */
-#define JFA_TIMING_KINDS 8 /* 0 plan, 1 forward (with the short-query chunk merge), 2 delta, 3 dK/dV, \
+#define JFA_TIMING_KINDS 9 /* 0 plan, 1 forward (with the short-query chunk merge), 2 delta, 3 dK/dV, \
                              4 dQ (with the short-query dQ sum), 5 offsets scan, 6 short-query backward chunks, \
-                             7 short-query forward chunks */
+                             7 short-query forward chunks, 8 bias-gradient sum */
 jfa_status jfa_timing_enable(int enable);
 
 /* Waits for every recorded launch, writes the summed kernel milliseconds and

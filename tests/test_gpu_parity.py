@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import BF16_TOL, compare_backward, compare_forward, raw_forward_error, to_device, tol_for
+from helpers import BF16_TOL, compare_backward, compare_forward, raw_forward_error, rel_l2, to_device, tol_for
 from variable_length_attention_jfa_amd import inputs as gen
 from variable_length_attention_jfa_amd import jfa
 
@@ -257,3 +257,55 @@ def test_masking_study_variants(mode, cfg):
     finally:
         jfa._LIB = None
         jfa.LIB_PATH = saved
+
+
+def _check_dbias(batch, label):
+    print(f"[case] dbias {label} B={len(batch.q_lengths)} H={batch.wl.H} D={batch.wl.D} dtype={batch.wl.dtype} "
+          f"causal={batch.wl.causal} Tq={batch.total_q} Tk={batch.total_kv}", flush=True)
+    d = to_device(batch)
+    args = (d["q"], d["k"], d["v"])
+    out, lse = jfa.forward(*args, d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal)
+    g0 = jfa.backward(*args, out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal)
+    g1 = jfa.backward(*args, out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal,
+                      bias_grad=True)
+    g2 = jfa.backward(*args, out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal,
+                      bias_grad=True)
+    torch.cuda.synchronize()
+    ref = oracle.bias_grad(batch.q, batch.k, batch.v, batch.dout, batch.q_offsets, batch.kv_offsets, batch.bias,
+                           batch.wl.causal)
+    got = g1[3].cpu().numpy()
+    e = rel_l2(got, ref)
+    print(f"   dbias relL2={e:.3e} |ref|max={np.abs(ref).max():.3e} sum over bins={got.sum(axis=1)}", flush=True)
+    assert e <= tol_for(batch)["grad"], f"bias gradient error {e}"
+    assert torch.equal(g1[3], g2[3]), "bias gradient must be bit-identical run to run"
+    for x, y in zip(g0, g1[:3]):  # asking for dbias leaves dq, dk, dv as they were
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("f32", 32), ("f32", 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bias_gradient(dtype, D, causal):
+    """Bias gradient through the dK/dV pass (one-role and paired kernels) and
+    the short-query owner: distances inside and beyond the clipping radius,
+    several chunks, asymmetric and empty sequences."""
+    ql = [300, 40, 0, 70, 5, 1, 600, 64]
+    kl = [300, 2100, 500, 40, 1500, 1, 650, 1025]
+    wl = gen.Workload("db", len(ql), 2, D, dtype, causal, True, gen.LengthDist("fixed", 1, 1), seed=71)
+    _check_dbias(gen.make_batch(wl, q_lengths=ql, kv_lengths=kl, with_dout=True), f"{dtype} D={D} causal={causal}")
+
+
+def test_bias_gradient_workload4_small():
+    _check_dbias(gen.make_batch(SMALL[4], with_dout=True), "small cfg4")
+
+
+def test_bias_gradient_no_pairs():
+    wl = gen.Workload("db0", 3, 2, 64, "bf16", False, True, gen.LengthDist("fixed", 1, 1), seed=72)
+    batch = gen.make_batch(wl, q_lengths=[0, 0, 0], kv_lengths=[0, 0, 0], with_dout=True)
+    d = to_device(batch)
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    g = jfa.backward(d["q"], d["k"], d["v"], out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], d["bias"], False,
+                     bias_grad=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(g[3]) == 0

@@ -55,11 +55,19 @@ def test_invalid_arguments_rejected_on_host(L):
     st = L.jfa_fwd(None, None, None, None, None, -1, 1, 64, 0, 0, None, 0, None, None, None, 0, None)
     assert st == 1
     assert b"invalid sizes" in L.jfa_last_error()
-    st = L.jfa_bwd(None, None, None, None, None, None, None, None, 4, 0, 64, 0, 0, None, 0, None, None, None, None, 0,
-                   None)
+    st = L.jfa_bwd(None, None, None, None, None, None, None, None, 4, 0, 64, 0, 0, None, 0, None, None, None, None, None,
+                   0, None)
     assert st == 1
     st = L.jfa_fwd(None, None, None, None, None, 2, 2, 64, 0, 0, None, 0, None, None, None, 0, None)
     assert st == 1 and b"offsets" in L.jfa_last_error()
     dummy = ctypes.c_void_p(4096)
     st = L.jfa_fwd(dummy, dummy, dummy, dummy, dummy, 2, 2, 64, 10, 10, None, 0, dummy, dummy, None, 0, None)
     assert st == 2
+
+
+def test_bias_gradient_needs_bias(L):
+    dummy = ctypes.c_void_p(4096)
+    fdummy = ctypes.c_void_p(4096)
+    st = L.jfa_bwd(dummy, dummy, dummy, dummy, fdummy, dummy, dummy, dummy, 2, 2, 64, 10, 10, None, 0, dummy, dummy,
+                   dummy, fdummy, dummy, 1 << 20, None)
+    assert st == 1 and b"dbias needs a bias" in L.jfa_last_error()

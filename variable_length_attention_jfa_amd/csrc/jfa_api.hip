@@ -71,8 +71,9 @@ jfa_status device_info(DeviceInfo** out) {
 
 // Optional per-launch timing: HIP events recorded on the launch stream around
 // each kernel, read back on jfa_timing_collect().
-enum { kKindPlan = 0, kKindFwd = 1, kKindDelta = 2, kKindDkdv = 3, kKindDq = 4, kKindScan = 5, kKindSq = 6, kKindFsq = 7 };
-static_assert(kKindFsq + 1 == JFA_TIMING_KINDS, "timing kinds published in the header");
+enum { kKindPlan = 0, kKindFwd = 1, kKindDelta = 2, kKindDkdv = 3, kKindDq = 4, kKindScan = 5, kKindSq = 6, kKindFsq = 7,
+       kKindDbias = 8 };
+static_assert(kKindDbias + 1 == JFA_TIMING_KINDS, "timing kinds published in the header");
 struct TimingRec {
   int kind;
   hipEvent_t a, b;
@@ -146,11 +147,12 @@ FwdLayout fwd_layout(int B, int H, int64_t tq, int64_t tk, int D) {
 
 // Backward workspace: three list headers (dK/dV, dQ, short-query passes), the
 // row constants [Tq, H] (lse * log2 e, Delta), the three item lists, the
-// short-query group table [B*H] and one [64, D] fp32 partial dQ per
-// short-query item.
+// short-query and dK/dV group tables [B*H], one [64, D] fp32 partial dQ per
+// short-query item, the 257 bias-gradient bins of every dK/dV and
+// short-query item, and their sums per (block of 4 sequences, head).
 struct BwdLayout {
   size_t hdr_kv = 0, hdr_q = sizeof(PlanHeader), hdr_sq = 2 * sizeof(PlanHeader), rowc = 0, items_kv = 0,
-         items_q = 0, items_sq = 0, gfirst = 0, dqp = 0, total = 0;
+         items_q = 0, items_sq = 0, gfirst = 0, gfirst_kv = 0, dqp = 0, dbp_kv = 0, dbp_sq = 0, dbpart = 0, total = 0;
   int64_t cap_kv = 0, cap_q = 0, cap_sq = 0;
 };
 BwdLayout bwd_layout(int B, int H, int64_t tq, int64_t tk, int D) {
@@ -163,8 +165,12 @@ BwdLayout bwd_layout(int B, int H, int64_t tq, int64_t tk, int D) {
   L.items_q = L.items_kv + align_up((size_t)L.cap_kv * 16);
   L.items_sq = L.items_q + align_up((size_t)L.cap_q * 16);
   L.gfirst = L.items_sq + align_up((size_t)L.cap_sq * 16);
-  L.dqp = L.gfirst + align_up((size_t)B * H * 4);
-  L.total = L.dqp + align_up((size_t)L.cap_sq * jfa::kSqQMax * D * 4);
+  L.gfirst_kv = L.gfirst + align_up((size_t)B * H * 4);
+  L.dqp = L.gfirst_kv + align_up((size_t)B * H * 4);
+  L.dbp_kv = L.dqp + align_up((size_t)L.cap_sq * jfa::kSqQMax * D * 4);
+  L.dbp_sq = L.dbp_kv + align_up((size_t)L.cap_kv * JFA_BIAS_LEN * 4);
+  L.dbpart = L.dbp_sq + align_up((size_t)L.cap_sq * JFA_BIAS_LEN * 4);
+  L.total = L.dbpart + align_up((size_t)((B + jfa::kDbSeqBlock - 1) / jfa::kDbSeqBlock) * H * JFA_BIAS_LEN * 4);
   return L;
 }
 
@@ -248,13 +254,15 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
 
 jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const void* out, const float* lse,
                     const void* dout, const int32_t* qo, const int32_t* ko, int B, int H, int D, int64_t tq,
-                    int64_t tk, const float* bias, int causal, void* dq, void* dk, void* dv, void* ws,
+                    int64_t tk, const float* bias, int causal, void* dq, void* dk, void* dv, float* dbias, void* ws,
                     size_t ws_bytes, void* stream) {
   jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, bias, ws);
   if (s != JFA_OK) return s;
   if (f32 && D > 64) return fail(JFA_ERR_UNSUPPORTED, "fp32 tensors support D = 32 or 64");
   if (tq > 0 && (!out || !lse || !dout || !dq)) return fail(JFA_ERR_INVALID_ARGUMENT, "out/lse/dout/dq must not be NULL");
   if (tk > 0 && (!dk || !dv)) return fail(JFA_ERR_INVALID_ARGUMENT, "dk/dv must not be NULL");
+  if (dbias && !bias) return fail(JFA_ERR_INVALID_ARGUMENT, "dbias needs a bias");
+  if (!aligned(dbias, 4)) return fail(JFA_ERR_INVALID_ARGUMENT, "dbias must be 4-byte aligned");
   if (!aligned(out, 16) || !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(lse, 4))
     return fail(JFA_ERR_INVALID_ARGUMENT, "out/dout/dq/dk/dv must be 16-byte aligned");
@@ -263,8 +271,15 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
     return fail(JFA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
   DeviceInfo* dev = nullptr;
   if ((s = device_info(&dev)) != JFA_OK) return s;
-  if (B == 0 || (tq == 0 && tk == 0)) return ok();
   hipStream_t st = (hipStream_t)stream;
+  if (B == 0 || (tq == 0 && tk == 0)) {
+    if (!dbias) return ok();
+    jfa::BwdArgs z{};  // no pairs: the bias gradient is zero (no sequence is read)
+    z.H = H;
+    z.dbias = dbias;
+    const hipError_t e = timed(kKindDbias, st, [&] { return jfa::launch_dbias(z, st); });
+    return e == hipSuccess ? ok() : fail(JFA_ERR_HIP, "bias gradient launch: %s", hipGetErrorString(e));
+  }
   char* w = (char*)ws;
 
   jfa::PlanArgs pa{};
@@ -274,7 +289,7 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.H = H;
   pa.causal = causal ? 1 : 0;
   pa.pass[0] = {(int4*)(w + L.items_kv), (PlanHeader*)(w + L.hdr_kv), (long)L.cap_kv, jfa::dkv_tile_rows(f32, D),
-                jfa::kDkvTN, jfa::kPassKV, jfa::kPlanQueues, jfa::kSqQMax, nullptr};
+                jfa::kDkvTN, jfa::kPassKV, jfa::kPlanQueues, jfa::kSqQMax, (int*)(w + L.gfirst_kv)};
   pa.pass[1] = {(int4*)(w + L.items_q), (PlanHeader*)(w + L.hdr_q), (long)L.cap_q, jfa::kDqTM, jfa::kDqTN,
                 jfa::kPassQ, jfa::kPlanQueues, jfa::kSqQMax, nullptr};
   pa.pass[2] = {(int4*)(w + L.items_sq), (PlanHeader*)(w + L.hdr_sq), (long)L.cap_sq, jfa::kSqQMax, jfa::kSqKC,
@@ -304,6 +319,11 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a.B = B;
   a.gfirst = (int*)(w + L.gfirst);
   a.dqp = (float*)(w + L.dqp);
+  a.gfirst_kv = (int*)(w + L.gfirst_kv);
+  a.dbp_kv = (float*)(w + L.dbp_kv);
+  a.dbp_sq = (float*)(w + L.dbp_sq);
+  a.dbpart = (float*)(w + L.dbpart);
+  a.dbias = dbias;
   jfa::BwdArgs a_kv = a, a_q = a, a_sq = a;
   a_kv.items = (const int4*)(w + L.items_kv);
   a_kv.hdr = (PlanHeader*)(w + L.hdr_kv);
@@ -316,11 +336,16 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   // start of the dQ launch), then the split passes.
   e = timed(kKindDelta, st, [&] { return jfa::launch_delta(f32, D, a_kv, st); });
   if (e == hipSuccess)
-    e = timed(kKindSq, st, [&] { return jfa::launch_sq(f32, D, a_sq, has_bias, (long)L.cap_sq, dev->num_cus, st); });
+    e = timed(kKindSq, st, [&] {
+      return jfa::launch_sq(f32, D, a_sq, has_bias, dbias != nullptr, (long)L.cap_sq, dev->num_cus, st);
+    });
   if (e == hipSuccess)
-    e = timed(kKindDkdv, st, [&] { return jfa::launch_dkdv(f32, D, a_kv, has_bias, (long)L.cap_kv, dev->num_cus, st); });
+    e = timed(kKindDkdv, st, [&] {
+      return jfa::launch_dkdv(f32, D, a_kv, has_bias, dbias != nullptr, (long)L.cap_kv, dev->num_cus, st);
+    });
   if (e == hipSuccess)
     e = timed(kKindDq, st, [&] { return jfa::launch_dq(f32, D, a_q, has_bias, (long)L.cap_q, dev->num_cus, st); });
+  if (e == hipSuccess && dbias) e = timed(kKindDbias, st, [&] { return jfa::launch_dbias(a, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -369,18 +394,18 @@ jfa_status jfa_fwd_f32(const void* q, const void* k, const void* v, const int32_
 
 jfa_status jfa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
                    const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D, int64_t total_q,
-                   int64_t total_kv, const float* bias, int causal, void* dq, void* dk, void* dv, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   int64_t total_kv, const float* bias, int causal, void* dq, void* dk, void* dv, float* dbias,
+                   void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(false, q, k, v, out, lse, dout, q_offsets, kv_offsets, B, H, D, total_q, total_kv, bias, causal,
-                  dq, dk, dv, workspace, workspace_bytes, stream);
+                  dq, dk, dv, dbias, workspace, workspace_bytes, stream);
 }
 
 jfa_status jfa_bwd_f32(const void* q, const void* k, const void* v, const void* out, const float* lse,
                        const void* dout, const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D,
                        int64_t total_q, int64_t total_kv, const float* bias, int causal, void* dq, void* dk, void* dv,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(true, q, k, v, out, lse, dout, q_offsets, kv_offsets, B, H, D, total_q, total_kv, bias, causal, dq,
-                  dk, dv, workspace, workspace_bytes, stream);
+                  dk, dv, dbias, workspace, workspace_bytes, stream);
 }
 
 jfa_status jfa_offsets_from_lengths(const int32_t* lengths, int B, int32_t* offsets, void* stream) {

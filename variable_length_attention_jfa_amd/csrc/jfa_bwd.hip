@@ -29,6 +29,7 @@
 // blocks that straddle it.
 #include "jfa_common.h"
 #include "jfa_kernels.h"
+#include "jfa_dbias.h"
 #include "jfa_short.h"
 
 namespace jfa {
@@ -111,7 +112,7 @@ struct DkvTiles {
 
 // State of one dK/dV work item, identical in every wave of the workgroup.
 struct DkvItem {
-  int b, h, Lq, Lk, kw_base, qb0, nblk;
+  int pos, b, h, Lq, Lk, kw_base, qb0, nblk;  // pos: list position of the item
   const char* qbase;
   const char* dobase;
   const float2* rcbase;
@@ -124,6 +125,7 @@ __device__ __forceinline__ bool dkv_begin(const BwdArgs& a, QueueCursor* qc, Tic
   const int i = next_item(a.hdr, qc, tk);
   if (i < 0) return false;
   const int4 item = a.items[i];
+  it.pos = i;
   it.b = uni(item.x);
   it.h = uni(item.y);
   const int q0 = uni(a.q_off[it.b]), k0 = uni(a.kv_off[it.b]);
@@ -198,7 +200,7 @@ __device__ __forceinline__ bool dkv_active(int qs0, int kw0, int Lk, int causal)
   return kw0 < Lk && (!causal || qs0 + 31 >= kw0);
 }
 
-template <typename T, int D, bool BIAS>
+template <typename T, int D, bool BIAS, bool DBIAS>
 __device__ __forceinline__ void dkv_score_role(const BwdArgs& a, lds_t* lds, QueueCursor* qc) {
   using C = DkvTiles<T, D>;
   constexpr int BMQ = C::BMQ, ES = (int)sizeof(T);
@@ -280,10 +282,11 @@ __device__ __forceinline__ void dkv_score_role(const BwdArgs& a, lds_t* lds, Que
         }
       }
     }
+    if (DBIAS) __syncthreads();  // the gradient waves' bias bins are complete
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool DBIAS>
 __device__ __forceinline__ void dkv_grad_role(const BwdArgs& a, lds_t* lds, QueueCursor* qc) {
   using C = DkvTiles<T, D>;
   constexpr int BMQ = C::BMQ, ES = (int)sizeof(T);
@@ -296,6 +299,11 @@ __device__ __forceinline__ void dkv_grad_role(const BwdArgs& a, lds_t* lds, Queu
   DkvStage<T, D> stg;
   while (dkv_begin<T, D>(a, qc, tk, it)) {
     const int kw0 = it.kw_base + 32 * pair;
+    DbWave db;
+    if (DBIAS) {
+      db = db_wave(lds + C::LDS, pair);
+      db_begin(db, lane);
+    }
     const View vv = seq_view((const char*)a.v + it.krow + (size_t)kw0 * gstride, max(0, min(32, it.Lk - kw0)), gstride, C::ROWB);
     Frag<T> vf[D / 16];
 #pragma unroll
@@ -331,6 +339,11 @@ __device__ __forceinline__ void dkv_grad_role(const BwdArgs& a, lds_t* lds, Queu
         // dS = P (dP - Delta)
 #pragma unroll
         for (int i = 0; i < 16; ++i) dp[i] = p[i] * (dp[i] - rc[2 * res_row(i, g) + 1]);
+        if (DBIAS) {  // keys past the end: K = V = 0 leaves dS = -P Delta there, which is no pair's gradient
+          f32x16 ds = dp;
+          if (kw0 + l32 >= it.Lk) ds = (f32x16){};
+          db_block(db, ds, (it.qb0 + jp) * BMQ - kw0, lane);
+        }
         // dK^T += Q^T dS^T
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -356,20 +369,25 @@ __device__ __forceinline__ void dkv_grad_role(const BwdArgs& a, lds_t* lds, Queu
         }
       }
     }
+    if (DBIAS) {  // the item's bias-gradient bins, gradient waves in order
+      db_finish(db, lane);
+      __syncthreads();
+      db_store(lds + C::LDS, C::PAIRS, a.dbp_kv + (size_t)it.pos * kBiasLen, tid - 64 * C::PAIRS, 64 * C::PAIRS);
+    }
   }
 }
 
 // The two roles run the same item sequence and meet at the same barriers
 // (two per item fetch, one after the prologue, one per block step).
-template <typename T, int D, bool BIAS>
+template <typename T, int D, bool BIAS, bool DBIAS>
 __device__ __forceinline__ void dkv_two_roles(const BwdArgs& a) {
   using C = DkvTiles<T, D>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS + (DBIAS ? C::PAIRS * kDbWaveBytes : 0)];
   __shared__ QueueCursor qcur;
   lds_t* lds = (lds_t*)smem;
   load_queues(a.hdr, &qcur);
-  if ((threadIdx.x >> 6) < C::PAIRS) dkv_score_role<T, D, BIAS>(a, lds, &qcur);
-  else dkv_grad_role<T, D>(a, lds, &qcur);
+  if ((threadIdx.x >> 6) < C::PAIRS) dkv_score_role<T, D, BIAS, DBIAS>(a, lds, &qcur);
+  else dkv_grad_role<T, D, DBIAS>(a, lds, &qcur);
 }
 
 // ---------------------------------------------------------------------------
@@ -394,11 +412,11 @@ struct Dkv1Tiles {
   static_assert(BMQ == kDkv1TM && BNK == kDkvTN, "tile shape published to the planner");
 };
 
-template <typename T, int D, bool BIAS>
+template <typename T, int D, bool BIAS, bool DBIAS>
 __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
   using C = Dkv1Tiles<T, D>;
   constexpr int BNK = C::BNK, BMQ = C::BMQ, ES = (int)sizeof(T);
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS + (DBIAS ? 4 * kDbWaveBytes : 0)];
   __shared__ QueueCursor qcur;
   lds_t* lds = (lds_t*)smem;
   __attribute__((address_space(3))) float* bias_lds = (__attribute__((address_space(3))) float*)(lds + C::BIAS_OFF);
@@ -436,6 +454,11 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
     const int kw0 = key_tile0 + 32 * w;  // first key of this wave
     const bool wave_on = kw0 < Lk;
     const int kj = kw0 + l32;            // this lane's key
+    DbWave db;
+    if (DBIAS) {
+      db = db_wave(lds + C::LDS, w);
+      db_begin(db, lane);
+    }
     Frag<T> kf[D / 16], vf[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -510,6 +533,11 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
           sc[i] = p;
           dp[i] = p * (dp[i] - rc[2 * r + 1]);
         }
+        if (DBIAS) {  // keys past the end: K = V = 0 leaves dS = -P Delta there, which is no pair's gradient
+          f32x16 ds = dp;
+          if (kj >= Lk) ds = (f32x16){};
+          db_block(db, ds, qs0 - kw0, lane);
+        }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const Frag<T> pf = rfrag(sc, c, (T*)0);
@@ -541,6 +569,11 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
         }
       }
     }
+    if (DBIAS) {  // the item's bias-gradient bins, waves in order
+      db_finish(db, lane);
+      __syncthreads();
+      db_store(lds + C::LDS, 4, a.dbp_kv + (size_t)it * kBiasLen, tid, C::THREADS);
+    }
   }
 }
 
@@ -552,10 +585,11 @@ struct DkvShape {
   static constexpr int threads = one_role ? Dkv1Tiles<T, D>::THREADS : 512;
 };
 
-template <typename T, int D, bool BIAS>
+// DBIAS (with BIAS): also the bias-gradient bins of each item.
+template <typename T, int D, bool BIAS, bool DBIAS>
 __global__ __launch_bounds__((DkvShape<T, D>::threads), 2) void jfa_dkdv_kernel(BwdArgs a) {
-  if constexpr (DkvShape<T, D>::one_role) dkv_one_role<T, D, BIAS>(a);
-  else dkv_two_roles<T, D, BIAS>(a);
+  if constexpr (DkvShape<T, D>::one_role) dkv_one_role<T, D, BIAS, DBIAS>(a);
+  else dkv_two_roles<T, D, BIAS, DBIAS>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -722,13 +756,51 @@ static hipError_t launch_delta_t(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T, int D, bool BIAS>
+template <typename T, int D, bool BIAS, bool DBIAS>
 static hipError_t launch_dkdv_t(const BwdArgs& a, long max_items, int num_cus, hipStream_t st) {
   static int occ = 0;
   constexpr int threads = DkvShape<T, D>::threads;
-  const long g = persistent_grid(jfa_dkdv_kernel<T, D, BIAS>, occ, max_items, num_cus, threads);
-  hipLaunchKernelGGL((jfa_dkdv_kernel<T, D, BIAS>), dim3((unsigned)g), dim3(threads), 0, st, a);
+  const long g = persistent_grid(jfa_dkdv_kernel<T, D, BIAS, DBIAS>, occ, max_items, num_cus, threads);
+  hipLaunchKernelGGL((jfa_dkdv_kernel<T, D, BIAS, DBIAS>), dim3((unsigned)g), dim3(threads), 0, st, a);
   return hipGetLastError();
+}
+
+// Bias gradient of each head, in two steps with a fixed order. Step 1: one
+// workgroup per (head, block of kDbSeqBlock consecutive sequences) sums the
+// bins of those sequences' items (sequences in order, each sequence's items
+// in list order: they are contiguous in its list), one thread per bin
+// (thread 0 also takes the last bin). Step 2: one workgroup per head sums
+// the blocks in order.
+__global__ __launch_bounds__(256) void jfa_dbias_part_kernel(BwdArgs a) {
+  const int h = blockIdx.x % a.H, c = blockIdx.x / a.H, tid = threadIdx.x;
+  const int b0 = c * kDbSeqBlock, b1 = min(a.B, b0 + kDbSeqBlock);
+  float acc = 0.f, acc_last = 0.f;
+  for (int b = b0; b < b1; ++b) {
+    const int Lq = a.q_off[b + 1] - a.q_off[b], Lk = a.kv_off[b + 1] - a.kv_off[b];
+    const bool sq = short_query(Lq, Lk);
+    const int first = sq ? a.gfirst[b * a.H + h] : a.gfirst_kv[b * a.H + h];
+    if (first < 0) continue;
+    const int n = sq ? cdiv(Lk, kSqKC) : cdiv(Lk, kDkvTN);
+    const float* src = (sq ? a.dbp_sq : a.dbp_kv) + (size_t)first * kBiasLen;
+#pragma unroll 8
+    for (int t = 0; t < n; ++t) {
+      acc += src[(size_t)t * kBiasLen + tid];
+      if (tid == 0) acc_last += src[(size_t)t * kBiasLen + 256];
+    }
+  }
+  float* out = a.dbpart + ((size_t)c * a.H + h) * kBiasLen;
+  out[tid] = acc;
+  if (tid == 0) out[256] = acc_last;
+}
+
+__global__ __launch_bounds__(256) void jfa_dbias_kernel(BwdArgs a) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int nc = cdiv(a.B, kDbSeqBlock);
+  for (int r = tid; r < kBiasLen; r += 256) {
+    float acc = 0.f;
+    for (int c = 0; c < nc; ++c) acc += a.dbpart[((size_t)c * a.H + h) * kBiasLen + r];
+    a.dbias[(size_t)h * kBiasLen + r] = acc;
+  }
 }
 
 int dkv_tile_rows(bool f32, int D) {
@@ -762,9 +834,18 @@ hipError_t launch_delta(bool f32, int D, const BwdArgs& a, hipStream_t st) {
   JFA_DISPATCH_TD(f32, D, (launch_delta_t<T, DD>(a, st)));
 }
 
-hipError_t launch_dkdv(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
-  if (bias) JFA_DISPATCH_TD(f32, D, (launch_dkdv_t<T, DD, true>(a, max_items, num_cus, st)));
-  JFA_DISPATCH_TD(f32, D, (launch_dkdv_t<T, DD, false>(a, max_items, num_cus, st)));
+hipError_t launch_dkdv(bool f32, int D, const BwdArgs& a, bool bias, bool dbias, long max_items, int num_cus,
+                       hipStream_t st) {
+  if (bias && dbias) JFA_DISPATCH_TD(f32, D, (launch_dkdv_t<T, DD, true, true>(a, max_items, num_cus, st)));
+  if (bias) JFA_DISPATCH_TD(f32, D, (launch_dkdv_t<T, DD, true, false>(a, max_items, num_cus, st)));
+  JFA_DISPATCH_TD(f32, D, (launch_dkdv_t<T, DD, false, false>(a, max_items, num_cus, st)));
+}
+
+hipError_t launch_dbias(const BwdArgs& a, hipStream_t st) {
+  const long nc = (a.B + kDbSeqBlock - 1) / kDbSeqBlock;
+  if (nc > 0) hipLaunchKernelGGL(jfa_dbias_part_kernel, dim3((unsigned)(nc * a.H)), dim3(256), 0, st, a);
+  if (a.H > 0) hipLaunchKernelGGL(jfa_dbias_kernel, dim3((unsigned)a.H), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_dq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {

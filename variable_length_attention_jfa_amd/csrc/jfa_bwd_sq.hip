@@ -35,6 +35,7 @@
 // causal mask, keys after the query get P = 0.
 #include "jfa_common.h"
 #include "jfa_kernels.h"
+#include "jfa_dbias.h"
 
 namespace jfa {
 
@@ -103,11 +104,20 @@ __device__ __forceinline__ void put4(lds_t* tile, int row, int col, float a, flo
   *(__attribute__((address_space(3))) f32x4*)(tile + Tile<float, W>::byte(row, col * 4)) = (f32x4){a, b, c, d};
 }
 
-template <typename T, int D, bool BIAS>
+// One entry of a [key][query] tile, as float.
+__device__ __forceinline__ float tile_at(const lds_t* tile, int row, int col, bf16*) {
+  return (float)*(const __attribute__((address_space(3))) bf16*)(tile + Tile<bf16, kSqQMax>::byte(row, col * 2));
+}
+__device__ __forceinline__ float tile_at(const lds_t* tile, int row, int col, float*) {
+  return *(const __attribute__((address_space(3))) float*)(tile + Tile<float, kSqQMax>::byte(row, col * 4));
+}
+
+// DBIAS (with BIAS): also the bias-gradient bins of each item.
+template <typename T, int D, bool BIAS, bool DBIAS>
 __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
   using C = SqTiles<T, D>;
   constexpr int QM = C::QM, KT = C::KT, KC = C::KC, ES = (int)sizeof(T);
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS + (DBIAS ? 4 * kDbHistBytes : 0)];
   __shared__ QueueCursor qcur;
   lds_t* lds = (lds_t*)smem;
   lds_t* qt = lds + C::QOFF;
@@ -216,12 +226,18 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
 
     const int kh = w & 1, qh = w >> 1;  // key half and query half of this wave
     const int krow_t = 32 * kh + l32;   // this lane's key row in the tile
+    DbWave db;
+    if (DBIAS) {
+      db = db_wave_hist(lds + C::LDS, w);
+      db_begin(db, lane);
+    }
     for (int t = 0; t < nt; ++t) {
       if (t + 1 < nt) {
         tload(a.k, t + 1, kr);
         tload(a.v, t + 1, vr);
       }
       const int kj = key_c0 + t * KT + krow_t;  // this lane's key
+      bool db_near = false;  // this wave's dS quarter straddles the bias radius
       // S, dP of (key half kh, query half qh).
       f32x16 sc = (f32x16){}, dp = (f32x16){};
       if (qh < nqs) {
@@ -243,6 +259,9 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
           sc[i] = p;
           dp[i] = p * (dp[i] - rc[2 * qi + 1]);
         }
+        // bias-gradient bins: blocks beyond the radius here, the others from the dS tile below
+        // (keys past the end already have P = 0)
+        if (DBIAS) db_near = !db_far(db, dp, 32 * qh - (key_c0 + t * KT + 32 * kh));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int q = 32 * qh + 8 * r + 4 * g;
@@ -251,6 +270,14 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
         }
       }
       __syncthreads();
+      if (DBIAS && db_near) {  // diagonal i - j = lane - 31 of this wave's quarter of the dS tile
+        const int d = lane - 31;
+        float v = 0.f;
+        if (lane < 63) {
+          for (int i = max(0, d); i < min(32, 32 + d); ++i) v += tile_at(st, 32 * kh + i - d, 32 * qh + i, (T*)0);
+        }
+        db_diag(db, v, 32 * qh - (key_c0 + t * KT + 32 * kh), lane);
+      }
       // dV^T, dK^T of key half kh, column blocks qh, qh + 2, ...: lane holds
       // rows d = 32db + res_row(i,g) of key kj.
       f32x16 av[C::NDB2], ak[C::NDB2];
@@ -325,18 +352,23 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
     __syncthreads();
     const View pv = seq_view(a.dqp + (size_t)it * QM * D, Lq, D * 4, D * 4);
     rows_out<float, D, QM, C::THREADS>(lds, pv, D * 4, 1.0f, tid);
+    if (DBIAS) {  // the item's bias-gradient bins, waves in order
+      db_finish(db, lane);
+      __syncthreads();
+      db_store(lds + C::LDS, 4, a.dbp_sq + (size_t)it * kBiasLen, tid, C::THREADS, kDbHistBytes, 0);
+    }
   }
 }
 
-template <typename T, int D, bool BIAS>
+template <typename T, int D, bool BIAS, bool DBIAS>
 static hipError_t launch_sq_t(const BwdArgs& a, long max_items, int num_cus, hipStream_t st) {
   static int occ = 0;
   if (occ == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, jfa_sq_kernel<T, D, BIAS>, 256, 0) != hipSuccess || occ < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, jfa_sq_kernel<T, D, BIAS, DBIAS>, 256, 0) != hipSuccess || occ < 1)
       occ = 1;
   }
   const long g = max(1L, min(max_items, (long)num_cus * occ));
-  hipLaunchKernelGGL((jfa_sq_kernel<T, D, BIAS>), dim3((unsigned)g), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((jfa_sq_kernel<T, D, BIAS, DBIAS>), dim3((unsigned)g), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -352,9 +384,11 @@ static hipError_t launch_sq_t(const BwdArgs& a, long max_items, int num_cus, hip
     { using T = bf16; constexpr int DD = 128; return CALL; }                     \
   } while (0)
 
-hipError_t launch_sq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
-  if (bias) JFA_SQ_DISPATCH(f32, D, (launch_sq_t<T, DD, true>(a, max_items, num_cus, st)));
-  JFA_SQ_DISPATCH(f32, D, (launch_sq_t<T, DD, false>(a, max_items, num_cus, st)));
+hipError_t launch_sq(bool f32, int D, const BwdArgs& a, bool bias, bool dbias, long max_items, int num_cus,
+                     hipStream_t st) {
+  if (bias && dbias) JFA_SQ_DISPATCH(f32, D, (launch_sq_t<T, DD, true, true>(a, max_items, num_cus, st)));
+  if (bias) JFA_SQ_DISPATCH(f32, D, (launch_sq_t<T, DD, true, false>(a, max_items, num_cus, st)));
+  JFA_SQ_DISPATCH(f32, D, (launch_sq_t<T, DD, false, false>(a, max_items, num_cus, st)));
 }
 
 }  // namespace jfa

@@ -51,7 +51,18 @@ struct BwdArgs {
   int B;
   int* gfirst;         // short-query pass: [B*H] list position of chunk 0 of each (b, h), -1 if none
   float* dqp;          // short-query pass: per item, a [64, D] fp32 partial dQ
+  // Bias gradient (null dbias: not computed): per item of the dK/dV and
+  // short-query passes, the 257 bins of its pairs; per (b, h), the list
+  // position of the dK/dV pass's first item of the group (-1 if none).
+  float* dbp_kv;
+  float* dbp_sq;
+  int* gfirst_kv;
+  float* dbpart;       // [ceil(B / kDbSeqBlock)][H][257]: sums over blocks of sequences
+  float* dbias;        // [H][257] fp32 output
 };
+
+// Bias gradient: sequences per block of its first summing step.
+constexpr int kDbSeqBlock = 4;
 
 // Pass kinds of the work lists.
 enum PlanKind { kPassQ = 0, kPassKV = 1, kPassSQ = 2 };
@@ -103,9 +114,12 @@ constexpr int kDqTM = 128, kDqTN = 64;
 hipError_t launch_fwd(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
 hipError_t launch_fsq(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
 hipError_t launch_delta(bool f32, int D, const BwdArgs& a, hipStream_t st);
-hipError_t launch_dkdv(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
+hipError_t launch_dkdv(bool f32, int D, const BwdArgs& a, bool bias, bool dbias, long max_items, int num_cus,
+                       hipStream_t st);
 hipError_t launch_dq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
-hipError_t launch_sq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
+hipError_t launch_sq(bool f32, int D, const BwdArgs& a, bool bias, bool dbias, long max_items, int num_cus,
+                     hipStream_t st);
+hipError_t launch_dbias(const BwdArgs& a, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, int npass, hipStream_t st);
 hipError_t launch_scan(const int* lengths, int B, int* offsets, hipStream_t st);
 

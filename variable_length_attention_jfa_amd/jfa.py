@@ -43,9 +43,9 @@ _SIGS = {
     "jfa_fwd": (_int, [_vp, _vp, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _f32p, _int, _vp, _f32p, _vp, _sz, _vp]),
     "jfa_fwd_f32": (_int, [_vp, _vp, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _f32p, _int, _vp, _f32p, _vp, _sz, _vp]),
     "jfa_bwd": (_int, [_vp, _vp, _vp, _vp, _f32p, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _f32p, _int,
-                       _vp, _vp, _vp, _vp, _sz, _vp]),
+                       _vp, _vp, _vp, _f32p, _vp, _sz, _vp]),
     "jfa_bwd_f32": (_int, [_vp, _vp, _vp, _vp, _f32p, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _f32p, _int,
-                           _vp, _vp, _vp, _vp, _sz, _vp]),
+                           _vp, _vp, _vp, _f32p, _vp, _sz, _vp]),
     "jfa_offsets_from_lengths": (_int, [_i32p, _int, _i32p, _vp]),
     "jfa_tile_config": (_int, [_int, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
     "jfa_build_plan": (_int, [_i32p, _i32p, _int, _int, _int, _int, _int, _int, _vp, _sz, _vp]),
@@ -157,8 +157,11 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: torch.
 
 
 def backward(q, k, v, out, lse, dout, q_offsets, kv_offsets, bias=None, causal: bool = False,
-             dq=None, dk=None, dv=None):
+             dq=None, dk=None, dv=None, bias_grad: bool = False):
+    """Gradients (dq, dk, dv); with bias_grad also the fp32 [H, 257] gradient of the bias table."""
     B, H, D, Tq, Tk = _common(q, k, v, q_offsets, kv_offsets, bias)
+    if bias_grad and bias is None:
+        raise ValueError("bias_grad needs a bias")
     _check_tensor("out", out, q.dtype, 3)
     _check_tensor("dout", dout, q.dtype, 3)
     _check_tensor("lse", lse, torch.float32, 2)
@@ -169,10 +172,12 @@ def backward(q, k, v, out, lse, dout, q_offsets, kv_offsets, bias=None, causal: 
     nbytes = L.jfa_bwd_workspace_bytes(B, H, Tq, Tk, D, int(causal))
     ws, wp = _workspace(nbytes, q.device)
     fn = L.jfa_bwd_f32 if q.dtype == torch.float32 else L.jfa_bwd
+    dbias = torch.empty((H, 2 * BIAS_RADIUS + 1), dtype=torch.float32, device=q.device) if bias_grad else None
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(q_offsets), _ptr(kv_offsets), B, H, D,
-            Tq, Tk, _ptr(bias), int(causal), _ptr(dq), _ptr(dk), _ptr(dv), ctypes.c_void_p(wp), nbytes, _stream())
+            Tq, Tk, _ptr(bias), int(causal), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), ctypes.c_void_p(wp), nbytes,
+            _stream())
     _check("jfa_bwd", st)
-    return dq, dk, dv
+    return (dq, dk, dv, dbias) if bias_grad else (dq, dk, dv)
 
 
 def offsets_from_lengths(lengths: torch.Tensor) -> torch.Tensor:
@@ -214,7 +219,7 @@ def build_plan(q_offsets: torch.Tensor, kv_offsets: torch.Tensor, H: int, D: int
     return header, items, ws[off + nbytes - tail:off + nbytes - tail + B * H * 4].view(torch.int32)
 
 
-TIMING_KINDS = ("plan", "forward", "delta", "dkdv", "dq", "scan", "sq", "fsq")
+TIMING_KINDS = ("plan", "forward", "delta", "dkdv", "dq", "scan", "sq", "fsq", "dbias")
 
 
 def timing_enable(enable: bool = True) -> None:
@@ -243,8 +248,9 @@ class JaggedAttention(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, lse, qo, ko, bias = ctx.saved_tensors
-        dq, dk, dv = backward(q, k, v, out, lse, dout.contiguous(), qo, ko, bias, ctx.causal)
-        return dq, dk, dv, None, None, None, None
+        want_db = bias is not None and ctx.needs_input_grad[5]
+        g = backward(q, k, v, out, lse, dout.contiguous(), qo, ko, bias, ctx.causal, bias_grad=want_db)
+        return g[0], g[1], g[2], None, None, (g[3] if want_db else None), None
 
 
 def jagged_attention(q, k, v, q_offsets, kv_offsets, bias=None, causal=False):
