@@ -35,23 +35,35 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanMaxB = 8192;
 
-__device__ __forceinline__ int plan_tiles(int Lq, int Lk, const PlanPass& p) {
-  if (p.kind == kPassSQ) return short_query(Lq, Lk) ? cdiv(Lk, p.TN) : 0;
-  if (Lq <= p.short_q && Lk > kSqKC) return 0;
-  return p.kind == kPassKV ? cdiv(Lk, p.TN) : cdiv(Lq, p.TM);
+// A pass's tile shape; TM and TN are powers of two (checked at launch), so
+// the divisions below are shifts.
+struct PlanGeom {
+  int kind, TM, TN, lgTM, lgTN, short_q;
+};
+
+__device__ __forceinline__ PlanGeom plan_geom(const PlanPass& p) {
+  return {p.kind, p.TM, p.TN, __builtin_ctz((unsigned)p.TM), __builtin_ctz((unsigned)p.TN), p.short_q};
 }
 
-__device__ __forceinline__ int plan_cost(int Lq, int Lk, int t, const PlanPass& p, int causal) {
+__device__ __forceinline__ int cdiv_lg(int a, int lg) { return (a + (1 << lg) - 1) >> lg; }
+
+__device__ __forceinline__ int plan_tiles(int Lq, int Lk, const PlanGeom& p) {
+  if (p.kind == kPassSQ) return short_query(Lq, Lk) ? cdiv_lg(Lk, p.lgTN) : 0;
+  if (Lq <= p.short_q && Lk > kSqKC) return 0;
+  return p.kind == kPassKV ? cdiv_lg(Lk, p.lgTN) : cdiv_lg(Lq, p.lgTM);
+}
+
+__device__ __forceinline__ int plan_cost(int Lq, int Lk, int t, const PlanGeom& p, int causal) {
   if (p.kind == kPassSQ) return max(0, min(p.TN, Lk - t * p.TN));
   if (p.kind == kPassQ) {
-    if (!causal) return cdiv(Lk, p.TN);
-    return cdiv(min(min((t + 1) * p.TM, Lq), Lk), p.TN);
+    if (!causal) return cdiv_lg(Lk, p.lgTN);
+    return cdiv_lg(min(min((t + 1) * p.TM, Lq), Lk), p.lgTN);
   }
-  const int nq = cdiv(Lq, p.TM);
+  const int nq = cdiv_lg(Lq, p.lgTM);
   if (!causal) return nq;
   const int first_key = t * p.TN;
   if (first_key >= Lq) return 0;
-  return nq - first_key / p.TM;
+  return nq - (first_key >> p.lgTM);
 }
 
 // Position of tile t in its group's order (cost descending, then t ascending).
@@ -61,12 +73,12 @@ __device__ __forceinline__ int plan_cost(int Lq, int Lk, int t, const PlanPass& 
 // with cost c are t in [floor((c-1)*TN/TM), t1) with t1 = floor(c*TN/TM) if
 // some tile reaches cost c+1 (min(Lq, Lk) > c*TN), else n. Tile t comes after
 // the n - t1 tiles of larger cost and the t - t0 tiles of equal cost before it.
-__device__ __forceinline__ int plan_pos(int Lq, int Lk, int t, int n, const PlanPass& p, int causal) {
+__device__ __forceinline__ int plan_pos(int Lq, int Lk, int t, int n, const PlanGeom& p, int causal) {
   const int lmin = min(Lq, Lk);
   if (!causal || p.kind != kPassQ || lmin == 0) return t;
   const int c = plan_cost(Lq, Lk, t, p, causal);
-  const int t0 = ((c - 1) * p.TN) / p.TM;
-  const int t1 = lmin > c * p.TN ? min((c * p.TN) / p.TM, n) : n;
+  const int t0 = ((c - 1) * p.TN) >> p.lgTM;
+  const int t1 = lmin > c * p.TN ? min((c * p.TN) >> p.lgTM, n) : n;
   return (n - t1) + (t - t0);
 }
 
@@ -110,6 +122,7 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
   __shared__ int excl[kPlanThreads];
 
   const PlanPass p = a.pass[blockIdx.x];
+  const PlanGeom pg = plan_geom(p);
   const int tid = threadIdx.x;
   const int B = a.B, H = a.H, NQ = p.nq;
   int P = 2;
@@ -120,9 +133,9 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
     unsigned long long k = ~0ull;
     if (b < B) {
       const int Lq = a.q_off[b + 1] - a.q_off[b], Lk = a.kv_off[b + 1] - a.kv_off[b];
-      const int n = plan_tiles(Lq, Lk, p);
+      const int n = plan_tiles(Lq, Lk, pg);
       int gc = 0;
-      for (int t = 0; t < n; ++t) gc += plan_cost(Lq, Lk, t, p, a.causal);
+      for (int t = 0; t < n; ++t) gc += plan_cost(Lq, Lk, t, pg, a.causal);
       lq_s[b] = Lq;
       lk_s[b] = Lk;
       k = ((unsigned long long)(0x7FFFFFFFu - (unsigned)gc) << 32) | (unsigned)b;
@@ -137,12 +150,24 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
     for (int x = tid; x < B * H; x += kPlanThreads) p.gfirst[x] = -1;
   __syncthreads();
 
-  // 2. bitonic sort of the P keys (ascending: cost descending, then b).
-  //    Compare-exchange steps of stride 64 and more go through LDS, one
-  //    barrier each; the steps of smaller stride pair lanes of one wave and
-  //    run in registers with cross-lane shuffles (1024 is a multiple of 64,
-  //    so element i sits in lane i mod 64 of its wave).
-  for (int k = 2; k <= P; k <<= 1) {
+  // 2. sort the keys (ascending: cost descending, then b); only the first B
+  //    positions are read afterwards.
+  if (P <= kPlanThreads) {
+    // Up to one key per thread: each key's rank is the count of smaller keys
+    // (the B real keys are distinct: b is part of the key; the padding keys
+    // are the largest), read by every thread from LDS in the same order.
+    const unsigned long long mine = tid < P ? key[tid] : 0ull;
+    int rank = 0;
+    if (tid < P)
+      for (int i = 0; i < P; ++i) rank += key[i] < mine;
+    __syncthreads();
+    if (tid < P) key[rank] = mine;
+    __syncthreads();
+  } else for (int k = 2; k <= P; k <<= 1) {
+    // Bitonic sort: compare-exchange steps of stride 64 and more go through
+    // LDS, one barrier each; the steps of smaller stride pair lanes of one
+    // wave and run in registers with cross-lane shuffles (1024 is a multiple
+    // of 64, so element i sits in lane i mod 64 of its wave).
     int j = k >> 1;
     for (; j >= 64; j >>= 1) {
       for (int i = tid; i < P; i += kPlanThreads) {
@@ -177,7 +202,7 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
   const int G = B * H;
   for (int g = tid; g < G; g += kPlanThreads) {
     const int b = (int)(key[g / H] & 0xFFFFFFFFu);
-    atomicAdd(&qtotal[snake(g, NQ)], plan_tiles(lq_s[b], lk_s[b], p));
+    atomicAdd(&qtotal[snake(g, NQ)], plan_tiles(lq_s[b], lk_s[b], pg));
   }
   __syncthreads();
   if (tid == 0) {
@@ -212,7 +237,7 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
     int b = 0, n = 0;
     if (g < G) {
       b = (int)(key[g / H] & 0xFFFFFFFFu);
-      n = plan_tiles(lq_s[b], lk_s[b], p);
+      n = plan_tiles(lq_s[b], lk_s[b], pg);
     }
     int tot;
     const int ex = block_exclusive_scan(n, &tot, wsum);
@@ -227,8 +252,8 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
     if (n > 0) {
       const int h = g % H, Lq = lq_s[b], Lk = lk_s[b];
       for (int t = 0; t < n; ++t) {
-        const long at = gbase + plan_pos(Lq, Lk, t, n, p, a.causal);
-        if (at >= 0 && at < p.capacity) p.items[at] = make_int4(b, h, t, plan_cost(Lq, Lk, t, p, a.causal));
+        const long at = gbase + plan_pos(Lq, Lk, t, n, pg, a.causal);
+        if (at >= 0 && at < p.capacity) p.items[at] = make_int4(b, h, t, plan_cost(Lq, Lk, t, pg, a.causal));
       }
     }
     __syncthreads();  // qcarry of the next chunk
@@ -251,6 +276,10 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_scan_kernel(const int* lengt
 }
 
 hipError_t launch_plan(const PlanArgs& a, int npass, hipStream_t st) {
+  for (int i = 0; i < npass; ++i) {
+    const PlanPass& p = a.pass[i];
+    if (p.TM <= 0 || p.TN <= 0 || (p.TM & (p.TM - 1)) || (p.TN & (p.TN - 1))) return hipErrorInvalidValue;
+  }
   hipLaunchKernelGGL(jfa_plan_kernel, dim3(npass), dim3(kPlanThreads), 0, st, a);
   return hipGetLastError();
 }
