@@ -27,6 +27,8 @@
 // K = V = 0 for pad keys), so every product they enter is zero: no jagged
 // mask is needed here. The causal mask zeroes P above the diagonal on the
 // blocks that straddle it.
+#include <type_traits>
+
 #include "jfa_common.h"
 #include "jfa_kernels.h"
 #include "jfa_dbias.h"
@@ -240,16 +242,21 @@ __device__ __forceinline__ void dkv_score_role(const BwdArgs& a, lds_t* lds, Que
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) mma(sc, lfrag<D>(qt, l32, 16 * kk + 8 * g, (T*)0), kf[kk]);
         // P = exp2(S * scale * log2(e) - lse2 (+ bias)), zero above the diagonal
+        // (the element test only on blocks that straddle it)
+        auto softmax = [&](auto mask_c) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = res_row(i, g);
-          const int qi = qs0 + r;
-          float x = sc[i] * a.scale2 - rc[2 * r];
-          if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
-          float p = __builtin_amdgcn_exp2f(x);
-          if (masked && kj > qi) p = 0.f;
-          sc[i] = p;
-        }
+          for (int i = 0; i < 16; ++i) {
+            const int r = res_row(i, g);
+            const int qi = qs0 + r;
+            float x = sc[i] * a.scale2 - rc[2 * r];
+            if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+            float p = __builtin_amdgcn_exp2f(x);
+            if (decltype(mask_c)::value && kj > qi) p = 0.f;
+            sc[i] = p;
+          }
+        };
+        if (masked) softmax(std::true_type{});
+        else softmax(std::false_type{});
         // handed to the gradient wave of the pair in fp32, lane order
         lds_t* pb = lds + C::PBUF + ((jb & 1) * C::PAIRS + pair) * C::PBLK;
 #pragma unroll
@@ -521,18 +528,23 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
           mma(sc, lfrag<D>(qt, 32 * sb + l32, 16 * kk + 8 * g, (T*)0), kf[kk]);
           mma(dp, lfrag<D>(dot, 32 * sb + l32, 16 * kk + 8 * g, (T*)0), vf[kk]);
         }
-        // sc[i] = S[query 32sb + res_row(i,g)][key kj]
+        // sc[i] = S[query 32sb + res_row(i,g)][key kj]; the element test for
+        // the causal mask only on blocks that straddle the diagonal
+        auto softmax = [&](auto mask_c) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = 32 * sb + res_row(i, g);
-          const int qi = qb * BMQ + r;
-          float x = sc[i] * a.scale2 - rc[2 * r];
-          if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
-          float p = __builtin_amdgcn_exp2f(x);
-          if (masked && kj > qi) p = 0.f;
-          sc[i] = p;
-          dp[i] = p * (dp[i] - rc[2 * r + 1]);
-        }
+          for (int i = 0; i < 16; ++i) {
+            const int r = 32 * sb + res_row(i, g);
+            const int qi = qb * BMQ + r;
+            float x = sc[i] * a.scale2 - rc[2 * r];
+            if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+            float p = __builtin_amdgcn_exp2f(x);
+            if (decltype(mask_c)::value && kj > qi) p = 0.f;
+            sc[i] = p;
+            dp[i] = p * (dp[i] - rc[2 * r + 1]);
+          }
+        };
+        if (masked) softmax(std::true_type{});
+        else softmax(std::false_type{});
         if (DBIAS) {  // keys past the end: K = V = 0 leaves dS = -P Delta there, which is no pair's gradient
           f32x16 ds = dp;
           if (kj >= Lk) ds = (f32x16){};
@@ -702,17 +714,39 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
             mma(dp[kb], lfrag<D>(vt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), df[kk]);
           }
         }
+        // Element tests only on blocks at the causal diagonal or the sequence end
+        // (at D = 128 a second copy of the loop costs more than the tests save).
+        auto softmax = [&](auto edge_c) {
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
+          for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kj = key0 + 32 * kb + res_row(i, g);
-            float x = sc[kb][i] * a.scale2 - lse2;
-            if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
-            float p = __builtin_amdgcn_exp2f(x);
-            if ((masked && kj > qi) || (padded && kj >= Lk)) p = 0.f;
-            dp[kb][i] = p * (dp[kb][i] - dlt);
+            for (int i = 0; i < 16; ++i) {
+              const int kj = key0 + 32 * kb + res_row(i, g);
+              float x = sc[kb][i] * a.scale2 - lse2;
+              if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+              float p = __builtin_amdgcn_exp2f(x);
+              if (decltype(edge_c)::value && ((masked && kj > qi) || (padded && kj >= Lk))) p = 0.f;
+              dp[kb][i] = p * (dp[kb][i] - dlt);
+            }
           }
+        };
+        if constexpr (D > 64) {
+#pragma unroll
+          for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int kj = key0 + 32 * kb + res_row(i, g);
+              float x = sc[kb][i] * a.scale2 - lse2;
+              if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+              float p = __builtin_amdgcn_exp2f(x);
+              if ((masked && kj > qi) || (padded && kj >= Lk)) p = 0.f;
+              dp[kb][i] = p * (dp[kb][i] - dlt);
+            }
+          }
+        } else if (masked || padded) {
+          softmax(std::true_type{});
+        } else {
+          softmax(std::false_type{});
         }
 #pragma unroll
         for (int kc = 0; kc < BN / 16; ++kc) {

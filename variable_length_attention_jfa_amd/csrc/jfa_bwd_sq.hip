@@ -33,6 +33,8 @@
 // share a CU.
 // Rows past a sequence's end load as zeros; keys past the end and, with the
 // causal mask, keys after the query get P = 0.
+#include <type_traits>
+
 #include "jfa_common.h"
 #include "jfa_kernels.h"
 #include "jfa_dbias.h"
@@ -249,16 +251,21 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
       }
       __syncthreads();  // V is consumed: P and dS take its place
       if (qh < nqs) {
+        // element tests only with the causal mask or on the tile holding the sequence end
+        auto softmax = [&](auto edge_c) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = 32 * qh + res_row(i, g);
-          float x = sc[i] * a.scale2 - rc[2 * qi];
-          if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
-          float p = __builtin_amdgcn_exp2f(x);
-          if (kj >= Lk || (a.causal && kj > qi)) p = 0.f;
-          sc[i] = p;
-          dp[i] = p * (dp[i] - rc[2 * qi + 1]);
-        }
+          for (int i = 0; i < 16; ++i) {
+            const int qi = 32 * qh + res_row(i, g);
+            float x = sc[i] * a.scale2 - rc[2 * qi];
+            if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+            float p = __builtin_amdgcn_exp2f(x);
+            if (decltype(edge_c)::value && (kj >= Lk || (a.causal && kj > qi))) p = 0.f;
+            sc[i] = p;
+            dp[i] = p * (dp[i] - rc[2 * qi + 1]);
+          }
+        };
+        if (a.causal || key_c0 + t * KT + KT > Lk) softmax(std::true_type{});
+        else softmax(std::false_type{});
         // bias-gradient bins: blocks beyond the radius here, the others from the dS tile below
         // (keys past the end already have P = 0)
         if (DBIAS) db_near = !db_far(db, dp, 32 * qh - (key_c0 + t * KT + 32 * kh));
