@@ -4,8 +4,8 @@
 
 One step is the whole hot path over one synthetic batch already resident in
 HBM: jfa_fwd (work-list build + forward kernel) then jfa_bwd (three work
-lists, delta, dK/dV pass, dQ pass, and for sequences of at most 64 queries the
-short-query backward and its dQ sum). Throughput counts valid (query, key) pairs only:
+lists and Delta in one launch, dK/dV pass, dQ pass, and for sequences of at
+most 64 queries the short-query backward and its dQ sum). Throughput counts valid (query, key) pairs only:
 forward 4*D*H*pairs flops, backward 10*D*H*pairs flops (pairs = sum Lq*Lk, or
 sum_i min(i+1, Lk) with the causal mask).
 
@@ -140,10 +140,10 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None,
     bwd_flops = 10.0 * wl.D * wl.H * pairs
     ms_step = (t1 - t0) * 1e3 / steps
     per = {k_: (ms / max(n, 1), n) for k_, (ms, n) in kt.items()}
-    # the plan kind covers one launch in forward and one in backward per step
-    plan_ms = kt["plan"][0] / max(kt["plan"][1], 1)
-    fwd_ms = (kt["forward"][0] + kt["fsq"][0]) / steps + plan_ms
-    bwd_ms = (kt["delta"][0] + kt["dkdv"][0] + kt["dq"][0] + kt["sq"][0] + kt["dbias"][0]) / steps + plan_ms
+    # forward: work lists, short-query chunks, forward; backward: work lists
+    # with Delta, short-query chunks, dK/dV, dQ (and the bias-gradient sums)
+    fwd_ms = (kt["plan"][0] + kt["forward"][0] + kt["fsq"][0]) / steps
+    bwd_ms = (kt["bwd_prep"][0] + kt["dkdv"][0] + kt["dq"][0] + kt["sq"][0] + kt["dbias"][0]) / steps
     res = {
         "workload": wl.name, "B": wl.B, "H": wl.H, "D": wl.D, "dtype": wl.dtype, "causal": wl.causal,
         "bias": wl.bias, "seed": wl.seed if seed is None else seed, "total_q": batch.total_q,

@@ -174,7 +174,8 @@ size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv,
 /* Launch timing, for benchmarks and profiling. While enabled, every kernel
  * launch of this library is bracketed by two HIP events recorded on its
  * stream (a few microseconds of host overhead per launch). */
-#define JFA_TIMING_KINDS 9 /* 0 plan, 1 forward (with the short-query chunk merge), 2 delta, 3 dK/dV, \
+#define JFA_TIMING_KINDS 9 /* 0 work lists (forward, jfa_build_plan), 1 forward (with the short-query \
+                             chunk merge), 2 backward work lists with Delta (one launch), 3 dK/dV, \
                              4 dQ (with the short-query dQ sum), 5 offsets scan, 6 short-query backward chunks, \
                              7 short-query forward chunks, 8 bias-gradient sum */
 jfa_status jfa_timing_enable(int enable);

@@ -71,7 +71,7 @@ jfa_status device_info(DeviceInfo** out) {
 
 // Optional per-launch timing: HIP events recorded on the launch stream around
 // each kernel, read back on jfa_timing_collect().
-enum { kKindPlan = 0, kKindFwd = 1, kKindDelta = 2, kKindDkdv = 3, kKindDq = 4, kKindScan = 5, kKindSq = 6, kKindFsq = 7,
+enum { kKindPlan = 0, kKindFwd = 1, kKindBwdPrep = 2, kKindDkdv = 3, kKindDq = 4, kKindScan = 5, kKindSq = 6, kKindFsq = 7,
        kKindDbias = 8 };
 static_assert(kKindDbias + 1 == JFA_TIMING_KINDS, "timing kinds published in the header");
 struct TimingRec {
@@ -294,9 +294,6 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
                 jfa::kPassQ, jfa::kPlanQueues, jfa::kSqQMax, nullptr};
   pa.pass[2] = {(int4*)(w + L.items_sq), (PlanHeader*)(w + L.hdr_sq), (long)L.cap_sq, jfa::kSqQMax, jfa::kSqKC,
                 jfa::kPassSQ, jfa::kPlanQueues, -1, (int*)(w + L.gfirst)};
-  hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 3, st); });
-  if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
-
   jfa::BwdArgs a{};
   a.q = q;
   a.k = k;
@@ -332,9 +329,10 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a_sq.items = (const int4*)(w + L.items_sq);
   a_sq.hdr = (PlanHeader*)(w + L.hdr_sq);
   const bool has_bias = bias != nullptr;
-  // Delta, then the short-query chunks (their partial dQ is summed at the
-  // start of the dQ launch), then the split passes.
-  e = timed(kKindDelta, st, [&] { return jfa::launch_delta(f32, D, a_kv, st); });
+  // The work lists and Delta (one launch), then the short-query chunks (their
+  // partial dQ is summed at the start of the dQ launch), then the split
+  // passes.
+  hipError_t e = timed(kKindBwdPrep, st, [&] { return jfa::launch_bwd_prep(pa, 3, f32, D, a_kv, st); });
   if (e == hipSuccess)
     e = timed(kKindSq, st, [&] {
       return jfa::launch_sq(f32, D, a_sq, has_bias, dbias != nullptr, (long)L.cap_sq, dev->num_cus, st);

@@ -8,9 +8,10 @@
 //   dS = P * (dP - Delta), dQ = dS K / sqrt(D), dK = dS^T Q / sqrt(D),
 // with P recomputed from the forward's log-sum-exp: P = exp(S - lse).
 //
-//  * jfa_delta_kernel : Delta per (token, head), one pass over O and dO, stored
-//                       as a pair with lse * log2(e) so that one 8-byte load
-//                       gives a row's two softmax constants.
+//  * Delta per (token, head), one pass over O and dO, stored as a pair with
+//    lse * log2(e) so that one 8-byte load gives a row's two softmax
+//    constants (jfa_delta.h; it runs in the launch that builds the work
+//    lists).
 //  * jfa_dkdv_kernel  : item = (b, h, 128-key tile), 8 waves in 4 pairs; each
 //                       pair owns 32 keys. The score wave of a pair keeps K
 //                       of its keys in VGPRs, turns each 32-row query block
@@ -37,54 +38,6 @@
 namespace jfa {
 
 
-
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-struct DeltaShape {
-  static constexpr int ROWB = D * (int)sizeof(T), TPR = ROWB / 16;  // threads per row
-  static constexpr int RPP = 256 / TPR;                               // rows per pass of the block
-  static constexpr int PASSES = 4;                                    // rows per thread, loads in flight together
-  static constexpr int RPB = RPP * PASSES;                            // rows per block
-};
-
-// rows = (token, head) pairs in memory order: reads and writes both stream.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void jfa_delta_kernel(BwdArgs a) {
-  using S = DeltaShape<T, D>;
-  const long rows = a.tq * a.H;
-  const int part = threadIdx.x % S::TPR;
-  const long r0 = (long)blockIdx.x * S::RPB + threadIdx.x / S::TPR;
-  i32x4 o[S::PASSES], d[S::PASSES];
-  float l[S::PASSES];
-#pragma unroll
-  for (int k = 0; k < S::PASSES; ++k) {
-    const long row = r0 + k * S::RPP;
-    o[k] = d[k] = (i32x4){};
-    l[k] = 0.f;
-    if (row < rows) {
-      o[k] = *(const i32x4*)((const char*)a.out + row * S::ROWB + part * 16);
-      d[k] = *(const i32x4*)((const char*)a.dout + row * S::ROWB + part * 16);
-      if (part == 0) l[k] = a.lse[row];
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < S::PASSES; ++k) {
-    float acc = 0.f;
-    if (sizeof(T) == 2) {
-      const bf16x8 o8 = __builtin_bit_cast(bf16x8, o[k]), d8 = __builtin_bit_cast(bf16x8, d[k]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc += (float)o8[e] * (float)d8[e];
-    } else {
-      const f32x4 o4 = __builtin_bit_cast(f32x4, o[k]), d4 = __builtin_bit_cast(f32x4, d[k]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc += o4[e] * d4[e];
-    }
-#pragma unroll
-    for (int s = S::TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
-    const long row = r0 + k * S::RPP;
-    if (row < rows && part == 0) a.rowc[row] = make_float2(l[k] * kLog2e, acc);
-  }
-}
 
 // ---------------------------------------------------------------------------
 template <typename T, int D>
@@ -783,13 +736,6 @@ static long persistent_grid(K kern, int& occ, long max_items, int num_cus, int t
   return max(1L, min(max_items, (long)num_cus * occ));
 }
 
-template <typename T, int D>
-static hipError_t launch_delta_t(const BwdArgs& a, hipStream_t st) {
-  const long nblk = (a.tq * a.H + DeltaShape<T, D>::RPB - 1) / DeltaShape<T, D>::RPB;
-  if (nblk > 0) hipLaunchKernelGGL((jfa_delta_kernel<T, D>), dim3((unsigned)nblk), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
 template <typename T, int D, bool BIAS, bool DBIAS>
 static hipError_t launch_dkdv_t(const BwdArgs& a, long max_items, int num_cus, hipStream_t st) {
   static int occ = 0;
@@ -864,9 +810,6 @@ static hipError_t launch_dq_t(const BwdArgs& a, long max_items, int num_cus, hip
     { using T = bf16; constexpr int DD = 128; return CALL; }                   \
   } while (0)
 
-hipError_t launch_delta(bool f32, int D, const BwdArgs& a, hipStream_t st) {
-  JFA_DISPATCH_TD(f32, D, (launch_delta_t<T, DD>(a, st)));
-}
 
 hipError_t launch_dkdv(bool f32, int D, const BwdArgs& a, bool bias, bool dbias, long max_items, int num_cus,
                        hipStream_t st) {

@@ -113,7 +113,6 @@ constexpr int kDqTM = 128, kDqTN = 64;
 // chunks of each sequence and the dQ launch sums its partial dQ.
 hipError_t launch_fwd(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
 hipError_t launch_fsq(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
-hipError_t launch_delta(bool f32, int D, const BwdArgs& a, hipStream_t st);
 hipError_t launch_dkdv(bool f32, int D, const BwdArgs& a, bool bias, bool dbias, long max_items, int num_cus,
                        hipStream_t st);
 hipError_t launch_dq(bool f32, int D, const BwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
@@ -121,6 +120,8 @@ hipError_t launch_sq(bool f32, int D, const BwdArgs& a, bool bias, bool dbias, l
                      hipStream_t st);
 hipError_t launch_dbias(const BwdArgs& a, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, int npass, hipStream_t st);
+// The backward's lists (passes of p) and Delta of every row (a.rowc), one launch.
+hipError_t launch_bwd_prep(const PlanArgs& p, int npass, bool f32, int D, const BwdArgs& a, hipStream_t st);
 hipError_t launch_scan(const int* lengths, int B, int* offsets, hipStream_t st);
 
 }  // namespace jfa

@@ -28,6 +28,7 @@
 // the list is the same on every run.
 #include "jfa_common.h"
 #include "jfa_kernels.h"
+#include "jfa_delta.h"
 
 namespace jfa {
 
@@ -114,19 +115,30 @@ __device__ int block_exclusive_scan(int v, int* total, int* wsum) {
   return before + x - v;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
-  __shared__ unsigned long long key[kPlanMaxB];  // (inverted group cost, b), sorted ascending
-  __shared__ int lq_s[kPlanMaxB], lk_s[kPlanMaxB];  // sequence lengths
+// LDS of one pass: the static scan and queue arrays below, and
+// plan_dyn_bytes(B) of dynamic LDS for the per-sequence arrays (sort keys,
+// then query and key lengths), sized by the power of two P >= B.
+__host__ __device__ inline int plan_pow2(int B) {
+  int P = 2;
+  while (P < B) P <<= 1;
+  return P;
+}
+inline size_t plan_dyn_bytes(int B) { return (size_t)plan_pow2(B) * (8 + 4 + 4); }
+
+// Builds the list of pass `pi` of `a`; one 1024-thread workgroup.
+__device__ __forceinline__ void plan_pass(const PlanArgs& a, int pi, char* dyn) {
+  const int P = plan_pow2(a.B);
+  unsigned long long* key = (unsigned long long*)dyn;  // (inverted group cost, b), sorted ascending
+  int* lq_s = (int*)(key + P);                          // sequence lengths
+  int* lk_s = lq_s + P;
   __shared__ int wsum[2 * kPlanWaves];
   __shared__ int qtotal[kMaxQueues], qstart[kMaxQueues], qcarry[kMaxQueues];
   __shared__ int excl[kPlanThreads];
 
-  const PlanPass p = a.pass[blockIdx.x];
+  const PlanPass p = a.pass[pi];
   const PlanGeom pg = plan_geom(p);
   const int tid = threadIdx.x;
   const int B = a.B, H = a.H, NQ = p.nq;
-  int P = 2;
-  while (P < B) P <<= 1;
 
   // 1. tiles and group cost of every sequence
   for (int b = tid; b < P; b += kPlanThreads) {
@@ -260,6 +272,21 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kPlanThreads) void jfa_plan_kernel(PlanArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char plan_dyn[];
+  plan_pass(a, blockIdx.x, plan_dyn);
+}
+
+// The backward's work lists and its row constants in one launch: workgroups
+// 0 .. npass-1 build the lists, the others stream O and dO into Delta, so
+// that the list building hides under the streaming.
+template <typename T, int D>
+__global__ __launch_bounds__(kPlanThreads) void jfa_bwd_prep_kernel(PlanArgs p, BwdArgs a, int npass) {
+  extern __shared__ __attribute__((aligned(16))) char plan_dyn[];
+  if ((int)blockIdx.x < npass) plan_pass(p, blockIdx.x, plan_dyn);
+  else delta_rows<T, D, kPlanThreads>(a, (long)blockIdx.x - npass, threadIdx.x);
+}
+
 // lengths [B] -> offsets [B+1] (exclusive prefix sums), one workgroup.
 __global__ __launch_bounds__(kPlanThreads) void jfa_scan_kernel(const int* lengths, int B, int* offsets) {
   __shared__ int wsum[2 * kPlanWaves];
@@ -275,13 +302,52 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_scan_kernel(const int* lengt
   if (threadIdx.x == 0) offsets[B] = carry;
 }
 
-hipError_t launch_plan(const PlanArgs& a, int npass, hipStream_t st) {
+static bool plan_tiles_ok(const PlanArgs& a, int npass) {
   for (int i = 0; i < npass; ++i) {
     const PlanPass& p = a.pass[i];
-    if (p.TM <= 0 || p.TN <= 0 || (p.TM & (p.TM - 1)) || (p.TN & (p.TN - 1))) return hipErrorInvalidValue;
+    if (p.TM <= 0 || p.TN <= 0 || (p.TM & (p.TM - 1)) || (p.TN & (p.TN - 1))) return false;
   }
-  hipLaunchKernelGGL(jfa_plan_kernel, dim3(npass), dim3(kPlanThreads), 0, st, a);
+  return a.B >= 0 && a.B <= kPlanMaxB;
+}
+
+// Dynamic LDS above 64 KB: the kernel's limit is raised once, to the largest
+// size a list can need.
+template <typename K>
+static hipError_t allow_plan_lds(K kern) {
+  static const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  (int)plan_dyn_bytes(kPlanMaxB));
+  return e;
+}
+
+hipError_t launch_plan(const PlanArgs& a, int npass, hipStream_t st) {
+  if (!plan_tiles_ok(a, npass)) return hipErrorInvalidValue;
+  hipError_t e = plan_dyn_bytes(a.B) > 65536 ? allow_plan_lds(jfa_plan_kernel) : hipSuccess;
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(jfa_plan_kernel, dim3(npass), dim3(kPlanThreads), plan_dyn_bytes(a.B), st, a);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_prep_t(const PlanArgs& p, int npass, const BwdArgs& a, hipStream_t st) {
+  hipError_t e = plan_dyn_bytes(p.B) > 65536 ? allow_plan_lds(jfa_bwd_prep_kernel<T, D>) : hipSuccess;
+  if (e != hipSuccess) return e;
+  const long rows = a.tq * a.H;
+  const long nblk = (rows + DeltaShape<T, D, kPlanThreads>::RPB - 1) / DeltaShape<T, D, kPlanThreads>::RPB;
+  hipLaunchKernelGGL((jfa_bwd_prep_kernel<T, D>), dim3((unsigned)(npass + nblk)), dim3(kPlanThreads),
+                     plan_dyn_bytes(p.B), st, p, a, npass);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const PlanArgs& p, int npass, bool f32, int D, const BwdArgs& a, hipStream_t st) {
+  if (!plan_tiles_ok(p, npass)) return hipErrorInvalidValue;
+  if (f32) {
+    if (D == 32) return launch_bwd_prep_t<float, 32>(p, npass, a, st);
+    if (D == 64) return launch_bwd_prep_t<float, 64>(p, npass, a, st);
+    return hipErrorInvalidValue;  // fp32 with D = 128 is rejected on the host
+  }
+  if (D == 32) return launch_bwd_prep_t<bf16, 32>(p, npass, a, st);
+  if (D == 64) return launch_bwd_prep_t<bf16, 64>(p, npass, a, st);
+  return launch_bwd_prep_t<bf16, 128>(p, npass, a, st);
 }
 
 hipError_t launch_scan(const int* lengths, int B, int* offsets, hipStream_t st) {

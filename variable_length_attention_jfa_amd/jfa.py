@@ -219,7 +219,7 @@ def build_plan(q_offsets: torch.Tensor, kv_offsets: torch.Tensor, H: int, D: int
     return header, items, ws[off + nbytes - tail:off + nbytes - tail + B * H * 4].view(torch.int32)
 
 
-TIMING_KINDS = ("plan", "forward", "delta", "dkdv", "dq", "scan", "sq", "fsq", "dbias")
+TIMING_KINDS = ("plan", "forward", "bwd_prep", "dkdv", "dq", "scan", "sq", "fsq", "dbias")
 
 
 def timing_enable(enable: bool = True) -> None:
