@@ -35,6 +35,13 @@
  * and no device-to-host reads. Concurrent calls must use distinct
  * workspaces.
  *
+ * max_kv_len (jfa_fwd, jfa_bwd and their fp32 twins): an upper bound on every
+ * sequence's key count when the caller knows one, else 0 (a negative value
+ * is an invalid argument). With a bound of at most 1024 no sequence can take
+ * the short-query path described below, whose launches are then skipped and
+ * every sequence takes the query-tile and key-tile passes. Those are exact
+ * for any lengths, so a bound that is wrong costs speed, never correctness.
+ *
  * Errors: every call returns a jfa_status. Invalid arguments are detected on
  * the host before anything is launched (nothing is written then);
  * jfa_last_error() gives a thread-local description of the last failure.
@@ -98,7 +105,7 @@ size_t jfa_bwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, 
  * deterministic (asymmetric query/key lengths, section "Definition"). */
 jfa_status jfa_fwd(const void* q, const void* k, const void* v, const int32_t* q_offsets,
                    const int32_t* kv_offsets, int B, int H, int D, int64_t total_q, int64_t total_kv,
-                   const float* bias, int causal, void* out, float* lse, void* workspace,
+                   int max_kv_len, const float* bias, int causal, void* out, float* lse, void* workspace,
                    size_t workspace_bytes, void* stream);
 
 /* Backward pass (bf16). Takes the forward's out and lse and the upstream
@@ -120,19 +127,21 @@ jfa_status jfa_fwd(const void* q, const void* k, const void* v, const int32_t* q
  * so it is bit-identical run to run. */
 jfa_status jfa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
                    const void* dout, const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H,
-                   int D, int64_t total_q, int64_t total_kv, const float* bias, int causal, void* dq,
-                   void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes, void* stream);
+                   int D, int64_t total_q, int64_t total_kv, int max_kv_len, const float* bias, int causal,
+                   void* dq, void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /* fp32 twins: identical parameters, every tensor of element type fp32;
  * D must be 32 or 64 (JFA_ERR_UNSUPPORTED for 128). */
 jfa_status jfa_fwd_f32(const void* q, const void* k, const void* v, const int32_t* q_offsets,
                        const int32_t* kv_offsets, int B, int H, int D, int64_t total_q, int64_t total_kv,
-                       const float* bias, int causal, void* out, float* lse, void* workspace,
+                       int max_kv_len, const float* bias, int causal, void* out, float* lse, void* workspace,
                        size_t workspace_bytes, void* stream);
 jfa_status jfa_bwd_f32(const void* q, const void* k, const void* v, const void* out, const float* lse,
                        const void* dout, const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H,
-                       int D, int64_t total_q, int64_t total_kv, const float* bias, int causal, void* dq,
-                       void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes, void* stream);
+                       int D, int64_t total_q, int64_t total_kv, int max_kv_len, const float* bias, int causal,
+                       void* dq, void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /* offsets[0] = 0, offsets[b+1] = offsets[b] + lengths[b] for b < B (device
  * int32 arrays, lengths [B], offsets [B+1]); the prefix-sum addressing of
@@ -186,6 +195,11 @@ jfa_status jfa_timing_collect(double* total_ms, int64_t* launches, int n_kinds);
 
 const char* jfa_status_string(jfa_status status);
 const char* jfa_last_error(void);
+
+/* Version of the argument lists above; a binding compares it with the one it
+ * was written for before calling anything else. */
+#define JFA_ABI_VERSION 2
+int jfa_abi_version(void);
 
 #ifdef __cplusplus
 }

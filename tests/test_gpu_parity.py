@@ -17,22 +17,24 @@ from variable_length_attention_jfa_amd import jfa
 pytestmark = pytest.mark.gpu
 
 
-def _run(batch, with_bwd=True):
+def _run(batch, with_bwd=True, max_kv_len=0):
     d = to_device(batch)
-    out, lse = jfa.forward(d["q"], d["k"], d["v"], d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal)
+    out, lse = jfa.forward(d["q"], d["k"], d["v"], d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal,
+                           max_kv_len=max_kv_len)
     grads = None
     if with_bwd:
         grads = jfa.backward(d["q"], d["k"], d["v"], out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], d["bias"],
-                             batch.wl.causal)
+                             batch.wl.causal, max_kv_len=max_kv_len)
     torch.cuda.synchronize()
     return out, lse, grads
 
 
-def _check(batch, with_bwd=True, label=""):
+def _check(batch, with_bwd=True, label="", max_kv_len=0):
     print(f"[case] {label} B={len(batch.q_lengths)} H={batch.wl.H} D={batch.wl.D} dtype={batch.wl.dtype} "
-          f"causal={batch.wl.causal} bias={batch.wl.bias} Tq={batch.total_q} Tk={batch.total_kv}", flush=True)
+          f"causal={batch.wl.causal} bias={batch.wl.bias} Tq={batch.total_q} Tk={batch.total_kv} "
+          f"max_kv_len={max_kv_len}", flush=True)
     tol = tol_for(batch)
-    out, lse, grads = _run(batch, with_bwd)
+    out, lse, grads = _run(batch, with_bwd, max_kv_len)
     e_o, e_l, o_ref, _ = compare_forward(batch, out, lse)
     raw = raw_forward_error(batch, out, o_ref)
     print(f"   fwd max|dO| beyond output rounding={e_o:.3e} (raw {raw:.3e}) max|dlse|={e_l:.3e}", flush=True)
@@ -102,6 +104,32 @@ def test_short_query_passes(dtype, D, causal, bias):
     kl = [2500, 70, 1024, 1025, 300, 0, 131, 3000, 4097, 1024]
     wl = gen.Workload("sq", len(ql), 2, D, dtype, causal, bias, gen.LengthDist("fixed", 1, 1), seed=61)
     _check(gen.make_batch(wl, q_lengths=ql, kv_lengths=kl), label=f"short-query {dtype} D={D} causal={causal} bias={bias}")
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("bf16", 128), ("f32", 32)])
+@pytest.mark.parametrize("causal,bias", [(False, False), (True, True)])
+def test_key_bound_broken_by_batch(dtype, D, causal, bias):
+    """A key-count bound of at most 1024 that the batch breaks (keys up to
+    4097) only switches the short-query passes off: every sequence then takes
+    the query-tile and key-tile passes, which still match the oracle."""
+    ql = [64, 65, 1, 33, 0, 17, 40, 0, 5, 64]
+    kl = [2500, 70, 1024, 1025, 300, 0, 131, 3000, 4097, 1024]
+    wl = gen.Workload("kb", len(ql), 2, D, dtype, causal, bias, gen.LengthDist("fixed", 1, 1), seed=62)
+    _check(gen.make_batch(wl, q_lengths=ql, kv_lengths=kl), label=f"broken key bound {dtype} D={D}", max_kv_len=1)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_key_bound_kept(cfg):
+    """A true bound of at most 1024 keys: no short-query sequence exists, so
+    the results are bit-identical to a call without the bound."""
+    batch = gen.make_batch(SMALL[cfg])
+    bound = int(batch.kv_lengths.max())
+    assert bound <= 1024
+    _check(batch, label=f"small cfg{cfg} with its key bound", max_kv_len=bound)
+    a, b = _run(batch), _run(batch, max_kv_len=bound)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+    for x, y in zip(a[2], b[2]):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
 def test_single_head_d128_long_causal():
@@ -211,7 +239,7 @@ def test_invalid_arguments_raise():
     L = jfa.lib()
     # D not supported
     st = L.jfa_fwd(jfa._ptr(d["q"]), jfa._ptr(d["k"]), jfa._ptr(d["v"]), jfa._ptr(d["q_offsets"]),
-                   jfa._ptr(d["kv_offsets"]), 6, 8, 48, batch.total_q, batch.total_kv, None, 0, jfa._ptr(d["q"]),
+                   jfa._ptr(d["kv_offsets"]), 6, 8, 48, batch.total_q, batch.total_kv, 0, None, 0, jfa._ptr(d["q"]),
                    jfa._ptr(d["q"]), None, 0, None)
     assert st == 1
     # workspace too small
@@ -220,18 +248,18 @@ def test_invalid_arguments_raise():
     lse = torch.empty(batch.total_q, 8, dtype=torch.float32, device="cuda")
     need = L.jfa_fwd_workspace_bytes(6, 8, batch.total_q, batch.total_kv, 64, 0)
     st = L.jfa_fwd(jfa._ptr(d["q"]), jfa._ptr(d["k"]), jfa._ptr(d["v"]), jfa._ptr(d["q_offsets"]),
-                   jfa._ptr(d["kv_offsets"]), 6, 8, 64, batch.total_q, batch.total_kv, None, 0, jfa._ptr(out),
+                   jfa._ptr(d["kv_offsets"]), 6, 8, 64, batch.total_q, batch.total_kv, 0, None, 0, jfa._ptr(out),
                    jfa._ptr(lse), jfa._ptr(ws), need - 16, None)
     assert st == 2
     assert b"workspace" in L.jfa_last_error()
     # misaligned q
     st = L.jfa_fwd(ctypes_offset(d["q"], 2), jfa._ptr(d["k"]), jfa._ptr(d["v"]), jfa._ptr(d["q_offsets"]),
-                   jfa._ptr(d["kv_offsets"]), 6, 8, 64, batch.total_q, batch.total_kv, None, 0, jfa._ptr(out),
+                   jfa._ptr(d["kv_offsets"]), 6, 8, 64, batch.total_q, batch.total_kv, 0, None, 0, jfa._ptr(out),
                    jfa._ptr(lse), jfa._ptr(ws), 4096, None)
     assert st == 1
     # B = 0 is a no-op
-    st = L.jfa_fwd(None, None, None, jfa._ptr(d["q_offsets"]), jfa._ptr(d["kv_offsets"]), 0, 8, 64, 0, 0, None, 0,
-                   None, None, jfa._ptr(ws), 4096, None)
+    st = L.jfa_fwd(None, None, None, jfa._ptr(d["q_offsets"]), jfa._ptr(d["kv_offsets"]), 0, 8, 64, 0, 0, 0, None,
+                   0, None, None, jfa._ptr(ws), 4096, None)
     assert st == 0
 
 
@@ -259,17 +287,18 @@ def test_masking_study_variants(mode, cfg):
         jfa.LIB_PATH = saved
 
 
-def _check_dbias(batch, label):
+def _check_dbias(batch, label, max_kv_len=0):
     print(f"[case] dbias {label} B={len(batch.q_lengths)} H={batch.wl.H} D={batch.wl.D} dtype={batch.wl.dtype} "
-          f"causal={batch.wl.causal} Tq={batch.total_q} Tk={batch.total_kv}", flush=True)
+          f"causal={batch.wl.causal} Tq={batch.total_q} Tk={batch.total_kv} max_kv_len={max_kv_len}", flush=True)
     d = to_device(batch)
     args = (d["q"], d["k"], d["v"])
-    out, lse = jfa.forward(*args, d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal)
-    g0 = jfa.backward(*args, out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal)
+    out, lse = jfa.forward(*args, d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal, max_kv_len=max_kv_len)
+    g0 = jfa.backward(*args, out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal,
+                      max_kv_len=max_kv_len)
     g1 = jfa.backward(*args, out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal,
-                      bias_grad=True)
+                      bias_grad=True, max_kv_len=max_kv_len)
     g2 = jfa.backward(*args, out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], d["bias"], batch.wl.causal,
-                      bias_grad=True)
+                      bias_grad=True, max_kv_len=max_kv_len)
     torch.cuda.synchronize()
     ref = oracle.bias_grad(batch.q, batch.k, batch.v, batch.dout, batch.q_offsets, batch.kv_offsets, batch.bias,
                            batch.wl.causal)
@@ -293,6 +322,17 @@ def test_bias_gradient(dtype, D, causal):
     kl = [300, 2100, 500, 40, 1500, 1, 650, 1025]
     wl = gen.Workload("db", len(ql), 2, D, dtype, causal, True, gen.LengthDist("fixed", 1, 1), seed=71)
     _check_dbias(gen.make_batch(wl, q_lengths=ql, kv_lengths=kl, with_dout=True), f"{dtype} D={D} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bias_gradient_key_bound_broken(causal):
+    """The bias gradient with the short-query passes switched off by a bound
+    the batch breaks: every sequence's bins come from the dK/dV pass."""
+    ql = [300, 40, 0, 70, 5, 1, 600, 64]
+    kl = [300, 2100, 500, 40, 1500, 1, 650, 1025]
+    wl = gen.Workload("dbk", len(ql), 2, 64, "bf16", causal, True, gen.LengthDist("fixed", 1, 1), seed=73)
+    _check_dbias(gen.make_batch(wl, q_lengths=ql, kv_lengths=kl, with_dout=True), f"broken key bound causal={causal}",
+                 max_kv_len=1024)
 
 
 def test_bias_gradient_workload4_small():

@@ -30,6 +30,13 @@ def test_binding_covers_the_header():
     assert set(jfa.declared_functions()) == set(jfa._SIGS)
 
 
+def test_abi_version_matches_header(L):
+    import re
+    with open(jfa.HEADER_PATH) as fh:
+        ver = int(re.search(r"#define JFA_ABI_VERSION (\d+)", fh.read()).group(1))
+    assert L.jfa_abi_version() == ver == jfa.ABI_VERSION
+
+
 def test_host_only_queries(L):
     assert L.jfa_fwd_workspace_bytes(4, 2, 153, 153, 32, 0) > 0
     assert L.jfa_fwd_workspace_bytes(4, 2, 153, 153, 48, 0) == 0
@@ -52,22 +59,25 @@ def test_host_only_queries(L):
 
 def test_invalid_arguments_rejected_on_host(L):
     # bad sizes are rejected before any device call
-    st = L.jfa_fwd(None, None, None, None, None, -1, 1, 64, 0, 0, None, 0, None, None, None, 0, None)
+    st = L.jfa_fwd(None, None, None, None, None, -1, 1, 64, 0, 0, 0, None, 0, None, None, None, 0, None)
     assert st == 1
     assert b"invalid sizes" in L.jfa_last_error()
-    st = L.jfa_bwd(None, None, None, None, None, None, None, None, 4, 0, 64, 0, 0, None, 0, None, None, None, None, None,
-                   0, None)
+    st = L.jfa_bwd(None, None, None, None, None, None, None, None, 4, 0, 64, 0, 0, 0, None, 0, None, None, None, None,
+                   None, 0, None)
     assert st == 1
-    st = L.jfa_fwd(None, None, None, None, None, 2, 2, 64, 0, 0, None, 0, None, None, None, 0, None)
+    st = L.jfa_fwd(None, None, None, None, None, 2, 2, 64, 0, 0, 0, None, 0, None, None, None, 0, None)
     assert st == 1 and b"offsets" in L.jfa_last_error()
     dummy = ctypes.c_void_p(4096)
-    st = L.jfa_fwd(dummy, dummy, dummy, dummy, dummy, 2, 2, 64, 10, 10, None, 0, dummy, dummy, None, 0, None)
+    st = L.jfa_fwd(dummy, dummy, dummy, dummy, dummy, 2, 2, 64, 10, 10, 0, None, 0, dummy, dummy, None, 0, None)
     assert st == 2
+    # a negative key-count bound is an invalid argument
+    st = L.jfa_fwd(dummy, dummy, dummy, dummy, dummy, 2, 2, 64, 10, 10, -1, None, 0, dummy, dummy, dummy, 1 << 20, None)
+    assert st == 1 and b"max_kv_len" in L.jfa_last_error()
 
 
 def test_bias_gradient_needs_bias(L):
     dummy = ctypes.c_void_p(4096)
     fdummy = ctypes.c_void_p(4096)
-    st = L.jfa_bwd(dummy, dummy, dummy, dummy, fdummy, dummy, dummy, dummy, 2, 2, 64, 10, 10, None, 0, dummy, dummy,
+    st = L.jfa_bwd(dummy, dummy, dummy, dummy, fdummy, dummy, dummy, dummy, 2, 2, 64, 10, 10, 0, None, 0, dummy, dummy,
                    dummy, fdummy, dummy, 1 << 20, None)
     assert st == 1 and b"dbias needs a bias" in L.jfa_last_error()

@@ -176,8 +176,15 @@ BwdLayout bwd_layout(int B, int H, int64_t tq, int64_t tk, int D) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The short-query passes run unless the caller's bound on every sequence's key
+// count rules them out (no sequence can have more than kSqKC keys). Without
+// them every sequence takes the query-tile and key-tile passes, which are
+// exact for any lengths, so a wrong bound costs speed, never correctness.
+bool short_pass_on(int max_kv_len) { return !(max_kv_len > 0 && max_kv_len <= jfa::kSqKC); }
+
 jfa_status check_common(const void* q, const void* k, const void* v, const int32_t* qo, const int32_t* ko, int B,
-                        int H, int D, int64_t tq, int64_t tk, const float* bias, const void* ws) {
+                        int H, int D, int64_t tq, int64_t tk, int max_kv_len, const float* bias, const void* ws) {
+  if (max_kv_len < 0) return fail(JFA_ERR_INVALID_ARGUMENT, "max_kv_len must be >= 0 (0: unknown)");
   if (!valid_sizes(B, H, tq, tk, D))
     return fail(JFA_ERR_INVALID_ARGUMENT, "invalid sizes: B=%d (0..%d), H=%d (1..%d), D=%d (32/64/128), total_q=%lld, total_kv=%lld",
                 B, JFA_MAX_BATCH, H, JFA_MAX_HEADS, D, (long long)tq, (long long)tk);
@@ -193,9 +200,9 @@ jfa_status check_common(const void* q, const void* k, const void* v, const int32
 }
 
 jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const int32_t* qo, const int32_t* ko,
-                    int B, int H, int D, int64_t tq, int64_t tk, const float* bias, int causal, void* out,
-                    float* lse, void* ws, size_t ws_bytes, void* stream) {
-  jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, bias, ws);
+                    int B, int H, int D, int64_t tq, int64_t tk, int max_kv_len, const float* bias, int causal,
+                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, max_kv_len, bias, ws);
   if (s != JFA_OK) return s;
   if (f32 && D > 64) return fail(JFA_ERR_UNSUPPORTED, "fp32 tensors support D = 32 or 64");
   if ((tq > 0 && (!out || !lse))) return fail(JFA_ERR_INVALID_ARGUMENT, "out/lse must not be NULL");
@@ -215,11 +222,12 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.B = B;
   pa.H = H;
   pa.causal = causal ? 1 : 0;
+  const bool short_on = short_pass_on(max_kv_len);
   pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::fwd_tile_rows(f32, D), jfa::kFwdTN,
-                jfa::kPassQ, jfa::kPlanQueues, jfa::kSqQMax, nullptr};
+                jfa::kPassQ, jfa::kPlanQueues, short_on ? jfa::kSqQMax : -1, nullptr};
   pa.pass[1] = {(int4*)(w + L.items_sq), (PlanHeader*)(w + L.hdr_sq), (long)L.cap_sq, jfa::kSqQMax, jfa::kSqKC,
                 jfa::kPassSQ, jfa::kPlanQueues, -1, (int*)(w + L.gfirst)};
-  hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, 2, st); });
+  hipError_t e = timed(kKindPlan, st, [&] { return jfa::launch_plan(pa, short_on ? 2 : 1, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
 
   jfa::FwdArgs a{};
@@ -237,7 +245,7 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a.causal = causal ? 1 : 0;
   a.scale2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
   a.B = B;
-  a.gfirst = (int*)(w + L.gfirst);
+  a.gfirst = short_on ? (int*)(w + L.gfirst) : nullptr;
   a.op = (float*)(w + L.op);
   a.lsep = (float*)(w + L.lsep);
   jfa::FwdArgs a_sq = a;
@@ -245,7 +253,8 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a_sq.hdr = (PlanHeader*)(w + L.hdr_sq);
   const bool has_bias = bias != nullptr;
   // Short-query chunks first: the query-tile launch then combines them.
-  e = timed(kKindFsq, st, [&] { return jfa::launch_fsq(f32, D, a_sq, has_bias, (long)L.cap_sq, dev->num_cus, st); });
+  if (short_on)
+    e = timed(kKindFsq, st, [&] { return jfa::launch_fsq(f32, D, a_sq, has_bias, (long)L.cap_sq, dev->num_cus, st); });
   if (e == hipSuccess)
     e = timed(kKindFwd, st, [&] { return jfa::launch_fwd(f32, D, a, has_bias, (long)L.cap, dev->num_cus, st); });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
@@ -254,9 +263,9 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
 
 jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const void* out, const float* lse,
                     const void* dout, const int32_t* qo, const int32_t* ko, int B, int H, int D, int64_t tq,
-                    int64_t tk, const float* bias, int causal, void* dq, void* dk, void* dv, float* dbias, void* ws,
-                    size_t ws_bytes, void* stream) {
-  jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, bias, ws);
+                    int64_t tk, int max_kv_len, const float* bias, int causal, void* dq, void* dk, void* dv,
+                    float* dbias, void* ws, size_t ws_bytes, void* stream) {
+  jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, max_kv_len, bias, ws);
   if (s != JFA_OK) return s;
   if (f32 && D > 64) return fail(JFA_ERR_UNSUPPORTED, "fp32 tensors support D = 32 or 64");
   if (tq > 0 && (!out || !lse || !dout || !dq)) return fail(JFA_ERR_INVALID_ARGUMENT, "out/lse/dout/dq must not be NULL");
@@ -288,10 +297,12 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.B = B;
   pa.H = H;
   pa.causal = causal ? 1 : 0;
+  const bool short_on = short_pass_on(max_kv_len);
+  const int short_q = short_on ? jfa::kSqQMax : -1;
   pa.pass[0] = {(int4*)(w + L.items_kv), (PlanHeader*)(w + L.hdr_kv), (long)L.cap_kv, jfa::dkv_tile_rows(f32, D),
-                jfa::kDkvTN, jfa::kPassKV, jfa::kPlanQueues, jfa::kSqQMax, (int*)(w + L.gfirst_kv)};
+                jfa::kDkvTN, jfa::kPassKV, jfa::kPlanQueues, short_q, (int*)(w + L.gfirst_kv)};
   pa.pass[1] = {(int4*)(w + L.items_q), (PlanHeader*)(w + L.hdr_q), (long)L.cap_q, jfa::kDqTM, jfa::kDqTN,
-                jfa::kPassQ, jfa::kPlanQueues, jfa::kSqQMax, nullptr};
+                jfa::kPassQ, jfa::kPlanQueues, short_q, nullptr};
   pa.pass[2] = {(int4*)(w + L.items_sq), (PlanHeader*)(w + L.hdr_sq), (long)L.cap_sq, jfa::kSqQMax, jfa::kSqKC,
                 jfa::kPassSQ, jfa::kPlanQueues, -1, (int*)(w + L.gfirst)};
   jfa::BwdArgs a{};
@@ -314,7 +325,7 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a.scale2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
   a.tq = (long)tq;
   a.B = B;
-  a.gfirst = (int*)(w + L.gfirst);
+  a.gfirst = short_on ? (int*)(w + L.gfirst) : nullptr;
   a.dqp = (float*)(w + L.dqp);
   a.gfirst_kv = (int*)(w + L.gfirst_kv);
   a.dbp_kv = (float*)(w + L.dbp_kv);
@@ -332,8 +343,8 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   // The work lists and Delta (one launch), then the short-query chunks (their
   // partial dQ is summed at the start of the dQ launch), then the split
   // passes.
-  hipError_t e = timed(kKindBwdPrep, st, [&] { return jfa::launch_bwd_prep(pa, 3, f32, D, a_kv, st); });
-  if (e == hipSuccess)
+  hipError_t e = timed(kKindBwdPrep, st, [&] { return jfa::launch_bwd_prep(pa, short_on ? 3 : 2, f32, D, a_kv, st); });
+  if (e == hipSuccess && short_on)
     e = timed(kKindSq, st, [&] {
       return jfa::launch_sq(f32, D, a_sq, has_bias, dbias != nullptr, (long)L.cap_sq, dev->num_cus, st);
     });
@@ -376,34 +387,34 @@ size_t jfa_bwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, 
 }
 
 jfa_status jfa_fwd(const void* q, const void* k, const void* v, const int32_t* q_offsets, const int32_t* kv_offsets,
-                   int B, int H, int D, int64_t total_q, int64_t total_kv, const float* bias, int causal, void* out,
-                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  return fwd_impl(false, q, k, v, q_offsets, kv_offsets, B, H, D, total_q, total_kv, bias, causal, out, lse,
-                  workspace, workspace_bytes, stream);
+                   int B, int H, int D, int64_t total_q, int64_t total_kv, int max_kv_len, const float* bias,
+                   int causal, void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(false, q, k, v, q_offsets, kv_offsets, B, H, D, total_q, total_kv, max_kv_len, bias, causal, out,
+                  lse, workspace, workspace_bytes, stream);
 }
 
 jfa_status jfa_fwd_f32(const void* q, const void* k, const void* v, const int32_t* q_offsets,
                        const int32_t* kv_offsets, int B, int H, int D, int64_t total_q, int64_t total_kv,
-                       const float* bias, int causal, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                       void* stream) {
-  return fwd_impl(true, q, k, v, q_offsets, kv_offsets, B, H, D, total_q, total_kv, bias, causal, out, lse,
-                  workspace, workspace_bytes, stream);
+                       int max_kv_len, const float* bias, int causal, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return fwd_impl(true, q, k, v, q_offsets, kv_offsets, B, H, D, total_q, total_kv, max_kv_len, bias, causal, out,
+                  lse, workspace, workspace_bytes, stream);
 }
 
 jfa_status jfa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
                    const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D, int64_t total_q,
-                   int64_t total_kv, const float* bias, int causal, void* dq, void* dk, void* dv, float* dbias,
-                   void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(false, q, k, v, out, lse, dout, q_offsets, kv_offsets, B, H, D, total_q, total_kv, bias, causal,
-                  dq, dk, dv, dbias, workspace, workspace_bytes, stream);
+                   int64_t total_kv, int max_kv_len, const float* bias, int causal, void* dq, void* dk, void* dv,
+                   float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(false, q, k, v, out, lse, dout, q_offsets, kv_offsets, B, H, D, total_q, total_kv, max_kv_len, bias,
+                  causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
 }
 
 jfa_status jfa_bwd_f32(const void* q, const void* k, const void* v, const void* out, const float* lse,
                        const void* dout, const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D,
-                       int64_t total_q, int64_t total_kv, const float* bias, int causal, void* dq, void* dk, void* dv,
-                       float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(true, q, k, v, out, lse, dout, q_offsets, kv_offsets, B, H, D, total_q, total_kv, bias, causal, dq,
-                  dk, dv, dbias, workspace, workspace_bytes, stream);
+                       int64_t total_q, int64_t total_kv, int max_kv_len, const float* bias, int causal, void* dq,
+                       void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(true, q, k, v, out, lse, dout, q_offsets, kv_offsets, B, H, D, total_q, total_kv, max_kv_len, bias,
+                  causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
 }
 
 jfa_status jfa_offsets_from_lengths(const int32_t* lengths, int B, int32_t* offsets, void* stream) {
@@ -521,5 +532,7 @@ const char* jfa_status_string(jfa_status status) {
 }
 
 const char* jfa_last_error(void) { return g_last_error.c_str(); }
+
+int jfa_abi_version(void) { return JFA_ABI_VERSION; }
 
 }  // extern "C"

@@ -757,7 +757,7 @@ __global__ __launch_bounds__(256) void jfa_dbias_part_kernel(BwdArgs a) {
   float acc = 0.f, acc_last = 0.f;
   for (int b = b0; b < b1; ++b) {
     const int Lq = a.q_off[b + 1] - a.q_off[b], Lk = a.kv_off[b + 1] - a.kv_off[b];
-    const bool sq = short_query(Lq, Lk);
+    const bool sq = a.gfirst != nullptr && short_query(Lq, Lk);  // null: no short-query pass in this call
     const int first = sq ? a.gfirst[b * a.H + h] : a.gfirst_kv[b * a.H + h];
     if (first < 0) continue;
     const int n = sq ? cdiv(Lk, kSqKC) : cdiv(Lk, kDkvTN);

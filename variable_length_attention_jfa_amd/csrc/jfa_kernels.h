@@ -22,7 +22,7 @@ struct FwdArgs {
   int causal;
   float scale2;        // softmax scale * log2(e)
   int B;
-  int* gfirst;         // short-query pass: [B*H] list position of chunk 0 of each (b, h), -1 if none
+  int* gfirst;         // short-query pass: [B*H] list position of chunk 0 of each (b, h), -1 if none; null: no such pass
   float* op;           // short-query pass: per item, [64, D] fp32 rows normalised over the chunk's keys
   float* lsep;         // short-query pass: per item, [64] log2 of each row's sum over the chunk's keys
 };
@@ -49,7 +49,7 @@ struct BwdArgs {
   float scale2;        // scale * log2(e)
   long tq;             // query tokens (rows of rowc per head)
   int B;
-  int* gfirst;         // short-query pass: [B*H] list position of chunk 0 of each (b, h), -1 if none
+  int* gfirst;         // short-query pass: [B*H] list position of chunk 0 of each (b, h), -1 if none; null: no such pass
   float* dqp;          // short-query pass: per item, a [64, D] fp32 partial dQ
   // Bias gradient (null dbias: not computed): per item of the dK/dV and
   // short-query passes, the 257 bins of its pairs; per (b, h), the list

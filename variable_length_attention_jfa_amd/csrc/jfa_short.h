@@ -17,10 +17,12 @@ constexpr int kShortGroupsOff = (kMergeNB + 2) * kSqQMax * 4;
 constexpr int kShortLds = kShortGroupsOff + 257 * 4;
 
 // Runs f(gi) for every (b, h) group gi with a short-query chunk list
-// (gfirst[gi] >= 0); group gi belongs to workgroup gi % gridDim.x. Every
-// thread of the workgroup calls f with the same gi.
+// (gfirst[gi] >= 0; gfirst null: the call has no short-query pass); group gi
+// belongs to workgroup gi % gridDim.x. Every thread of the workgroup calls f
+// with the same gi.
 template <typename F>
 __device__ __forceinline__ void for_short_groups(const int* gfirst, int ngroups, lds_t* lds, F&& f) {
+  if (gfirst == nullptr) return;  // no short-query pass in this call
   int* list = (int*)(lds + kShortGroupsOff);
   int* count = list + 256;
   const int per = ((int)gridDim.x - 1 + ngroups - (int)blockIdx.x) / (int)gridDim.x;  // groups of this workgroup

@@ -5,8 +5,8 @@ provides device memory and the current HIP stream; nothing here computes
 attention, and there is no fallback: if the library is not built or the device
 is not an MI355X, calls raise.
 
-    out, lse = forward(q, k, v, q_offsets, kv_offsets, bias=None, causal=False)
-    dq, dk, dv = backward(q, k, v, out, lse, dout, q_offsets, kv_offsets, bias, causal)
+    out, lse = forward(q, k, v, q_offsets, kv_offsets, bias=None, causal=False, max_kv_len=0)
+    dq, dk, dv = backward(q, k, v, out, lse, dout, q_offsets, kv_offsets, bias, causal, max_kv_len=0)
 
 Tensors: q/out/dout [Tq, H, D], k/v [Tk, H, D] (bf16 or fp32, contiguous, on
 the GPU); offsets int32 [B+1] on the GPU; bias fp32 [H, 257] or None; lse fp32
@@ -28,6 +28,7 @@ KERNEL_FWD, KERNEL_BWD_DKDV, KERNEL_BWD_DQ, KERNEL_BWD_SQ, KERNEL_FWD_SQ = 0, 1,
 SQ_KERNELS = (KERNEL_BWD_SQ, KERNEL_FWD_SQ)  # short-query chunk lists (one list, two passes)
 DTYPE_BF16, DTYPE_F32 = 0, 1
 BIAS_RADIUS = 128
+ABI_VERSION = 2  # JFA_ABI_VERSION of include/jfa.h
 WORKSPACE_ALIGN = 256
 PLAN_HEADER_BYTES = 2048
 PLAN_QUEUES = 8
@@ -38,13 +39,16 @@ _vp, _i32p, _f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
 _int, _i64, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 
 _SIGS = {
+    "jfa_abi_version": (_int, []),
     "jfa_fwd_workspace_bytes": (_sz, [_int, _int, _i64, _i64, _int, _int]),
     "jfa_bwd_workspace_bytes": (_sz, [_int, _int, _i64, _i64, _int, _int]),
-    "jfa_fwd": (_int, [_vp, _vp, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _f32p, _int, _vp, _f32p, _vp, _sz, _vp]),
-    "jfa_fwd_f32": (_int, [_vp, _vp, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _f32p, _int, _vp, _f32p, _vp, _sz, _vp]),
-    "jfa_bwd": (_int, [_vp, _vp, _vp, _vp, _f32p, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _f32p, _int,
+    "jfa_fwd": (_int, [_vp, _vp, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _int, _f32p, _int, _vp, _f32p, _vp, _sz,
+                       _vp]),
+    "jfa_fwd_f32": (_int, [_vp, _vp, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _int, _f32p, _int, _vp, _f32p, _vp,
+                           _sz, _vp]),
+    "jfa_bwd": (_int, [_vp, _vp, _vp, _vp, _f32p, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _int, _f32p, _int,
                        _vp, _vp, _vp, _f32p, _vp, _sz, _vp]),
-    "jfa_bwd_f32": (_int, [_vp, _vp, _vp, _vp, _f32p, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _f32p, _int,
+    "jfa_bwd_f32": (_int, [_vp, _vp, _vp, _vp, _f32p, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _int, _f32p, _int,
                            _vp, _vp, _vp, _f32p, _vp, _sz, _vp]),
     "jfa_offsets_from_lengths": (_int, [_i32p, _int, _i32p, _vp]),
     "jfa_tile_config": (_int, [_int, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
@@ -70,6 +74,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m variable_length_attention_jfa_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
+        # argument lists must match the ones below: a library built from
+        # older sources would read the arguments wrongly
+        ver = getattr(L, "jfa_abi_version", None)
+        if ver is None or ver() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} was built for another ABI version (rebuild it)")
         for name, (res, args) in _SIGS.items():
             f = getattr(L, name)
             f.restype = res
@@ -138,7 +147,9 @@ def _common(q, k, v, q_offsets, kv_offsets, bias):
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: torch.Tensor, kv_offsets: torch.Tensor,
             bias: Optional[torch.Tensor] = None, causal: bool = False, out: Optional[torch.Tensor] = None,
-            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+            lse: Optional[torch.Tensor] = None, max_kv_len: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """max_kv_len: an upper bound on every sequence's key count if known on the host, else 0 (a bound of at
+    most 1024 skips the short-query launches; a wrong bound costs speed only)."""
     B, H, D, Tq, Tk = _common(q, k, v, q_offsets, kv_offsets, bias)
     if out is None:
         out = torch.empty_like(q)
@@ -150,15 +161,16 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: torch.
     nbytes = L.jfa_fwd_workspace_bytes(B, H, Tq, Tk, D, int(causal))
     ws, wp = _workspace(nbytes, q.device)
     fn = L.jfa_fwd_f32 if q.dtype == torch.float32 else L.jfa_fwd
-    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets), B, H, D, Tq, Tk, _ptr(bias), int(causal),
-            _ptr(out), _ptr(lse), ctypes.c_void_p(wp), nbytes, _stream())
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets), B, H, D, Tq, Tk, int(max_kv_len), _ptr(bias),
+            int(causal), _ptr(out), _ptr(lse), ctypes.c_void_p(wp), nbytes, _stream())
     _check("jfa_fwd", st)
     return out, lse
 
 
 def backward(q, k, v, out, lse, dout, q_offsets, kv_offsets, bias=None, causal: bool = False,
-             dq=None, dk=None, dv=None, bias_grad: bool = False):
-    """Gradients (dq, dk, dv); with bias_grad also the fp32 [H, 257] gradient of the bias table."""
+             dq=None, dk=None, dv=None, bias_grad: bool = False, max_kv_len: int = 0):
+    """Gradients (dq, dk, dv); with bias_grad also the fp32 [H, 257] gradient of the bias table.
+    max_kv_len: as for forward."""
     B, H, D, Tq, Tk = _common(q, k, v, q_offsets, kv_offsets, bias)
     if bias_grad and bias is None:
         raise ValueError("bias_grad needs a bias")
@@ -174,8 +186,8 @@ def backward(q, k, v, out, lse, dout, q_offsets, kv_offsets, bias=None, causal: 
     fn = L.jfa_bwd_f32 if q.dtype == torch.float32 else L.jfa_bwd
     dbias = torch.empty((H, 2 * BIAS_RADIUS + 1), dtype=torch.float32, device=q.device) if bias_grad else None
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(q_offsets), _ptr(kv_offsets), B, H, D,
-            Tq, Tk, _ptr(bias), int(causal), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), ctypes.c_void_p(wp), nbytes,
-            _stream())
+            Tq, Tk, int(max_kv_len), _ptr(bias), int(causal), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias),
+            ctypes.c_void_p(wp), nbytes, _stream())
     _check("jfa_bwd", st)
     return (dq, dk, dv, dbias) if bias_grad else (dq, dk, dv)
 
@@ -239,19 +251,21 @@ class JaggedAttention(torch.autograd.Function):
     """autograd wrapper: O = jagged attention(q, k, v); gradients via jfa_bwd."""
 
     @staticmethod
-    def forward(ctx, q, k, v, q_offsets, kv_offsets, bias=None, causal=False):
-        out, lse = forward(q, k, v, q_offsets, kv_offsets, bias, causal)
+    def forward(ctx, q, k, v, q_offsets, kv_offsets, bias=None, causal=False, max_kv_len=0):
+        out, lse = forward(q, k, v, q_offsets, kv_offsets, bias, causal, max_kv_len=max_kv_len)
         ctx.save_for_backward(q, k, v, out, lse, q_offsets, kv_offsets, bias)
         ctx.causal = causal
+        ctx.max_kv_len = max_kv_len
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, lse, qo, ko, bias = ctx.saved_tensors
         want_db = bias is not None and ctx.needs_input_grad[5]
-        g = backward(q, k, v, out, lse, dout.contiguous(), qo, ko, bias, ctx.causal, bias_grad=want_db)
-        return g[0], g[1], g[2], None, None, (g[3] if want_db else None), None
+        g = backward(q, k, v, out, lse, dout.contiguous(), qo, ko, bias, ctx.causal, bias_grad=want_db,
+                     max_kv_len=ctx.max_kv_len)
+        return g[0], g[1], g[2], None, None, (g[3] if want_db else None), None, None
 
 
-def jagged_attention(q, k, v, q_offsets, kv_offsets, bias=None, causal=False):
-    return JaggedAttention.apply(q, k, v, q_offsets, kv_offsets, bias, causal)
+def jagged_attention(q, k, v, q_offsets, kv_offsets, bias=None, causal=False, max_kv_len=0):
+    return JaggedAttention.apply(q, k, v, q_offsets, kv_offsets, bias, causal, max_kv_len)
