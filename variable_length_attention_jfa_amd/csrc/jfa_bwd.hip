@@ -52,7 +52,7 @@ struct DkvTiles {
   static constexpr int ROWB = TL::ROWB;
   static constexpr int QTILE = BMQ * ROWB;  // Q (or dO) rows of one block
   static constexpr int QBLK = QTILE / 1024; // 1 KB load instructions per tile
-  static constexpr int RCOFF = 2 * QTILE;   // (lse2, Delta) of the block's rows
+  static constexpr int RCOFF = 2 * QTILE;   // lse2 of the block's rows, then -Delta
   static constexpr int SLOT = 2 * QTILE + BMQ * 8;
   static constexpr int NQC = QTILE / 16;    // 16-byte pieces per tile
   static constexpr int NCH = (2 * NQC + THREADS - 1) / THREADS;  // Q and dO pieces per thread
@@ -137,7 +137,10 @@ __device__ __forceinline__ void dkv_swrite(int jb, int tid, const DkvStage<T, D>
       *(__attribute__((address_space(3))) i32x4*)(sl + (x < C::NQC ? 0 : C::QTILE) + C::TL::chunk(row, col)) = st.c[c];
     }
   }
-  if (tid < C::BMQ) *(__attribute__((address_space(3))) i32x2*)(sl + C::RCOFF + 8 * tid) = st.rc;
+  if (tid < C::BMQ) {  // lse2 of the block's rows, then -Delta (the start of each dP accumulation)
+    ((__attribute__((address_space(3))) float*)(sl + C::RCOFF))[tid] = __int_as_float(st.rc[0]);
+    ((__attribute__((address_space(3))) float*)(sl + C::RCOFF))[C::BMQ + tid] = -__int_as_float(st.rc[1]);
+  }
 }
 
 // Blocks 0 and 1 of an item, both loads in flight together.
@@ -201,7 +204,7 @@ __device__ __forceinline__ void dkv_score_role(const BwdArgs& a, lds_t* lds, Que
           for (int i = 0; i < 16; ++i) {
             const int r = res_row(i, g);
             const int qi = qs0 + r;
-            float x = sc[i] * a.scale2 - rc[2 * r];
+            float x = sc[i] * a.scale2 - rc[r];
             if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
             float p = __builtin_amdgcn_exp2f(x);
             if (decltype(mask_c)::value && kj > qi) p = 0.f;
@@ -282,8 +285,16 @@ __device__ __forceinline__ void dkv_grad_role(const BwdArgs& a, lds_t* lds, Queu
         const lds_t* qt = lds + (jp % C::NSLOT) * C::SLOT;
         const lds_t* dot = qt + C::QTILE;
         const __attribute__((address_space(3))) float* rc = (const __attribute__((address_space(3))) float*)(qt + C::RCOFF);
-        // dP = dO V^T (same layout as S: lane = key, element i = query res_row(i, g))
-        f32x16 dp = (f32x16){};
+        // dP - Delta = dO V^T - Delta (same layout as S: lane = key, element i =
+        // query res_row(i, g)); the accumulation starts at -Delta of the rows
+        // (rows 8k + 4g .. 8k + 4g + 3 are elements 4k .. 4k + 3)
+        f32x16 dp;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const f32x4 nd = *(const __attribute__((address_space(3))) f32x4*)(rc + BMQ + 8 * k4 + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[4 * k4 + e] = nd[e];
+        }
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) mma(dp, lfrag<D>(dot, l32, 16 * kk + 8 * g, (T*)0), vf[kk]);
         const lds_t* pb = lds + C::PBUF + ((jp & 1) * C::PAIRS + pair) * C::PBLK;
@@ -298,7 +309,7 @@ __device__ __forceinline__ void dkv_grad_role(const BwdArgs& a, lds_t* lds, Queu
         }
         // dS = P (dP - Delta)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dp[i] = p[i] * (dp[i] - rc[2 * res_row(i, g) + 1]);
+        for (int i = 0; i < 16; ++i) dp[i] = p[i] * dp[i];
         if (DBIAS) {  // keys past the end: K = V = 0 leaves dS = -P Delta there, which is no pair's gradient
           f32x16 ds = dp;
           if (kw0 + l32 >= it.Lk) ds = (f32x16){};
@@ -363,7 +374,7 @@ struct Dkv1Tiles {
   using TL = Tile<T, D>;
   static constexpr int ROWB = TL::ROWB;
   static constexpr int QTILE = BMQ * ROWB;
-  static constexpr int STAGE = 2 * QTILE + 2 * BMQ * 4;  // Q, dO, (lse2, Delta) pairs
+  static constexpr int STAGE = 2 * QTILE + 2 * BMQ * 4;  // Q, dO, lse2 and -Delta per row
   static constexpr int CPR = ROWB / 16;
   static constexpr int CPT = BMQ * CPR / THREADS;
   static constexpr int BIAS_OFF = 2 * STAGE;
@@ -447,7 +458,10 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
         *(__attribute__((address_space(3))) i32x4*)(st + o) = qr[c];
         *(__attribute__((address_space(3))) i32x4*)(st + C::QTILE + o) = dr[c];
       }
-      if (tid < BMQ) *(__attribute__((address_space(3))) i32x2*)(st + 2 * C::QTILE + 8 * tid) = lr;
+      if (tid < BMQ) {  // lse2 of the block's rows, then -Delta (the start of each dP accumulation)
+        ((__attribute__((address_space(3))) float*)(st + 2 * C::QTILE))[tid] = __int_as_float(lr[0]);
+        ((__attribute__((address_space(3))) float*)(st + 2 * C::QTILE))[BMQ + tid] = -__int_as_float(lr[1]);
+      }
     };
     if (qb0 < nq) {
       gload(qb0);
@@ -475,7 +489,16 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
         const bool active = wave_on && qs0 < Lq && (!a.causal || qs0 + 31 >= kw0);
         if (!active) continue;
         const bool masked = a.causal && qs0 < kw0 + 31;
-        f32x16 sc = (f32x16){}, dp = (f32x16){};
+        // dP starts at -Delta of its rows (rows 8k + 4g .. 8k + 4g + 3 of the
+        // sub-block are elements 4k .. 4k + 3), so dP - Delta comes out of
+        // the matrix cores
+        f32x16 sc = (f32x16){}, dp;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const f32x4 nd = *(const __attribute__((address_space(3))) f32x4*)(rc + BMQ + 32 * sb + 8 * k4 + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[4 * k4 + e] = nd[e];
+        }
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
           mma(sc, lfrag<D>(qt, 32 * sb + l32, 16 * kk + 8 * g, (T*)0), kf[kk]);
@@ -488,12 +511,12 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
           for (int i = 0; i < 16; ++i) {
             const int r = 32 * sb + res_row(i, g);
             const int qi = qb * BMQ + r;
-            float x = sc[i] * a.scale2 - rc[2 * r];
+            float x = sc[i] * a.scale2 - rc[r];
             if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
             float p = __builtin_amdgcn_exp2f(x);
             if (decltype(mask_c)::value && kj > qi) p = 0.f;
             sc[i] = p;
-            dp[i] = p * (dp[i] - rc[2 * r + 1]);
+            dp[i] = p * dp[i];
           }
         };
         if (masked) softmax(std::true_type{});
