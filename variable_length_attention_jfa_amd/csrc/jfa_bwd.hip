@@ -679,11 +679,16 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
         const bool padded = key0 + BN > Lk;
         const lds_t* kt = lds + s * C::STAGE;
         const lds_t* vt = kt + C::KTILE;
+        // For D <= 64 the dP accumulation starts at -Delta (this lane's query),
+        // so dP - Delta comes out of the matrix cores; at D = 128 the 16
+        // registers this takes are not free.
+        constexpr bool kNegDelta = D <= 64;
         f32x16 sc[BN / 32], dp[BN / 32];
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) {
           sc[kb] = (f32x16){};
-          dp[kb] = (f32x16){};
+#pragma unroll
+          for (int i = 0; i < 16; ++i) dp[kb][i] = kNegDelta ? -dlt : 0.f;
 #pragma unroll
           for (int kk = 0; kk < D / 16; ++kk) {
             mma(sc[kb], lfrag<D>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), qf[kk]);
@@ -702,7 +707,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
               if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
               float p = __builtin_amdgcn_exp2f(x);
               if (decltype(edge_c)::value && ((masked && kj > qi) || (padded && kj >= Lk))) p = 0.f;
-              dp[kb][i] = p * (dp[kb][i] - dlt);
+              dp[kb][i] = p * (kNegDelta ? dp[kb][i] : dp[kb][i] - dlt);
             }
           }
         };
