@@ -250,8 +250,8 @@ def main(argv=None):
                     help="also run a plain device copy of MB mebibytes (reference for HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(multi-GPU runs are not part of this benchmark)",
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the library computes one GPU's share; sharding across GPUs is not implemented)",
               file=sys.stderr)
         return 2
 
