@@ -14,7 +14,10 @@ Prints one JSON line. `value` is fwd+bwd TFLOP/s of the default workload
 `roofline` entry is for the kernel with the largest share of the step,
 timed with HIP events around each of its launches on its own stream over the
 timed steps; `cpu_baseline` times the fp64 CPU oracle on a bounded sample of
-the same workload on the host cores.
+the same workload on the host cores; `padded_baseline` runs the same batch
+copied into zeroed slots of the longest sequence's length through the
+library's padded-dense kernels (a -inf key mask on every block, every block
+visited) and gives the jagged path's speedup and memory ratio over it.
 """
 from __future__ import annotations
 
@@ -93,7 +96,7 @@ KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "fsq": 4, "dkdv": 8, "dq": 6, "sq": 10}
 KERNEL_SEQS = {"forward": "long", "fsq": "short", "dkdv": "long", "dq": "long", "sq": "short"}
 
 
-def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None, bias_grad=False):
+def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None, bias_grad=False, padded_steps=0):
     wl = gen.WORKLOADS[idx]
     batch = gen.make_batch(wl, seed=seed)
     dev = torch.device("cuda")
@@ -182,8 +185,67 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None,
     res["roofline"] = {"kernel": label, **roof, "traffic": recorded_traffic(label, idx), "traffic_unit": "bytes/launch",
                        "avg_launch_ms": avg_ms, "algorithmic_flops_per_launch": alg,
                        "algorithmic_bytes_per_launch": alg_bytes}
+    if padded_steps > 0 and wl.dtype == "bf16":  # the padded-dense kernels are bf16 only
+        res["padded_baseline"] = run_padded(batch, d=dict(q=q, k=k, v=v, do=do, bias=bias, out=out, lse=lse, dq=dq),
+                                            steps=padded_steps, jfa_ms=ms_step, jfa_fwd_ms=fwd_ms, jfa_bwd_ms=bwd_ms,
+                                            torch=torch, jfa=jfa)
     res["_batch"] = batch
     return res
+
+
+def run_padded(batch, d, steps, jfa_ms, jfa_fwd_ms, jfa_bwd_ms, torch, jfa):
+    """The padded-dense baseline on the same batch: every sequence copied into a
+    zeroed slot of the longest sequence's length, forward with a -inf key mask
+    on every block, backward over every block (jfa_fwd_padded /
+    jfa_bwd_padded). Returns its step time, the speedup of the jagged path and
+    the memory ratio; the slots' valid rows are checked against the jagged
+    outputs."""
+    from variable_length_attention_jfa_amd import padded
+    wl = batch.wl
+    qo, ko = batch.q_offsets, batch.kv_offsets
+    q_slot, kv_slot = int(batch.q_lengths.max()), int(batch.kv_lengths.max())
+    qp, dop = padded.to_slots(d["q"], qo, q_slot), padded.to_slots(d["do"], qo, q_slot)
+    kp, vp = padded.to_slots(d["k"], ko, kv_slot), padded.to_slots(d["v"], ko, kv_slot)
+    kv_lens = torch.from_numpy(batch.kv_lengths.astype(np.int32)).to(qp.device)
+    outp, lsep = torch.empty_like(qp), torch.empty(qp.shape[:3], dtype=torch.float32, device=qp.device)
+    dqp, dkp, dvp = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
+
+    def step():
+        jfa.forward_padded(qp, kp, vp, kv_lens, d["bias"], wl.causal, out=outp, lse=lsep)
+        jfa.backward_padded(qp, kp, vp, outp, lsep, dop, d["bias"], wl.causal, dq=dqp, dk=dkp, dv=dvp)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    jfa.timing_collect()
+    jfa.timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    jfa.timing_enable(False)
+    kt = jfa.timing_collect()
+    fwd_ms = (kt["plan"][0] + kt["forward"][0]) / steps
+    bwd_ms = (kt["bwd_prep"][0] + kt["dkdv"][0] + kt["dq"][0]) / steps
+    # the same valid rows as the jagged path (different block order and masking: rounding-level differences)
+    diff_o = float((padded.from_slots(outp, qo).float() - d["out"].float()).abs().max()) if batch.total_q else 0.0
+    diff_dq = float((padded.from_slots(dqp, qo).float() - d["dq"].float()).abs().max()) if batch.total_q else 0.0
+    B, H, D = len(batch.q_lengths), wl.H, wl.D
+    elt = 2 if wl.dtype == "bf16" else 4
+    slot_b = padded.slot_bytes(B, q_slot, kv_slot, H, D, elt)
+    jag_b = padded.jagged_bytes(batch.total_q, batch.total_kv, H, D, elt)
+    scores_b = B * H * q_slot * kv_slot * 4  # a materialised fp32 score matrix of dense attention
+    del qp, dop, kp, vp, outp, lsep, dqp, dkp, dvp
+    return {"q_slot": q_slot, "kv_slot": kv_slot, "ms_per_step": ms, "fwd_ms_kernels": fwd_ms,
+            "bwd_ms_kernels": bwd_ms, "steps": steps,
+            "speedup_step": ms / jfa_ms, "speedup_fwd": fwd_ms / jfa_fwd_ms, "speedup_bwd": bwd_ms / jfa_bwd_ms,
+            "padded_bytes": slot_b, "jagged_bytes": jag_b, "memory_ratio": slot_b / jag_b,
+            "dense_scores_bytes": scores_b, "dense_memory_ratio": (slot_b + scores_b) / jag_b,
+            "max_abs_diff_out_vs_jagged": diff_o, "max_abs_diff_dq_vs_jagged": diff_dq}
 
 
 def algorithmic_bytes(kernel: str, batch) -> int:
@@ -243,6 +305,7 @@ def main(argv=None):
     ap.add_argument("--also", type=str, default="3", help="comma list of extra workloads reported alongside")
     ap.add_argument("--all", action="store_true", help="also report workloads 1..5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-padded", action="store_true", help="skip the padded-dense baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--bias-grad", action="store_true",
                     help="the backward also returns the bias-table gradient (workloads with a bias)")
@@ -276,18 +339,26 @@ def main(argv=None):
     if args.bias_grad and not gen.WORKLOADS[args.workload].bias:
         print(f"bench.py: workload {args.workload} has no bias; --bias-grad needs one", file=sys.stderr)
         return 2
-    main_res = run_workload(args.workload, args.steps, args.warmup, torch, jfa, gen, bias_grad=args.bias_grad)
+    pad_steps = 0 if args.no_padded else max(3, min(20, args.steps // 10))
+    main_res = run_workload(args.workload, args.steps, args.warmup, torch, jfa, gen, bias_grad=args.bias_grad,
+                            padded_steps=pad_steps)
+    pb = main_res.get("padded_baseline")
     print(f"[bench] workload {args.workload}: {main_res['tflops_step']:.1f} TFLOP/s fwd+bwd, "
-          f"fwd {main_res['fwd_tflops']:.1f} bwd {main_res['bwd_tflops']:.1f}", file=sys.stderr, flush=True)
+          f"fwd {main_res['fwd_tflops']:.1f} bwd {main_res['bwd_tflops']:.1f}"
+          + (f"; padded-dense {pb['ms_per_step']:.2f} ms/step, speedup {pb['speedup_step']:.2f}x, "
+             f"memory {pb['memory_ratio']:.2f}x" if pb else ""), file=sys.stderr, flush=True)
     extra_ids = list(range(1, 6)) if args.all else [int(x) for x in args.also.split(",") if x.strip()]
     extras = []
     for i in extra_ids:
         if i == args.workload:
             continue
-        r = run_workload(i, max(3, args.steps // 2), 2, torch, jfa, gen)
+        r = run_workload(i, max(3, args.steps // 2), 2, torch, jfa, gen, padded_steps=pad_steps)
         r.pop("_batch")
+        pb = r.get("padded_baseline")
         print(f"[bench] workload {i}: fwd {r['fwd_tflops']:.1f} ({r['fwd_pct_peak']:.1f}%) "
-              f"bwd {r['bwd_tflops']:.1f} ({r['bwd_pct_peak']:.1f}%)", file=sys.stderr, flush=True)
+              f"bwd {r['bwd_tflops']:.1f} ({r['bwd_pct_peak']:.1f}%)"
+              + (f"; padded-dense {pb['ms_per_step']:.2f} ms/step, speedup {pb['speedup_step']:.2f}x, "
+                 f"memory {pb['memory_ratio']:.2f}x" if pb else ""), file=sys.stderr, flush=True)
         extras.append(r)
         torch.cuda.empty_cache()
 
@@ -321,6 +392,7 @@ def main(argv=None):
         "kernel_avg_ms": main_res["kernel_avg_ms"],
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
+        "padded_baseline": main_res.get("padded_baseline"),
         "other_workloads": extras,
     }
     print(json.dumps(line))

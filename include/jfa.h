@@ -143,6 +143,41 @@ jfa_status jfa_bwd_f32(const void* q, const void* k, const void* v, const void* 
                        void* dq, void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* Padded-dense baseline (bf16), the comparison the method is measured
+ * against: padding every sequence to a common length wastes compute
+ * ("Jagged Flash Attention (JFA)", sections "Definition" and "Why standard
+ * FlashAttention falls short"), and the speedup and memory reduction over
+ * dense attention are the paper's headline figures ("Enhancing Performance
+ * and Scalability of Large-Scale Recommendation Systems with Jagged Flash
+ * Attention", section "Abstract"). Every sequence b occupies a fixed-length
+ * slot:
+ *   q, out, dout, dq  [B, q_slot,  H, D] bf16     lse [B, q_slot, H] fp32
+ *   k, v, dk, dv      [B, kv_slot, H, D] bf16
+ *   kv_lens           [B] int32 (device): the true key count of each slot,
+ *                     in [0, kv_slot] (values outside are clamped)
+ * The forward visits every block of every slot (query rows and keys up to the
+ * slot length) and masks keys j >= kv_lens[b] with -inf, element by element on
+ * every block, as a conventional kernel over padded tensors does; the causal
+ * mask and the bias are those of jfa_fwd. Rows of out and lse that lie past a
+ * sequence's true query length are computed like any other row and are the
+ * caller's to ignore. The backward visits every block as well. It needs the
+ * rows of q, k, v and dout past each sequence's true lengths to be zero (as a
+ * jagged batch copied into zeroed slots has them) and the lse of
+ * jfa_fwd_padded: then every product that involves a pad row is zero, and the
+ * rows of dq, dk, dv inside the true lengths are exact. It applies no key
+ * mask of its own, so it is no slower than a conventional masked backward.
+ * The softmax scale is 1/sqrt(D); no bias gradient. B * q_slot and
+ * B * kv_slot must be below 2^31. Workspace: jfa_padded_workspace_bytes, for
+ * either pass. Same ownership, asynchrony and error rules as jfa_fwd. */
+size_t jfa_padded_workspace_bytes(int B, int H, int q_slot, int kv_slot, int D);
+jfa_status jfa_fwd_padded(const void* q, const void* k, const void* v, const int32_t* kv_lens, int B, int q_slot,
+                          int kv_slot, int H, int D, const float* bias, int causal, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+jfa_status jfa_bwd_padded(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                          const void* dout, int B, int q_slot, int kv_slot, int H, int D, const float* bias,
+                          int causal, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* offsets[0] = 0, offsets[b+1] = offsets[b] + lengths[b] for b < B (device
  * int32 arrays, lengths [B], offsets [B+1]); the prefix-sum addressing of
  * jagged tensors ("Jagged Flash Attention (JFA)", section "Definition"). */
@@ -183,7 +218,7 @@ size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv,
 /* Launch timing, for benchmarks and profiling. While enabled, every kernel
  * launch of this library is bracketed by two HIP events recorded on its
  * stream (a few microseconds of host overhead per launch). */
-#define JFA_TIMING_KINDS 9 /* 0 work lists (forward, jfa_build_plan), 1 forward (with the short-query \
+#define JFA_TIMING_KINDS 9 /* 0 work lists (forward, jfa_build_plan, padded slot offsets), 1 forward (with the short-query \
                              chunk merge), 2 backward work lists with Delta (one launch), 3 dK/dV, \
                              4 dQ (with the short-query dQ sum), 5 offsets scan, 6 short-query backward chunks, \
                              7 short-query forward chunks, 8 bias-gradient sum */
@@ -198,7 +233,7 @@ const char* jfa_last_error(void);
 
 /* Version of the argument lists above; a binding compares it with the one it
  * was written for before calling anything else. */
-#define JFA_ABI_VERSION 2
+#define JFA_ABI_VERSION 3
 int jfa_abi_version(void);
 
 #ifdef __cplusplus

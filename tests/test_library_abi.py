@@ -81,3 +81,22 @@ def test_bias_gradient_needs_bias(L):
     st = L.jfa_bwd(dummy, dummy, dummy, dummy, fdummy, dummy, dummy, dummy, 2, 2, 64, 10, 10, 0, None, 0, dummy, dummy,
                    dummy, fdummy, dummy, 1 << 20, None)
     assert st == 1 and b"dbias needs a bias" in L.jfa_last_error()
+
+
+def test_padded_baseline_host_checks(L):
+    # workspace of the padded-dense baseline covers either pass at the padded totals
+    n = L.jfa_padded_workspace_bytes(64, 8, 1024, 1024, 64)
+    assert n >= L.jfa_bwd_workspace_bytes(64, 8, 64 * 1024, 64 * 1024, 64, 0)
+    assert n >= L.jfa_fwd_workspace_bytes(64, 8, 64 * 1024, 64 * 1024, 64, 0)
+    assert L.jfa_padded_workspace_bytes(8192, 1, 1 << 18, 1, 64) == 0  # B * q_slot = 2^31
+    assert L.jfa_padded_workspace_bytes(4, 2, -1, 8, 64) == 0
+    assert L.jfa_padded_workspace_bytes(4, 2, 8, 8, 48) == 0
+    dummy = ctypes.c_void_p(4096)
+    st = L.jfa_fwd_padded(dummy, dummy, dummy, dummy, 2, -1, 8, 2, 64, None, 0, dummy, dummy, dummy, 1 << 20, None)
+    assert st == 1 and b"invalid sizes" in L.jfa_last_error()
+    st = L.jfa_fwd_padded(dummy, dummy, dummy, None, 2, 8, 8, 2, 64, None, 0, dummy, dummy, dummy, 1 << 20, None)
+    assert st == 1 and b"kv_lens" in L.jfa_last_error()
+    ws = ctypes.c_void_p(4096 * 16)
+    st = L.jfa_bwd_padded(dummy, dummy, dummy, dummy, dummy, dummy, 2, 8, 8, 2, 64, None, 0, dummy, dummy, dummy, ws,
+                          64, None)
+    assert st == 2 and b"workspace too small" in L.jfa_last_error()

@@ -199,9 +199,12 @@ jfa_status check_common(const void* q, const void* k, const void* v, const int32
   return JFA_OK;
 }
 
+// pad_kv_len: non-null only for the padded-dense baseline (uniform slot
+// offsets in qo/ko, true key counts in pad_kv_len); it takes neither the
+// short-query passes nor the subtraction of pad terms.
 jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const int32_t* qo, const int32_t* ko,
                     int B, int H, int D, int64_t tq, int64_t tk, int max_kv_len, const float* bias, int causal,
-                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream, const int32_t* pad_kv_len = nullptr) {
   jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, max_kv_len, bias, ws);
   if (s != JFA_OK) return s;
   if (f32 && D > 64) return fail(JFA_ERR_UNSUPPORTED, "fp32 tensors support D = 32 or 64");
@@ -222,7 +225,7 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.B = B;
   pa.H = H;
   pa.causal = causal ? 1 : 0;
-  const bool short_on = short_pass_on(max_kv_len);
+  const bool short_on = short_pass_on(max_kv_len) && !pad_kv_len;
   pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::fwd_tile_rows(f32, D), jfa::kFwdTN,
                 jfa::kPassQ, jfa::kPlanQueues, short_on ? jfa::kSqQMax : -1, nullptr};
   pa.pass[1] = {(int4*)(w + L.items_sq), (PlanHeader*)(w + L.hdr_sq), (long)L.cap_sq, jfa::kSqQMax, jfa::kSqKC,
@@ -248,6 +251,7 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a.gfirst = short_on ? (int*)(w + L.gfirst) : nullptr;
   a.op = (float*)(w + L.op);
   a.lsep = (float*)(w + L.lsep);
+  a.kv_len = pad_kv_len;
   jfa::FwdArgs a_sq = a;
   a_sq.items = (const int4*)(w + L.items_sq);
   a_sq.hdr = (PlanHeader*)(w + L.hdr_sq);
@@ -256,7 +260,10 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   if (short_on)
     e = timed(kKindFsq, st, [&] { return jfa::launch_fsq(f32, D, a_sq, has_bias, (long)L.cap_sq, dev->num_cus, st); });
   if (e == hipSuccess)
-    e = timed(kKindFwd, st, [&] { return jfa::launch_fwd(f32, D, a, has_bias, (long)L.cap, dev->num_cus, st); });
+    e = timed(kKindFwd, st, [&] {
+      return pad_kv_len ? jfa::launch_fwd_padded(D, a, has_bias, (long)L.cap, dev->num_cus, st)
+                        : jfa::launch_fwd(f32, D, a, has_bias, (long)L.cap, dev->num_cus, st);
+    });
   if (e != hipSuccess) return fail(JFA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -264,7 +271,7 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
 jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const void* out, const float* lse,
                     const void* dout, const int32_t* qo, const int32_t* ko, int B, int H, int D, int64_t tq,
                     int64_t tk, int max_kv_len, const float* bias, int causal, void* dq, void* dk, void* dv,
-                    float* dbias, void* ws, size_t ws_bytes, void* stream) {
+                    float* dbias, void* ws, size_t ws_bytes, void* stream, bool padded = false) {
   jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, max_kv_len, bias, ws);
   if (s != JFA_OK) return s;
   if (f32 && D > 64) return fail(JFA_ERR_UNSUPPORTED, "fp32 tensors support D = 32 or 64");
@@ -297,7 +304,7 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.B = B;
   pa.H = H;
   pa.causal = causal ? 1 : 0;
-  const bool short_on = short_pass_on(max_kv_len);
+  const bool short_on = short_pass_on(max_kv_len) && !padded;
   const int short_q = short_on ? jfa::kSqQMax : -1;
   pa.pass[0] = {(int4*)(w + L.items_kv), (PlanHeader*)(w + L.hdr_kv), (long)L.cap_kv, jfa::dkv_tile_rows(f32, D),
                 jfa::kDkvTN, jfa::kPassKV, jfa::kPlanQueues, short_q, (int*)(w + L.gfirst_kv)};
@@ -359,6 +366,44 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   return ok();
 }
 
+// Padded-dense baseline: B fixed-length slots of q_slot query rows and
+// kv_slot key rows. Workspace: the slots' offsets [B+1] x 2, then the
+// forward's or the backward's workspace for the padded totals.
+bool padded_sizes_ok(int B, int H, int64_t q_slot, int64_t kv_slot, int D) {
+  return q_slot >= 0 && kv_slot >= 0 && B >= 0 && (int64_t)B * q_slot < (1LL << 31) &&
+         (int64_t)B * kv_slot < (1LL << 31) && valid_sizes(B, H, (int64_t)B * q_slot, (int64_t)B * kv_slot, D);
+}
+size_t padded_offsets_bytes(int B) { return 2 * align_up((size_t)(B + 1) * 4); }
+size_t padded_ws_bytes(int B, int H, int64_t q_slot, int64_t kv_slot, int D) {
+  const int64_t tq = (int64_t)B * q_slot, tk = (int64_t)B * kv_slot;
+  const size_t f = fwd_layout(B, H, tq, tk, D).total, b = bwd_layout(B, H, tq, tk, D).total;
+  return padded_offsets_bytes(B) + (f > b ? f : b);
+}
+
+// Checks the slot sizes and the workspace, then writes the slot offsets at
+// its start. *rest receives the part left for the pass itself.
+jfa_status padded_setup(int B, int H, int q_slot, int kv_slot, int D, void* ws, size_t ws_bytes, void* stream,
+                        char** rest, size_t* rest_bytes) {
+  if (!padded_sizes_ok(B, H, q_slot, kv_slot, D))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "invalid sizes: B=%d, H=%d, D=%d, q_slot=%d, kv_slot=%d (B * slot < 2^31)", B,
+                H, D, q_slot, kv_slot);
+  if (!ws || !aligned(ws, kAlign)) return fail(JFA_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  const size_t need = padded_ws_bytes(B, H, q_slot, kv_slot, D);
+  if (ws_bytes < need) return fail(JFA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  DeviceInfo* dev = nullptr;
+  jfa_status s = device_info(&dev);
+  if (s != JFA_OK) return s;
+  char* w = (char*)ws;
+  int* qo = (int*)w;
+  int* ko = (int*)(w + align_up((size_t)(B + 1) * 4));
+  hipError_t e = timed(kKindPlan, (hipStream_t)stream,
+                       [&] { return jfa::launch_slot_offsets(B, q_slot, kv_slot, qo, ko, (hipStream_t)stream); });
+  if (e != hipSuccess) return fail(JFA_ERR_HIP, "slot offsets launch: %s", hipGetErrorString(e));
+  *rest = w + padded_offsets_bytes(B);
+  *rest_bytes = ws_bytes - padded_offsets_bytes(B);
+  return JFA_OK;
+}
+
 bool tile_of(int kernel, int D, int dtype, int* tm, int* tn) {
   switch (kernel) {
     case JFA_KERNEL_FWD: *tm = jfa::fwd_tile_rows(dtype == JFA_DTYPE_F32, D); *tn = jfa::kFwdTN; return true;
@@ -415,6 +460,40 @@ jfa_status jfa_bwd_f32(const void* q, const void* k, const void* v, const void* 
                        void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(true, q, k, v, out, lse, dout, q_offsets, kv_offsets, B, H, D, total_q, total_kv, max_kv_len, bias,
                   causal, dq, dk, dv, dbias, workspace, workspace_bytes, stream);
+}
+
+size_t jfa_padded_workspace_bytes(int B, int H, int q_slot, int kv_slot, int D) {
+  if (!padded_sizes_ok(B, H, q_slot, kv_slot, D)) return 0;
+  return padded_ws_bytes(B, H, q_slot, kv_slot, D);
+}
+
+jfa_status jfa_fwd_padded(const void* q, const void* k, const void* v, const int32_t* kv_lens, int B, int q_slot,
+                          int kv_slot, int H, int D, const float* bias, int causal, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!kv_lens || !aligned(kv_lens, 4)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "kv_lens must be non-NULL and 4-byte aligned");
+  char* rest = nullptr;
+  size_t rest_bytes = 0;
+  jfa_status s = padded_setup(B, H, q_slot, kv_slot, D, workspace, workspace_bytes, stream, &rest, &rest_bytes);
+  if (s != JFA_OK) return s;
+  const int32_t* qo = (const int32_t*)workspace;
+  const int32_t* ko = (const int32_t*)((char*)workspace + align_up((size_t)(B + 1) * 4));
+  return fwd_impl(false, q, k, v, qo, ko, B, H, D, (int64_t)B * q_slot, (int64_t)B * kv_slot, 0, bias, causal, out,
+                  lse, rest, rest_bytes, stream, B > 0 ? kv_lens : nullptr);
+}
+
+jfa_status jfa_bwd_padded(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                          const void* dout, int B, int q_slot, int kv_slot, int H, int D, const float* bias,
+                          int causal, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  char* rest = nullptr;
+  size_t rest_bytes = 0;
+  jfa_status s = padded_setup(B, H, q_slot, kv_slot, D, workspace, workspace_bytes, stream, &rest, &rest_bytes);
+  if (s != JFA_OK) return s;
+  const int32_t* qo = (const int32_t*)workspace;
+  const int32_t* ko = (const int32_t*)((char*)workspace + align_up((size_t)(B + 1) * 4));
+  return bwd_impl(false, q, k, v, out, lse, dout, qo, ko, B, H, D, (int64_t)B * q_slot, (int64_t)B * kv_slot, 0,
+                  bias, causal, dq, dk, dv, nullptr, rest, rest_bytes, stream, true);
 }
 
 jfa_status jfa_offsets_from_lengths(const int32_t* lengths, int B, int32_t* offsets, void* stream) {

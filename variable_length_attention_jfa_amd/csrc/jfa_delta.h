@@ -56,7 +56,8 @@ __device__ __forceinline__ void delta_rows(const BwdArgs& a, long blk, int tid) 
 #pragma unroll
     for (int s = S::TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
     const long row = r0 + k * S::RPP;
-    if (row < rows && part == 0) a.rowc[row] = make_float2(l[k] * kLog2e, acc);
+    // a row that sees no key (lse = -inf) gets +inf, so that its P = 2^(s - c) is 0 for every key
+    if (row < rows && part == 0) a.rowc[row] = make_float2(l[k] == -INFINITY ? INFINITY : l[k] * kLog2e, acc);
   }
 }
 

@@ -57,7 +57,12 @@ struct FwdTiles {
   static_assert(BM == FwdRows<T, D>::value && BN == kFwdTN, "tile shape published to the planner");
 };
 
-template <typename T, int D, bool BIAS>
+// PADDED: the padded-dense baseline. Every sequence occupies a fixed-length
+// slot of a dense [B, L, H, D] tensor (uniform offsets), every block of the
+// slot is visited, and keys at or past the sequence's true length
+// (a.kv_len[b]) are masked with -inf on every block, element by element, as a
+// conventional kernel over padded tensors does.
+template <typename T, int D, bool BIAS, bool PADDED = false>
 __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_kernel(FwdArgs a) {
   using C = FwdTiles<T, D>;
   constexpr int BM = C::BM, BN = C::BN, ES = (int)sizeof(T);
@@ -86,6 +91,8 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
     const int k0 = a.kv_off[b], Lk = a.kv_off[b + 1] - k0;
     const int row0 = qt * BM;
     const int n_kv = a.causal ? cdiv(min(min(row0 + BM, Lq), Lk), BN) : cdiv(Lk, BN);
+    // keys at or past Lmask are dropped by the element mask of masked blocks
+    const int Lmask = PADDED ? min(max(a.kv_len[b], 0), Lk) : Lk;
 
     const size_t qrow = ((size_t)q0 * H + h) * C::ROWB, krow = ((size_t)k0 * H + h) * C::ROWB;
     const View qv = seq_view((const char*)a.q + qrow, Lq, gstride, C::ROWB);
@@ -142,9 +149,10 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
       const int key0 = j * BN;
       const bool active = wave_on && (!a.causal || key0 <= wr0 + 31);
       if (active) {
-        const bool masked = (a.causal && (key0 + BN - 1 > wr0)) || kFwdMaskMode == 2 ||
+        const bool masked = PADDED || (a.causal && (key0 + BN - 1 > wr0)) || kFwdMaskMode == 2 ||
                             (kFwdMaskMode == 1 && key0 + BN > Lk);
-        const bool cmask = kFwdMaskMode == 0 || a.causal;  // with the subtraction, masked blocks are causal ones
+        // with the subtraction, masked blocks are causal ones
+        const bool cmask = PADDED ? a.causal != 0 : (kFwdMaskMode == 0 || a.causal);
         last_tile = j;
         last_masked = masked;
         const lds_t* kt = lds + s * C::STAGE;
@@ -175,7 +183,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
               const int kj = key0 + 32 * kb + res_row(i, g);
               float x = sc[kb][i] * a.scale2;
               if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
-              if (masked && ((cmask && kj > qi) || kj >= Lk)) x = -INFINITY;
+              if (masked && ((cmask && kj > qi) || kj >= Lmask)) x = -INFINITY;
               sc[kb][i] = x;
               mx = fmaxf(mx, x);
             }
@@ -264,9 +272,9 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PADDED = false>
 static hipError_t launch_fwd_t(const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
-  auto kern = bias ? jfa_fwd_kernel<T, D, true> : jfa_fwd_kernel<T, D, false>;
+  auto kern = bias ? jfa_fwd_kernel<T, D, true, PADDED> : jfa_fwd_kernel<T, D, false, PADDED>;
   static int occ_b = 0, occ_n = 0;
   int& occ = bias ? occ_b : occ_n;
   if (occ == 0) {
@@ -294,6 +302,13 @@ hipError_t launch_fwd(bool f32, int D, const FwdArgs& a, bool bias, long max_ite
   if (D == 32) return launch_fwd_t<bf16, 32>(a, bias, max_items, num_cus, st);
   if (D == 64) return launch_fwd_t<bf16, 64>(a, bias, max_items, num_cus, st);
   return launch_fwd_t<bf16, 128>(a, bias, max_items, num_cus, st);
+}
+
+// Padded-dense baseline (bf16): uniform offsets in a, true key lengths in a.kv_len.
+hipError_t launch_fwd_padded(int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
+  if (D == 32) return launch_fwd_t<bf16, 32, true>(a, bias, max_items, num_cus, st);
+  if (D == 64) return launch_fwd_t<bf16, 64, true>(a, bias, max_items, num_cus, st);
+  return launch_fwd_t<bf16, 128, true>(a, bias, max_items, num_cus, st);
 }
 
 }  // namespace jfa

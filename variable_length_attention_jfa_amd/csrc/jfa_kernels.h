@@ -25,6 +25,7 @@ struct FwdArgs {
   int* gfirst;         // short-query pass: [B*H] list position of chunk 0 of each (b, h), -1 if none; null: no such pass
   float* op;           // short-query pass: per item, [64, D] fp32 rows normalised over the chunk's keys
   float* lsep;         // short-query pass: per item, [64] log2 of each row's sum over the chunk's keys
+  const int* kv_len;   // padded-dense baseline only: [B] true key count of each fixed-length slot
 };
 
 struct BwdArgs {
@@ -112,6 +113,7 @@ constexpr int kDqTM = 128, kDqTN = 64;
 // The short-query chunk passes run first; the forward launch then merges the
 // chunks of each sequence and the dQ launch sums its partial dQ.
 hipError_t launch_fwd(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
+hipError_t launch_fwd_padded(int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
 hipError_t launch_fsq(bool f32, int D, const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st);
 hipError_t launch_dkdv(bool f32, int D, const BwdArgs& a, bool bias, bool dbias, long max_items, int num_cus,
                        hipStream_t st);
@@ -123,5 +125,7 @@ hipError_t launch_plan(const PlanArgs& a, int npass, hipStream_t st);
 // The backward's lists (passes of p) and Delta of every row (a.rowc), one launch.
 hipError_t launch_bwd_prep(const PlanArgs& p, int npass, bool f32, int D, const BwdArgs& a, hipStream_t st);
 hipError_t launch_scan(const int* lengths, int B, int* offsets, hipStream_t st);
+// Uniform offsets of B fixed-length slots: qo[b] = b * Lq, ko[b] = b * Lk, b <= B.
+hipError_t launch_slot_offsets(int B, int Lq, int Lk, int* qo, int* ko, hipStream_t st);
 
 }  // namespace jfa

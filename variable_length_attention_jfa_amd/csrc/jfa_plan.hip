@@ -302,6 +302,16 @@ __global__ __launch_bounds__(kPlanThreads) void jfa_scan_kernel(const int* lengt
   if (threadIdx.x == 0) offsets[B] = carry;
 }
 
+// Offsets of B fixed-length slots (the padded-dense baseline's layout):
+// qo[b] = b * Lq, ko[b] = b * Lk for b = 0 .. B. B * L < 2^31 is checked on the host.
+__global__ __launch_bounds__(kPlanThreads) void jfa_slot_offsets_kernel(int B, int Lq, int Lk, int* qo, int* ko) {
+  const int b = blockIdx.x * kPlanThreads + threadIdx.x;
+  if (b <= B) {
+    qo[b] = b * Lq;
+    ko[b] = b * Lk;
+  }
+}
+
 static bool plan_tiles_ok(const PlanArgs& a, int npass) {
   for (int i = 0; i < npass; ++i) {
     const PlanPass& p = a.pass[i];
@@ -352,6 +362,12 @@ hipError_t launch_bwd_prep(const PlanArgs& p, int npass, bool f32, int D, const 
 
 hipError_t launch_scan(const int* lengths, int B, int* offsets, hipStream_t st) {
   hipLaunchKernelGGL(jfa_scan_kernel, dim3(1), dim3(kPlanThreads), 0, st, lengths, B, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_offsets(int B, int Lq, int Lk, int* qo, int* ko, hipStream_t st) {
+  const int nblk = (B + 1 + kPlanThreads - 1) / kPlanThreads;
+  hipLaunchKernelGGL(jfa_slot_offsets_kernel, dim3(nblk), dim3(kPlanThreads), 0, st, B, Lq, Lk, qo, ko);
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ KERNEL_FWD, KERNEL_BWD_DKDV, KERNEL_BWD_DQ, KERNEL_BWD_SQ, KERNEL_FWD_SQ = 0, 1,
 SQ_KERNELS = (KERNEL_BWD_SQ, KERNEL_FWD_SQ)  # short-query chunk lists (one list, two passes)
 DTYPE_BF16, DTYPE_F32 = 0, 1
 BIAS_RADIUS = 128
-ABI_VERSION = 2  # JFA_ABI_VERSION of include/jfa.h
+ABI_VERSION = 3  # JFA_ABI_VERSION of include/jfa.h
 WORKSPACE_ALIGN = 256
 PLAN_HEADER_BYTES = 2048
 PLAN_QUEUES = 8
@@ -50,6 +50,10 @@ _SIGS = {
                        _vp, _vp, _vp, _f32p, _vp, _sz, _vp]),
     "jfa_bwd_f32": (_int, [_vp, _vp, _vp, _vp, _f32p, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _int, _f32p, _int,
                            _vp, _vp, _vp, _f32p, _vp, _sz, _vp]),
+    "jfa_padded_workspace_bytes": (_sz, [_int, _int, _int, _int, _int]),
+    "jfa_fwd_padded": (_int, [_vp, _vp, _vp, _i32p, _int, _int, _int, _int, _int, _f32p, _int, _vp, _f32p, _vp, _sz, _vp]),
+    "jfa_bwd_padded": (_int, [_vp, _vp, _vp, _vp, _f32p, _vp, _int, _int, _int, _int, _int, _f32p, _int, _vp, _vp, _vp,
+                              _vp, _sz, _vp]),
     "jfa_offsets_from_lengths": (_int, [_i32p, _int, _i32p, _vp]),
     "jfa_tile_config": (_int, [_int, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
     "jfa_build_plan": (_int, [_i32p, _i32p, _int, _int, _int, _int, _int, _int, _vp, _sz, _vp]),
@@ -190,6 +194,63 @@ def backward(q, k, v, out, lse, dout, q_offsets, kv_offsets, bias=None, causal: 
             ctypes.c_void_p(wp), nbytes, _stream())
     _check("jfa_bwd", st)
     return (dq, dk, dv, dbias) if bias_grad else (dq, dk, dv)
+
+
+def _padded_common(q, k, v, bias):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch.bfloat16, 4)
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if k.shape[0] != B or k.shape[2:] != (H, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, kv_slot, H, D] with q's B, H and D")
+    if bias is not None:
+        _check_tensor("bias", bias, torch.float32, 2)
+        if bias.shape != (H, 2 * BIAS_RADIUS + 1):
+            raise ValueError(f"bias must be [H, {2 * BIAS_RADIUS + 1}]")
+    return B, Sq, Sk, H, D
+
+
+def forward_padded(q, k, v, kv_lens, bias=None, causal: bool = False, out=None, lse=None):
+    """Padded-dense baseline forward: q [B, q_slot, H, D], k/v [B, kv_slot, H, D] bf16, kv_lens int32 [B] on
+    the GPU (true key counts). Returns (out [B, q_slot, H, D], lse fp32 [B, q_slot, H]); rows past a
+    sequence's true query length are not meaningful."""
+    B, Sq, Sk, H, D = _padded_common(q, k, v, bias)
+    _check_tensor("kv_lens", kv_lens, torch.int32, 1)
+    if kv_lens.numel() != B:
+        raise ValueError("kv_lens must have B entries")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Sq, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor("out", out, q.dtype, 4)
+    _check_tensor("lse", lse, torch.float32, 3)
+    L = lib()
+    nbytes = L.jfa_padded_workspace_bytes(B, H, Sq, Sk, D)
+    if nbytes == 0:
+        raise ValueError("invalid padded sizes")
+    ws, wp = _workspace(nbytes, q.device)
+    st = L.jfa_fwd_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), B, Sq, Sk, H, D, _ptr(bias), int(causal),
+                          _ptr(out), _ptr(lse), ctypes.c_void_p(wp), nbytes, _stream())
+    _check("jfa_fwd_padded", st)
+    return out, lse
+
+
+def backward_padded(q, k, v, out, lse, dout, bias=None, causal: bool = False, dq=None, dk=None, dv=None):
+    """Padded-dense baseline backward (pad rows of q, k, v, dout must be zero); returns (dq, dk, dv)."""
+    B, Sq, Sk, H, D = _padded_common(q, k, v, bias)
+    _check_tensor("out", out, q.dtype, 4)
+    _check_tensor("dout", dout, q.dtype, 4)
+    _check_tensor("lse", lse, torch.float32, 3)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    L = lib()
+    nbytes = L.jfa_padded_workspace_bytes(B, H, Sq, Sk, D)
+    if nbytes == 0:
+        raise ValueError("invalid padded sizes")
+    ws, wp = _workspace(nbytes, q.device)
+    st = L.jfa_bwd_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), B, Sq, Sk, H, D, _ptr(bias),
+                          int(causal), _ptr(dq), _ptr(dk), _ptr(dv), ctypes.c_void_p(wp), nbytes, _stream())
+    _check("jfa_bwd_padded", st)
+    return dq, dk, dv
 
 
 def offsets_from_lengths(lengths: torch.Tensor) -> torch.Tensor:
