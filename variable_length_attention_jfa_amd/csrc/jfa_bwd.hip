@@ -499,11 +499,13 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) dp[4 * k4 + e] = nd[e];
         }
+        prio_mfma();
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
           mma(sc, lfrag<D>(qt, 32 * sb + l32, 16 * kk + 8 * g, (T*)0), kf[kk]);
           mma(dp, lfrag<D>(dot, 32 * sb + l32, 16 * kk + 8 * g, (T*)0), vf[kk]);
         }
+        prio_valu();
         // sc[i] = S[query 32sb + res_row(i,g)][key kj]; the element test for
         // the causal mask only on blocks that straddle the diagonal
         auto softmax = [&](auto mask_c) {
@@ -526,6 +528,7 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
           if (kj >= Lk) ds = (f32x16){};
           db_block(db, ds, qs0 - kw0, lane);
         }
+        prio_mfma();
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const Frag<T> pf = rfrag(sc, c, (T*)0);
@@ -536,6 +539,7 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
             mma(dk[db], tfrag<D>(qt, 32 * sb + 16 * c, 32 * db, lane, (T*)0), sf);
           }
         }
+        prio_valu();
       }
       if (qb + 1 < nq) swrite((qb + 1 - qb0) & 1);
       __syncthreads();

@@ -363,6 +363,15 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Wave priority around the matrix-product clusters: a wave that reaches its
+// MFMAs is issued ahead of the SIMD's other waves (which are then in their
+// softmax VALU work), so the matrix pipe is refilled as soon as one of them
+// has products ready. Measured: forward -2 to -3% (D = 64 and 128), one-role
+// dK/dV kernel -2%; the paired-wave dK/dV kernel and the dQ kernel were
+// 0.5-1% slower with it and do not use it.
+__device__ __forceinline__ void prio_mfma() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void prio_valu() { __builtin_amdgcn_s_setprio(0); }
+
 // Work-list header in the caller's workspace: kMaxQueues queues stored one
 // after the other in the item array (one queue per XCD). Each queue's ticket
 // sits on its own 128-byte line, away from the read-only words, so that the

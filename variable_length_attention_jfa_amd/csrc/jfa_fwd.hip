@@ -158,6 +158,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
         const lds_t* kt = lds + s * C::STAGE;
         const lds_t* vt = kt + C::KTILE;
         f32x16 sc[BN / 32];
+        prio_mfma();
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) {
           sc[kb] = (f32x16){};
@@ -165,6 +166,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
           for (int kk = 0; kk < D / 16; ++kk)
             mma(sc[kb], lfrag<D>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), qf[kk]);
         }
+        prio_valu();
         // Scores in log2 units: x = s * scale * log2(e) (+ bias * log2(e)).
         float mx = -INFINITY;
         const bool plain = !BIAS && !masked;
@@ -225,12 +227,14 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
             }
           }
         }
+        prio_mfma();
 #pragma unroll
         for (int kc = 0; kc < BN / 16; ++kc) {
           const Frag<T> pf = rfrag(sc[kc >> 1], kc & 1, (T*)0);
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) mma(o[db], tfrag<D>(vt, 16 * kc, 32 * db, lane, (T*)0), pf);
         }
+        prio_valu();
       }
       if (j + 1 < n_kv) swrite((j + 1) & 1);
       __syncthreads();
