@@ -166,6 +166,9 @@ jfa_status jfa_bwd_f32(const void* q, const void* k, const void* v, const void* 
  * jfa_fwd_padded: then every product that involves a pad row is zero, and the
  * rows of dq, dk, dv inside the true lengths are exact. It applies no key
  * mask of its own, so it is no slower than a conventional masked backward.
+ * Without that mask, a pad key's P = exp(bias - lse) overflows fp32 for a
+ * row whose lse lies more than ~88 below the pad score, and dq of that row is
+ * then not finite; inputs with unit-scale scores are far from this.
  * The softmax scale is 1/sqrt(D); no bias gradient. B * q_slot and
  * B * kv_slot must be below 2^31. Workspace: jfa_padded_workspace_bytes, for
  * either pass. Same ownership, asynchrony and error rules as jfa_fwd. */
