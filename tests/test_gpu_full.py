@@ -43,3 +43,35 @@ def test_full_workload_sampled_parity(cfg):
     del d, out, lse, dq, dk, dv, batch
     gc.collect()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_full_workload_padded_baseline_sampled_parity(cfg):
+    """The padded-dense baseline at full size (slots of the batch's longest
+    lengths, as the benchmark runs it), sampled slices against the oracle."""
+    from variable_length_attention_jfa_amd import padded
+    wl = gen.WORKLOADS[cfg]
+    print(f"[case] padded baseline, full workload {cfg} ({wl.name})", flush=True)
+    batch = gen.make_batch(wl)
+    d = to_device(batch)
+    qo, ko = batch.q_offsets, batch.kv_offsets
+    q_slot, kv_slot = int(batch.q_lengths.max()), int(batch.kv_lengths.max())
+    qp, dop = padded.to_slots(d["q"], qo, q_slot), padded.to_slots(d["dout"], qo, q_slot)
+    kp, vp = padded.to_slots(d["k"], ko, kv_slot), padded.to_slots(d["v"], ko, kv_slot)
+    kv_lens = torch.from_numpy(batch.kv_lengths.astype(np.int32)).cuda()
+    out_p, lse_p = jfa.forward_padded(qp, kp, vp, kv_lens, d["bias"], wl.causal)
+    dq_p, dk_p, dv_p = jfa.backward_padded(qp, kp, vp, out_p, lse_p, dop, d["bias"], wl.causal)
+    torch.cuda.synchronize()
+    out, lse = padded.from_slots(out_p, qo), padded.from_slots(lse_p, qo)
+    dq, dk, dv = padded.from_slots(dq_p, qo), padded.from_slots(dk_p, ko), padded.from_slots(dv_p, ko)
+    for t in (out, lse, dq, dk, dv):
+        assert torch.isfinite(t.float()).all(), "non-finite output"
+    pairs = sample_pairs(batch, n_random=2, seed=cfg)
+    tol = tol_for(batch)
+    e_o, e_l, _, _ = compare_forward(batch, out, lse, pairs)
+    r = compare_backward(batch, dq, dk, dv, pairs)
+    print(f"   slots {q_slot}/{kv_slot}: fwd {e_o:.3e} lse {e_l:.3e} bwd relL2 {r[0]:.2e}/{r[1]:.2e}/{r[2]:.2e}", flush=True)
+    assert e_o <= tol["out"] and e_l <= tol["lse"] and max(r) <= tol["grad"]
+    del d, qp, dop, kp, vp, out_p, lse_p, dq_p, dk_p, dv_p, batch
+    gc.collect()
+    torch.cuda.empty_cache()
