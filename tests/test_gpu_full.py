@@ -25,9 +25,12 @@ def test_full_workload_sampled_parity(cfg):
     batch = gen.make_batch(wl)
     d = to_device(batch)
     print(f"   B={wl.B} Tq={batch.total_q} Tk={batch.total_kv} on device", flush=True)
-    out, lse = jfa.forward(d["q"], d["k"], d["v"], d["q_offsets"], d["kv_offsets"], d["bias"], wl.causal)
+    # the key-count bound the benchmark passes (the batch's longest key side)
+    max_kv = int(batch.kv_lengths.max())
+    out, lse = jfa.forward(d["q"], d["k"], d["v"], d["q_offsets"], d["kv_offsets"], d["bias"], wl.causal,
+                           max_kv_len=max_kv)
     dq, dk, dv = jfa.backward(d["q"], d["k"], d["v"], out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], d["bias"],
-                              wl.causal)
+                              wl.causal, max_kv_len=max_kv)
     torch.cuda.synchronize()
     for t in (out, lse, dq, dk, dv):
         assert torch.isfinite(t.float()).all(), "non-finite output"
