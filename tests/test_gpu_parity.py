@@ -349,3 +349,27 @@ def test_bias_gradient_no_pairs():
                      bias_grad=True)
     torch.cuda.synchronize()
     assert torch.count_nonzero(g[3]) == 0
+
+
+@pytest.mark.parametrize("variant", [1, 2, 3])
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_scheduling_study_variants(variant, cfg):
+    """The list-order and grid variants of the scheduling study compute every
+    work item the same way: their forward equals the library's bit for bit, and
+    the oracle's within the tolerances."""
+    from variable_length_attention_jfa_amd import sched_study
+    path = sched_study.lib_path(variant)
+    if not os.path.exists(path):
+        pytest.skip("study variants not built (python -m variable_length_attention_jfa_amd.sched_study --build)")
+    batch = gen.make_batch(SMALL[cfg])
+    ref = _run(batch, with_bwd=False)
+    saved = jfa.LIB_PATH
+    try:
+        jfa._LIB = None
+        jfa.LIB_PATH = path
+        _check(batch, with_bwd=False, label=f"scheduling variant {variant} cfg{cfg}")
+        got = _run(batch, with_bwd=False)
+    finally:
+        jfa._LIB = None
+        jfa.LIB_PATH = saved
+    assert torch.equal(got[0].view(torch.int16), ref[0].view(torch.int16)) and torch.equal(got[1], ref[1])

@@ -37,7 +37,15 @@
 
 namespace jfa {
 
+// How forward workgroups take work. 1: persistent, CUs x resident workgroups,
+// each takes items until the list is empty (the method). 0 exists only for a
+// scheduling study: one workgroup per list slot, each takes one item.
+#ifndef JFA_SCHED_PERSISTENT
+#define JFA_SCHED_PERSISTENT 1
+#endif
+
 constexpr int kFwdMaskMode = JFA_FWD_MASK_MODE;
+constexpr bool kSchedPersistent = JFA_SCHED_PERSISTENT != 0;
 static_assert(kFwdMaskMode >= 0 && kFwdMaskMode <= 2, "mask mode");
 
 template <typename T, int D>
@@ -273,6 +281,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
         st4f(lv, (uint32_t)qi * H * 4, lse);
       }
     }
+    if constexpr (!kSchedPersistent) break;  // one item per workgroup
   }
 }
 
@@ -286,7 +295,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, bool bias, long max_items, int 
     if (e != hipSuccess) return e;
     if (occ < 1) occ = 1;
   }
-  const long grid = max(1L, min(max_items, (long)num_cus * occ));
+  const long grid = kSchedPersistent ? max(1L, min(max_items, (long)num_cus * occ)) : max(1L, max_items);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -32,6 +32,10 @@
 
 namespace jfa {
 
+#ifndef JFA_SCHED_LPT
+#define JFA_SCHED_LPT 1
+#endif
+
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanMaxB = 8192;
@@ -150,7 +154,9 @@ __device__ __forceinline__ void plan_pass(const PlanArgs& a, int pi, char* dyn) 
       for (int t = 0; t < n; ++t) gc += plan_cost(Lq, Lk, t, pg, a.causal);
       lq_s[b] = Lq;
       lk_s[b] = Lk;
-      k = ((unsigned long long)(0x7FFFFFFFu - (unsigned)gc) << 32) | (unsigned)b;
+      // JFA_SCHED_LPT = 0 (scheduling study only): groups in sequence order, not longest first
+      const unsigned rank_cost = JFA_SCHED_LPT ? 0x7FFFFFFFu - (unsigned)gc : 0u;
+      k = ((unsigned long long)rank_cost << 32) | (unsigned)b;
     }
     key[b] = k;
   }
