@@ -373,3 +373,21 @@ def test_scheduling_study_variants(variant, cfg):
         jfa._LIB = None
         jfa.LIB_PATH = saved
     assert torch.equal(got[0].view(torch.int16), ref[0].view(torch.int16)) and torch.equal(got[1], ref[1])
+
+
+def test_binding_rejects_wrong_output_shapes():
+    """Output buffers are written through plain pointers: the binding refuses
+    any whose shape differs from what the call writes."""
+    batch = gen.make_batch(SMALL[2])
+    d = to_device(batch)
+    args = (d["q"], d["k"], d["v"], d["q_offsets"], d["kv_offsets"], None, False)
+    short = torch.empty((batch.total_q - 1,) + tuple(d["q"].shape[1:]), dtype=d["q"].dtype, device="cuda")
+    with pytest.raises(ValueError, match="shape"):
+        jfa.forward(*args, out=short)
+    out, lse = jfa.forward(*args)
+    with pytest.raises(ValueError, match="shape"):
+        jfa.backward(d["q"], d["k"], d["v"], out, lse, d["dout"], d["q_offsets"], d["kv_offsets"], None, False,
+                     dk=d["k"][:-1])
+    with pytest.raises(ValueError, match="shape"):
+        jfa.backward(d["q"], d["k"], d["v"], out, lse[:-1], d["dout"], d["q_offsets"], d["kv_offsets"], None, False)
+    torch.cuda.synchronize()

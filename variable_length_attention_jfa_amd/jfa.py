@@ -128,6 +128,13 @@ def _check_tensor(name: str, t: torch.Tensor, dtype, dims: int):
         raise ValueError(f"{name} must be a contiguous {dims}-d tensor")
 
 
+def _check_shape(name: str, t: torch.Tensor, shape) -> None:
+    # the library writes through plain pointers: a buffer smaller than its
+    # tensor's logical size would be written past its end
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _common(q, k, v, q_offsets, kv_offsets, bias):
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q/k/v must be bfloat16 or float32")
@@ -161,6 +168,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: torch.
         lse = torch.empty((Tq, H), dtype=torch.float32, device=q.device)
     _check_tensor("out", out, q.dtype, 3)
     _check_tensor("lse", lse, torch.float32, 2)
+    _check_shape("out", out, q.shape)
+    _check_shape("lse", lse, (Tq, H))
     L = lib()
     nbytes = L.jfa_fwd_workspace_bytes(B, H, Tq, Tk, D, int(causal))
     ws, wp = _workspace(nbytes, q.device)
@@ -184,6 +193,10 @@ def backward(q, k, v, out, lse, dout, q_offsets, kv_offsets, bias=None, causal: 
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("out", out, q), ("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(name, t, q.dtype, 3)
+        _check_shape(name, t, ref.shape)
+    _check_shape("lse", lse, (Tq, H))
     L = lib()
     nbytes = L.jfa_bwd_workspace_bytes(B, H, Tq, Tk, D, int(causal))
     ws, wp = _workspace(nbytes, q.device)
@@ -222,6 +235,8 @@ def forward_padded(q, k, v, kv_lens, bias=None, causal: bool = False, out=None, 
     lse = torch.empty((B, Sq, H), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensor("out", out, q.dtype, 4)
     _check_tensor("lse", lse, torch.float32, 3)
+    _check_shape("out", out, q.shape)
+    _check_shape("lse", lse, (B, Sq, H))
     L = lib()
     nbytes = L.jfa_padded_workspace_bytes(B, H, Sq, Sk, D)
     if nbytes == 0:
@@ -236,12 +251,14 @@ def forward_padded(q, k, v, kv_lens, bias=None, causal: bool = False, out=None, 
 def backward_padded(q, k, v, out, lse, dout, bias=None, causal: bool = False, dq=None, dk=None, dv=None):
     """Padded-dense baseline backward (pad rows of q, k, v, dout must be zero); returns (dq, dk, dv)."""
     B, Sq, Sk, H, D = _padded_common(q, k, v, bias)
-    _check_tensor("out", out, q.dtype, 4)
-    _check_tensor("dout", dout, q.dtype, 4)
     _check_tensor("lse", lse, torch.float32, 3)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("out", out, q), ("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(name, t, q.dtype, 4)
+        _check_shape(name, t, ref.shape)
+    _check_shape("lse", lse, (B, Sq, H))
     L = lib()
     nbytes = L.jfa_padded_workspace_bytes(B, H, Sq, Sk, D)
     if nbytes == 0:
