@@ -138,6 +138,9 @@ __device__ __forceinline__ void plan_pass(const PlanArgs& a, int pi, char* dyn) 
   __shared__ int wsum[2 * kPlanWaves];
   __shared__ int qtotal[kMaxQueues], qstart[kMaxQueues], qcarry[kMaxQueues];
   __shared__ int excl[kPlanThreads];
+  // item writing of one chunk: per thread (group) its first list position, its
+  // sequence and head, and the end of its items in the chunk's thread order
+  __shared__ int wbase[kPlanThreads], wbh[kPlanThreads], wend[kPlanThreads];
 
   const PlanPass p = a.pass[pi];
   const PlanGeom pg = plan_geom(p);
@@ -246,8 +249,9 @@ __device__ __forceinline__ void plan_pass(const PlanArgs& a, int pi, char* dyn) 
 
   // 4. positions inside each queue, chunk by chunk. Thread tid of a chunk
   //    handles the i-th group of queue x in that chunk, so that each queue's
-  //    groups are contiguous in one block scan, and writes that group's
-  //    items.
+  //    groups are contiguous in one block scan. With many groups each thread
+  //    writes its group's items; with few (a few long sequences) every thread
+  //    writes items of the chunk, so that most threads are not left idle.
   const int per_q = kPlanThreads / NQ;  // groups of one queue in a chunk of kPlanThreads groups
   const int x = tid / per_q, i = tid % per_q;
   for (int c0 = 0; c0 < G; c0 += kPlanThreads) {
@@ -266,15 +270,41 @@ __device__ __forceinline__ void plan_pass(const PlanArgs& a, int pi, char* dyn) 
     if (p.gfirst && n > 0) p.gfirst[b * H + g % H] = (int)gbase;  // chunk 0 is first (costs non-increasing)
     __syncthreads();
     if (i == per_q - 1) qcarry[x] += pos + n;  // last group of queue x in this chunk
-    // The thread writes its group's items.
-    if (n > 0) {
-      const int h = g % H, Lq = lq_s[b], Lk = lk_s[b];
-      for (int t = 0; t < n; ++t) {
-        const long at = gbase + plan_pos(Lq, Lk, t, n, pg, a.causal);
-        if (at >= 0 && at < p.capacity) p.items[at] = make_int4(b, h, t, plan_cost(Lq, Lk, t, pg, a.causal));
+    if (G - c0 >= kPlanThreads / 4) {
+      // Many groups: each thread writes its own group's items.
+      if (n > 0) {
+        const int h = g % H, Lq = lq_s[b], Lk = lk_s[b];
+        for (int t = 0; t < n; ++t) {
+          const long at = gbase + plan_pos(Lq, Lk, t, n, pg, a.causal);
+          if (at >= 0 && at < p.capacity) p.items[at] = make_int4(b, h, t, plan_cost(Lq, Lk, t, pg, a.causal));
+        }
       }
+      __syncthreads();  // qcarry of the next chunk
+      continue;
     }
-    __syncthreads();  // qcarry of the next chunk
+    // Few groups (a few long sequences): all threads take the chunk's items in
+    // turn. Item y belongs to the thread u whose range [wend[u] - n_u, wend[u])
+    // holds it (a binary search over the inclusive scan), and is tile
+    // y - (wend[u] - n_u) of u's group.
+    wbase[tid] = (int)gbase;
+    wbh[tid] = g < G ? (b << 16) | (g % H) : 0;  // b < 2^13 and h < 2^16 (checked on the host)
+    wend[tid] = ex + n;
+    __syncthreads();
+    for (int y = tid; y < tot; y += kPlanThreads) {
+      int lo = 0, hi = kPlanThreads - 1;  // first u with wend[u] > y
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (wend[mid] > y) hi = mid;
+        else lo = mid + 1;
+      }
+      const int ub = wbh[lo] >> 16, uh = wbh[lo] & 0xFFFF;
+      const int Lq = lq_s[ub], Lk = lk_s[ub];
+      const int un = plan_tiles(Lq, Lk, pg);
+      const int t = y - (wend[lo] - un);
+      const long at = (long)wbase[lo] + plan_pos(Lq, Lk, t, un, pg, a.causal);
+      if (at >= 0 && at < p.capacity) p.items[at] = make_int4(ub, uh, t, plan_cost(Lq, Lk, t, pg, a.causal));
+    }
+    __syncthreads();  // qcarry and the chunk arrays of the next chunk
   }
 }
 
