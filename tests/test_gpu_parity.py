@@ -391,3 +391,46 @@ def test_binding_rejects_wrong_output_shapes():
     with pytest.raises(ValueError, match="shape"):
         jfa.backward(d["q"], d["k"], d["v"], out, lse[:-1], d["dout"], d["q_offsets"], d["kv_offsets"], None, False)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bias", [False, True])
+def test_subtraction_cancellation_guard(D, bias):
+    """Every valid score ~20 below the pad keys' score (0, or the bias): in
+    fp32 the pad terms absorb the valid ones, and subtracting them leaves
+    nothing. The forward then sums the last block's valid terms again; O and
+    lse must match the oracle, and the backward with them."""
+    ql, kl = [4, 70, 9], [5, 70, 130]
+    wl = gen.Workload("cancel", len(ql), 2, D, "bf16", False, bias, gen.LengthDist("fixed", 1, 1), seed=81)
+    batch = gen.make_batch(wl, q_lengths=ql, kv_lengths=kl)
+    a, b = 16.0, (10.0 if D == 64 else 14.0)  # score = -a * b / sqrt(D): -20 (D = 64), -19.8 (D = 128)
+    for s in (0, 2):  # sequences 0 and 2: one block with 59 pad keys; two full blocks and 62 pads
+        qs = slice(batch.q_offsets[s], batch.q_offsets[s + 1])
+        ks = slice(batch.kv_offsets[s], batch.kv_offsets[s + 1])
+        batch.q[qs] = 0.0
+        batch.q[qs, :, 0] = a
+        batch.k[ks, :, 0] = -b
+    batch.q_bits = gen.bf16_round(batch.q)
+    batch.k_bits = gen.bf16_round(batch.k)
+    _check(batch, label=f"cancellation guard D={D} bias={bias}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bias", [False, True])
+def test_subtraction_cancellation_guard_short_query(D, bias):
+    """The same adversarial scores on the key-split forward of short-query
+    sequences (at most 64 queries, more than 1024 keys): the chunk that holds
+    the pad keys is the one that cancels."""
+    ql, kl = [4, 9, 40], [1030, 2050, 1500]
+    wl = gen.Workload("cancel_sq", len(ql), 2, D, "bf16", False, bias, gen.LengthDist("fixed", 1, 1), seed=82)
+    batch = gen.make_batch(wl, q_lengths=ql, kv_lengths=kl)
+    a, b = 16.0, (10.0 if D == 64 else 14.0)
+    for s in (0, 1):
+        qs = slice(batch.q_offsets[s], batch.q_offsets[s + 1])
+        ks = slice(batch.kv_offsets[s], batch.kv_offsets[s + 1])
+        batch.q[qs] = 0.0
+        batch.q[qs, :, 0] = a
+        batch.k[ks, :, 0] = -b
+    batch.q_bits = gen.bf16_round(batch.q)
+    batch.k_bits = gen.bf16_round(batch.k)
+    _check(batch, label=f"short-query cancellation guard D={D} bias={bias}")

@@ -70,8 +70,14 @@ struct FwdTiles {
 // slot is visited, and keys at or past the sequence's true length
 // (a.kv_len[b]) are masked with -inf on every block, element by element, as a
 // conventional kernel over padded tensors does.
+// Resident waves per SIMD the register budget is held to (the compiler's
+// allocation gives bf16 at D <= 64 three).
+template <typename T, int D> constexpr int fwd_min_waves() {
+  return D * sizeof(T) >= 512 ? 1 : 2;
+}
+
 template <typename T, int D, bool BIAS, bool PADDED = false>
-__global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(FwdArgs a) {
   using C = FwdTiles<T, D>;
   constexpr int BM = C::BM, BN = C::BN, ES = (int)sizeof(T);
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
@@ -148,6 +154,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
     float m = kNegInit, l = 0.f;
+    float l_pre = 0.f;  // this half-wave's sum before the item's last block (cancellation guard)
     int last_tile = -1;
     bool last_masked = false;
 
@@ -213,6 +220,7 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
         }
+        if (j + 1 == n_kv) l_pre = l;
         if (plain) {
           const float nm = -m;
 #pragma unroll
@@ -253,13 +261,56 @@ __global__ __launch_bounds__(256, (D * sizeof(T) >= 512 ? 1 : 2)) void jfa_fwd_k
     if (wave_on && last_tile >= 0 && !last_masked) {
       const int pad1 = (last_tile + 1) * BN;
       if (pad1 > Lk) {
+        float pads;
         if (!BIAS) {
-          lt -= (float)(pad1 - Lk) * __builtin_amdgcn_exp2f(-m);
+          pads = (float)(pad1 - Lk) * __builtin_amdgcn_exp2f(-m);
         } else {
           float sub = 0.f;
           for (int kj = Lk + g; kj < pad1; kj += 2)
             sub += __builtin_amdgcn_exp2f(bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius] - m);
-          lt -= sub + other_half(sub);
+          pads = sub + other_half(sub);
+        }
+        const float full = lt;
+        lt -= pads;
+        // Cancellation guard: the subtraction is exact in real arithmetic, but
+        // in fp32 it loses the valid terms when they are tiny next to the pad
+        // terms (every valid score far below the pad keys' score, which is the
+        // bias, or 0). A row whose remainder keeps fewer than ~12 significant
+        // bits gets its last block's valid terms summed again from the K tile
+        // still in LDS, without the pad keys, on top of the sum before that
+        // block. Not taken for unit-scale scores.
+        const bool cancel = !(lt > full * 0x1p-12f);
+        if (__any(cancel)) {
+          const lds_t* kt = lds + (last_tile & 1) * C::STAGE;
+          const int key0 = last_tile * BN;
+          // Plain dot products, one key row of the tile at a time (rare path:
+          // kept small so that it adds nothing to the kernel's registers).
+          float sv = 0.f;
+#pragma unroll 1
+          for (int r = g; r < BN; r += 2) {
+            const int kj = key0 + r;
+            if (kj >= Lk) break;  // keys past the end follow the valid ones
+            float dot = 0.f;
+#pragma unroll 1
+            for (int c = 0; c < C::CPR; ++c) {
+              const i32x4 kq = *(const __attribute__((address_space(3))) i32x4*)(kt + C::TL::chunk(r, c));
+              const i32x4 qq = ld16(qv, (uint32_t)qi * gstride + c * 16);
+              if constexpr (sizeof(T) == 2) {
+                const bf16x8 k8 = __builtin_bit_cast(bf16x8, kq), q8 = __builtin_bit_cast(bf16x8, qq);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot += (float)k8[e] * (float)q8[e];
+              } else {
+                const f32x4 k4 = __builtin_bit_cast(f32x4, kq), q4 = __builtin_bit_cast(f32x4, qq);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dot += k4[e] * q4[e];
+              }
+            }
+            float x = dot * a.scale2;
+            if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+            sv += __builtin_amdgcn_exp2f(x - m);
+          }
+          const float fixed = l_pre + other_half(l_pre) + sv + other_half(sv);
+          if (cancel) lt = fixed;
         }
       }
     }

@@ -144,6 +144,7 @@ __global__ __launch_bounds__(256, 2) void jfa_fsq_kernel(FwdArgs a) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
     float m = kNegInit, l = 0.f;
+    float l_pre = 0.f;  // this half-wave's sum before its latest half-tile (cancellation guard)
     int last_tile = -1;
     bool last_masked = false;
 
@@ -191,6 +192,7 @@ __global__ __launch_bounds__(256, 2) void jfa_fsq_kernel(FwdArgs a) {
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
         }
+        l_pre = l;
         if (plain) {
           const float nm = -m;
 #pragma unroll
@@ -221,18 +223,57 @@ __global__ __launch_bounds__(256, 2) void jfa_fsq_kernel(FwdArgs a) {
     // Row sum over both lane halves; remove the terms of keys past the end.
     float lt = l + other_half(l);
     if (wave_on && last_tile >= 0 && !last_masked) {
-      const int pad1 = kc0 + last_tile * KT + 32 * kh + 32;  // end of this wave's last half-tile
+      const int hk0 = kc0 + last_tile * KT + 32 * kh;  // first key of this wave's last half-tile
+      const int pad1 = hk0 + 32;
       if (pad1 > Lk) {
+        float pads;
         if (!BIAS) {
-          lt -= (float)(pad1 - Lk) * __builtin_amdgcn_exp2f(-m);
+          pads = (float)(pad1 - Lk) * __builtin_amdgcn_exp2f(-m);
         } else {
           float sub = 0.f;
           for (int kj = Lk + g; kj < pad1; kj += 2)
             sub += __builtin_amdgcn_exp2f(bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius] - m);
-          lt -= sub + other_half(sub);
+          pads = sub + other_half(sub);
+        }
+        const float full = lt;
+        lt -= pads;
+        // Cancellation guard, as in the regular forward: when the remainder
+        // keeps fewer than ~12 significant bits, the half-tile's valid terms
+        // are summed again (plain dot products against the K rows still in
+        // LDS) on top of the sum before that half-tile.
+        const bool cancel = !(lt > full * 0x1p-12f);
+        if (__any(cancel)) {
+          const lds_t* kt = lds + (last_tile & 1) * C::STAGE;
+          float sv = 0.f;
+#pragma unroll 1
+          for (int r = g; r < 32; r += 2) {
+            const int kj = hk0 + r;
+            if (kj >= Lk) break;  // keys past the end follow the valid ones
+            float dot = 0.f;
+#pragma unroll 1
+            for (int c = 0; c < C::CPR; ++c) {
+              const i32x4 kq = *(const __attribute__((address_space(3))) i32x4*)(kt + C::TL::chunk(32 * kh + r, c));
+              const i32x4 qq = ld16(qv, (uint32_t)qi * gstride + c * 16);
+              if constexpr (sizeof(T) == 2) {
+                const bf16x8 k8 = __builtin_bit_cast(bf16x8, kq), q8 = __builtin_bit_cast(bf16x8, qq);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot += (float)k8[e] * (float)q8[e];
+              } else {
+                const f32x4 k4 = __builtin_bit_cast(f32x4, kq), q4 = __builtin_bit_cast(f32x4, qq);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dot += k4[e] * q4[e];
+              }
+            }
+            float x = dot * a.scale2;
+            if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+            sv += __builtin_amdgcn_exp2f(x - m);
+          }
+          const float fixed = l_pre + other_half(l_pre) + sv + other_half(sv);
+          if (cancel) lt = fixed;
         }
       }
     }
+    __syncthreads();  // the K tiles are read above; the merge below reuses their LDS
 
     // Merge the two key halves of each query half: (m, l) through LDS, then
     // the key-half-1 wave's weighted O^T, to which its partner adds its own.
