@@ -306,6 +306,7 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="also report workloads 1..5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-padded", action="store_true", help="skip the padded-dense baseline")
+    ap.add_argument("--lib", default=None, help="run another build of the library (study variants)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--bias-grad", action="store_true",
                     help="the backward also returns the bias-table gradient (workloads with a bias)")
@@ -321,6 +322,8 @@ def main(argv=None):
     import torch
     from variable_length_attention_jfa_amd import inputs as gen
     from variable_length_attention_jfa_amd import jfa
+    if args.lib:
+        jfa.LIB_PATH = os.path.abspath(args.lib)
     jfa.lib()
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)

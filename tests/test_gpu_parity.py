@@ -434,3 +434,20 @@ def test_subtraction_cancellation_guard_short_query(D, bias):
     batch.q_bits = gen.bf16_round(batch.q)
     batch.k_bits = gen.bf16_round(batch.k)
     _check(batch, label=f"short-query cancellation guard D={D} bias={bias}")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_unswizzled_lds_variant(cfg):
+    """The bank-conflict study's build (LDS tiles stored unpermuted) reads what
+    it writes in every kernel: forward and backward still match the oracle."""
+    path = os.path.join(os.path.dirname(jfa.LIB_PATH), "_study", "libjfa_noswz.so")
+    if not os.path.exists(path):
+        pytest.skip("study variant not built (__graft_entry__.build())")
+    saved = jfa.LIB_PATH
+    try:
+        jfa._LIB = None
+        jfa.LIB_PATH = path
+        _check(gen.make_batch(SMALL[cfg]), label=f"unswizzled LDS cfg{cfg}")
+    finally:
+        jfa._LIB = None
+        jfa.LIB_PATH = saved

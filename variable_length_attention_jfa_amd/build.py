@@ -1,6 +1,6 @@
 """Builds libjfa.so (gfx950) from csrc/ with hipcc, in place.
 
-    python -m variable_length_attention_jfa_amd.build [--jobs N] [--save-temps]
+    python -m variable_length_attention_jfa_amd.build [--jobs N] [--save-temps] [--define N=V --out PATH]
 
 Every source is compiled for gfx950 only, with packed fp32 VALU instructions
 disabled, then linked into variable_length_attention_jfa_amd/libjfa.so.
@@ -62,8 +62,13 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)
     ap.add_argument("--save-temps", action="store_true")
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="extra preprocessor definition (study variants, e.g. JFA_LDS_SWIZZLE=0)")
+    ap.add_argument("--out", default=LIB, help="library path (default: the package's libjfa.so)")
     args = ap.parse_args(argv)
-    build(args.jobs, args.save_temps)
+    out = os.path.abspath(args.out)
+    objdir = BUILD if out == LIB else os.path.join(BUILD, os.path.splitext(os.path.basename(out))[0])
+    build(args.jobs, args.save_temps, defines=args.define, out=out, objdir=objdir)
     return 0
 
 

@@ -115,11 +115,18 @@ __device__ __forceinline__ Frag<float> gfrag(const View& v, uint32_t off, float*
 //   * transposing reads (32 lanes per cycle, 4 consecutive rows x 64 bytes),
 //   * 16-byte staging writes (whole rows)
 // each touch every bank at most once per cycle.
+// Chunk permutation of the LDS tiles: 1 (the library) XORs each row's
+// 16-byte chunk index with a function of the row so that the MFMA operand
+// reads spread over the banks; 0 exists only for a bank-conflict study.
+#ifndef JFA_LDS_SWIZZLE
+#define JFA_LDS_SWIZZLE 1
+#endif
 template <typename T, int D>
 struct Tile {
   static constexpr int ROWB = D * (int)sizeof(T);
   static constexpr int CPR = ROWB / 16;
   __device__ __forceinline__ static int swz(int r) {
+    if constexpr (!JFA_LDS_SWIZZLE) return 0;  // swizzle study only: rows stored unpermuted
     if constexpr (CPR >= 16) return 4 * (r & 3) + ((r >> 2) & 3);
     else if constexpr (CPR == 8) return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
     else return (r >> 2) & 3;
