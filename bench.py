@@ -17,7 +17,9 @@ timed steps; `cpu_baseline` times the fp64 CPU oracle on a bounded sample of
 the same workload on the host cores; `padded_baseline` runs the same batch
 copied into zeroed slots of the longest sequence's length through the
 library's padded-dense kernels (a -inf key mask on every block, every block
-visited) and gives the jagged path's speedup and memory ratio over it.
+visited) and gives the jagged path's speedup and memory ratio over it;
+`cold_cache` times single steps after a 512 MiB write that empties the L2
+and Infinity Cache (median, p10, p90), next to the warm back-to-back `value`.
 """
 from __future__ import annotations
 
@@ -96,7 +98,28 @@ KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "fsq": 4, "dkdv": 8, "dq": 6, "sq": 10}
 KERNEL_SEQS = {"forward": "long", "fsq": "short", "dkdv": "long", "dq": "long", "sq": "short"}
 
 
-def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None, bias_grad=False, padded_steps=0):
+def cold_cache_steps(step, n, torch, flush_mib=512):
+    """Per-step times with the caches emptied before each step: a write of
+    flush_mib MiB (more than the 4 MB L2 of each XCD plus the 256 MB Infinity
+    Cache) outside the events, then one step between two events on the
+    current stream. Returns (median, p10, p90) in ms."""
+    buf = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
+    times = []
+    for i in range(n):
+        buf.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    del buf
+    t = np.sort(np.array(times))
+    return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+
+def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None, bias_grad=False, padded_steps=0,
+                 cold_steps=0):
     wl = gen.WORKLOADS[idx]
     batch = gen.make_batch(wl, seed=seed)
     dev = torch.device("cuda")
@@ -144,6 +167,7 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None,
     jfa.timing_enable(False)
     kt = jfa.timing_collect()
 
+    cold = cold_cache_steps(step, cold_steps, torch) if cold_steps > 0 else None
     pairs = valid_pairs(batch.q_lengths, batch.kv_lengths, wl.causal)
     fwd_flops = 4.0 * wl.D * wl.H * pairs
     bwd_flops = 10.0 * wl.D * wl.H * pairs
@@ -164,6 +188,9 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None,
         "bwd_tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12,
         "kernel_avg_ms": {k_: per[k_][0] for k_ in per if per[k_][1] > 0},
     }
+    if cold is not None:
+        res["cold_cache"] = {"steps": cold_steps, "flush_mib": 512, "median_ms": cold[0], "p10_ms": cold[1],
+                             "p90_ms": cold[2], "tflops_median": (fwd_flops + bwd_flops) / (cold[0] * 1e-3) / 1e12}
     peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_BF16_TFLOPS
     res["fwd_pct_peak"] = 100.0 * res["fwd_tflops"] / peak
     res["bwd_pct_peak"] = 100.0 * res["bwd_tflops"] / peak
@@ -344,7 +371,7 @@ def main(argv=None):
         return 2
     pad_steps = 0 if args.no_padded else max(3, min(20, args.steps // 10))
     main_res = run_workload(args.workload, args.steps, args.warmup, torch, jfa, gen, bias_grad=args.bias_grad,
-                            padded_steps=pad_steps)
+                            padded_steps=pad_steps, cold_steps=max(5, min(50, args.steps // 6)))
     pb = main_res.get("padded_baseline")
     print(f"[bench] workload {args.workload}: {main_res['tflops_step']:.1f} TFLOP/s fwd+bwd, "
           f"fwd {main_res['fwd_tflops']:.1f} bwd {main_res['bwd_tflops']:.1f}"
@@ -396,6 +423,7 @@ def main(argv=None):
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
         "padded_baseline": main_res.get("padded_baseline"),
+        "cold_cache": main_res.get("cold_cache"),
         "other_workloads": extras,
     }
     print(json.dumps(line))
