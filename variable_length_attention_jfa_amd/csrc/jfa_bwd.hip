@@ -37,6 +37,13 @@
 
 namespace jfa {
 
+// P handed from score wave to gradient wave in bf16 (bf16 inputs) or fp32.
+#ifndef JFA_P_BF16
+#define JFA_P_BF16 1
+#endif
+template <typename T> constexpr bool kPHalf = JFA_P_BF16 && sizeof(T) == 2;
+
+
 
 
 // ---------------------------------------------------------------------------
@@ -213,17 +220,22 @@ __device__ __forceinline__ void dkv_score_role(const BwdArgs& a, lds_t* lds, Que
         };
         if (masked) softmax(std::true_type{});
         else softmax(std::false_type{});
-        // handed to the gradient wave of the pair in fp32, lane order
+        // handed to the gradient wave of the pair, lane order: for bf16 inputs
+        // the bf16 fragments the dV product takes anyway (half the LDS bytes),
+        // for fp32 inputs fp32
         lds_t* pb = lds + C::PBUF + ((jb & 1) * C::PAIRS + pair) * C::PBLK;
+        if constexpr (!kPHalf<T>) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *(__attribute__((address_space(3))) f32x4*)(pb + 1024 * e + 16 * lane) =
-              (f32x4){sc[4 * e], sc[4 * e + 1], sc[4 * e + 2], sc[4 * e + 3]};
+          for (int e = 0; e < 4; ++e)
+            *(__attribute__((address_space(3))) f32x4*)(pb + 1024 * e + 16 * lane) =
+                (f32x4){sc[4 * e], sc[4 * e + 1], sc[4 * e + 2], sc[4 * e + 3]};
+        }
         // dV^T += dO^T P^T
         const lds_t* dot = qt + C::QTILE;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const Frag<T> pf = rfrag(sc, c, (T*)0);
+          if constexpr (kPHalf<T>) put_frag(pb + 1024 * c, pf, lane);
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) mma(dv[db], tfrag<D>(dot, 16 * c, 32 * db, lane, (T*)0), pf);
         }
@@ -299,13 +311,22 @@ __device__ __forceinline__ void dkv_grad_role(const BwdArgs& a, lds_t* lds, Queu
         for (int kk = 0; kk < D / 16; ++kk) mma(dp, lfrag<D>(dot, l32, 16 * kk + 8 * g, (T*)0), vf[kk]);
         const lds_t* pb = lds + C::PBUF + ((jp & 1) * C::PAIRS + pair) * C::PBLK;
         f32x16 p;
+        if constexpr (kPHalf<T>) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const f32x4 x = *(const __attribute__((address_space(3))) f32x4*)(pb + 1024 * e + 16 * lane);
-          p[4 * e] = x[0];
-          p[4 * e + 1] = x[1];
-          p[4 * e + 2] = x[2];
-          p[4 * e + 3] = x[3];
+          for (int c = 0; c < 2; ++c) {
+            const bf16x8 x = __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) i32x4*)(pb + 1024 * c + 16 * lane));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[8 * c + e] = (float)x[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f32x4 x = *(const __attribute__((address_space(3))) f32x4*)(pb + 1024 * e + 16 * lane);
+            p[4 * e] = x[0];
+            p[4 * e + 1] = x[1];
+            p[4 * e + 2] = x[2];
+            p[4 * e + 3] = x[3];
+          }
         }
         // dS = P (dP - Delta)
 #pragma unroll
