@@ -97,7 +97,9 @@ size_t jfa_bwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, 
  * rows are never written outside their sequence. The softmax scale is
  * 1/sqrt(D). Jagged edges are handled by zero-filled loads and a subtraction
  * of the extra exponent terms ("Jagged Flash Attention (JFA)", section "Four
- * generations", item 1); work is scheduled longest-first over persistent
+ * generations", item 1); a row whose valid terms the fp32 subtraction would
+ * cancel (every valid score far below the pad keys' score) has its last
+ * block's valid terms summed again instead. Work is scheduled longest-first over persistent
  * workgroups (same section, item 3). A sequence with at most 64 queries and
  * more than 1024 keys is split over its keys instead, one workgroup per
  * chunk of 1024 keys; each chunk's rows, normalised over its keys, and their
