@@ -239,7 +239,7 @@ def run_padded(batch, d, steps, jfa_ms, jfa_fwd_ms, jfa_bwd_ms, torch, jfa):
 
     def step():
         jfa.forward_padded(qp, kp, vp, kv_lens, d["bias"], wl.causal, out=outp, lse=lsep)
-        jfa.backward_padded(qp, kp, vp, outp, lsep, dop, d["bias"], wl.causal, dq=dqp, dk=dkp, dv=dvp)
+        jfa.backward_padded(qp, kp, vp, outp, lsep, dop, kv_lens, d["bias"], wl.causal, dq=dqp, dk=dkp, dv=dvp)
 
     for _ in range(2):
         step()

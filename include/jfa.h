@@ -162,16 +162,14 @@ jfa_status jfa_bwd_f32(const void* q, const void* k, const void* v, const void* 
  * every block, as a conventional kernel over padded tensors does; the causal
  * mask and the bias are those of jfa_fwd. Rows of out and lse that lie past a
  * sequence's true query length are computed like any other row and are the
- * caller's to ignore. The backward visits every block as well. It needs the
- * rows of q, k, v and dout past each sequence's true lengths to be zero (as a
- * jagged batch copied into zeroed slots has them) and the lse of
- * jfa_fwd_padded: then every product that involves a pad row is zero, and the
- * rows of dq, dk, dv inside the true lengths are exact. It applies no key
- * mask of its own, so it is no slower than a conventional masked backward.
- * Without that mask, a pad key's P = exp(bias - lse) overflows fp32 for a
- * row whose lse lies more than ~88 below the pad score, and dq of that row is
- * then not finite; inputs with unit-scale scores are far from this.
- * The softmax scale is 1/sqrt(D); no bias gradient. B * q_slot and
+ * caller's to ignore. The backward visits every block as well; its dQ pass
+ * masks keys j >= kv_lens[b] element by element on the blocks that hold them.
+ * It needs the rows of q, k, v and dout past each sequence's true lengths to
+ * be zero (as a jagged batch copied into zeroed slots has them) and the lse
+ * of jfa_fwd_padded: then every product of the dK/dV pass that involves a
+ * pad row is zero, and the rows of dq, dk, dv inside the true lengths are
+ * exact (that pass applies no mask, so it is no slower than a conventional
+ * masked one). The softmax scale is 1/sqrt(D); no bias gradient. B * q_slot and
  * B * kv_slot must be below 2^31. Workspace: jfa_padded_workspace_bytes, for
  * either pass. Same ownership, asynchrony and error rules as jfa_fwd. */
 size_t jfa_padded_workspace_bytes(int B, int H, int q_slot, int kv_slot, int D);
@@ -179,9 +177,9 @@ jfa_status jfa_fwd_padded(const void* q, const void* k, const void* v, const int
                           int kv_slot, int H, int D, const float* bias, int causal, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);
 jfa_status jfa_bwd_padded(const void* q, const void* k, const void* v, const void* out, const float* lse,
-                          const void* dout, int B, int q_slot, int kv_slot, int H, int D, const float* bias,
-                          int causal, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                          void* stream);
+                          const void* dout, const int32_t* kv_lens, int B, int q_slot, int kv_slot, int H, int D,
+                          const float* bias, int causal, void* dq, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* offsets[0] = 0, offsets[b+1] = offsets[b] + lengths[b] for b < B (device
  * int32 arrays, lengths [B], offsets [B+1]); the prefix-sum addressing of
@@ -238,7 +236,7 @@ const char* jfa_last_error(void);
 
 /* Version of the argument lists above; a binding compares it with the one it
  * was written for before calling anything else. */
-#define JFA_ABI_VERSION 3
+#define JFA_ABI_VERSION 4
 int jfa_abi_version(void);
 
 #ifdef __cplusplus

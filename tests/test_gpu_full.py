@@ -63,7 +63,7 @@ def test_full_workload_padded_baseline_sampled_parity(cfg):
     kp, vp = padded.to_slots(d["k"], ko, kv_slot), padded.to_slots(d["v"], ko, kv_slot)
     kv_lens = torch.from_numpy(batch.kv_lengths.astype(np.int32)).cuda()
     out_p, lse_p = jfa.forward_padded(qp, kp, vp, kv_lens, d["bias"], wl.causal)
-    dq_p, dk_p, dv_p = jfa.backward_padded(qp, kp, vp, out_p, lse_p, dop, d["bias"], wl.causal)
+    dq_p, dk_p, dv_p = jfa.backward_padded(qp, kp, vp, out_p, lse_p, dop, kv_lens, d["bias"], wl.causal)
     torch.cuda.synchronize()
     out, lse = padded.from_slots(out_p, qo), padded.from_slots(lse_p, qo)
     dq, dk, dv = padded.from_slots(dq_p, qo), padded.from_slots(dk_p, ko), padded.from_slots(dv_p, ko)

@@ -25,7 +25,7 @@ def _check_padded(batch, label, extra_slot=0):
     kp, vp = padded.to_slots(d["k"], ko, kv_slot), padded.to_slots(d["v"], ko, kv_slot)
     kv_lens = torch.from_numpy(batch.kv_lengths.astype(np.int32)).cuda()
     out_p, lse_p = jfa.forward_padded(qp, kp, vp, kv_lens, d["bias"], wl.causal)
-    dq_p, dk_p, dv_p = jfa.backward_padded(qp, kp, vp, out_p, lse_p, dop, d["bias"], wl.causal)
+    dq_p, dk_p, dv_p = jfa.backward_padded(qp, kp, vp, out_p, lse_p, dop, kv_lens, d["bias"], wl.causal)
     torch.cuda.synchronize()
     out, lse = padded.from_slots(out_p, qo), padded.from_slots(lse_p, qo)
     dq, dk, dv = padded.from_slots(dq_p, qo), padded.from_slots(dk_p, ko), padded.from_slots(dv_p, ko)
@@ -69,3 +69,21 @@ def test_padded_sequence_without_keys():
     ql, kl = [3, 40, 7], [0, 50, 0]
     wl = gen.Workload("pad0", len(ql), 2, 64, "bf16", False, False, gen.LengthDist("fixed", 1, 1), seed=72)
     _check_padded(gen.make_batch(wl, q_lengths=ql, kv_lengths=kl), "zero keys", extra_slot=10)
+
+
+def test_padded_backward_very_negative_scores():
+    """Every valid score ~20 below the pad keys' score: a pad key's P =
+    exp(-lse) is ~e^18 there, and the dQ pass must drop the pad keys (it masks
+    them at kv_lens) for dQ to stay finite and exact."""
+    ql, kl = [4, 70, 9], [5, 70, 130]
+    wl = gen.Workload("pad_neg", len(ql), 2, 64, "bf16", False, False, gen.LengthDist("fixed", 1, 1), seed=83)
+    batch = gen.make_batch(wl, q_lengths=ql, kv_lengths=kl)
+    for s in (0, 2):
+        qs = slice(batch.q_offsets[s], batch.q_offsets[s + 1])
+        ks = slice(batch.kv_offsets[s], batch.kv_offsets[s + 1])
+        batch.q[qs] = 0.0
+        batch.q[qs, :, 0] = 16.0
+        batch.k[ks, :, 0] = -10.0
+    batch.q_bits = gen.bf16_round(batch.q)
+    batch.k_bits = gen.bf16_round(batch.k)
+    _check_padded(batch, "very negative scores", extra_slot=200)

@@ -97,6 +97,9 @@ def test_padded_baseline_host_checks(L):
     st = L.jfa_fwd_padded(dummy, dummy, dummy, None, 2, 8, 8, 2, 64, None, 0, dummy, dummy, dummy, 1 << 20, None)
     assert st == 1 and b"kv_lens" in L.jfa_last_error()
     ws = ctypes.c_void_p(4096 * 16)
-    st = L.jfa_bwd_padded(dummy, dummy, dummy, dummy, dummy, dummy, 2, 8, 8, 2, 64, None, 0, dummy, dummy, dummy, ws,
-                          64, None)
+    st = L.jfa_bwd_padded(dummy, dummy, dummy, dummy, dummy, dummy, dummy, 2, 8, 8, 2, 64, None, 0, dummy, dummy, dummy,
+                          ws, 64, None)
     assert st == 2 and b"workspace too small" in L.jfa_last_error()
+    st = L.jfa_bwd_padded(dummy, dummy, dummy, dummy, dummy, dummy, None, 2, 8, 8, 2, 64, None, 0, dummy, dummy, dummy,
+                          ws, 1 << 20, None)
+    assert st == 1 and b"kv_lens" in L.jfa_last_error()

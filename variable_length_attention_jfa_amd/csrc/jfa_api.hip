@@ -271,7 +271,8 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
 jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const void* out, const float* lse,
                     const void* dout, const int32_t* qo, const int32_t* ko, int B, int H, int D, int64_t tq,
                     int64_t tk, int max_kv_len, const float* bias, int causal, void* dq, void* dk, void* dv,
-                    float* dbias, void* ws, size_t ws_bytes, void* stream, bool padded = false) {
+                    float* dbias, void* ws, size_t ws_bytes, void* stream, const int32_t* pad_kv_len = nullptr) {
+  const bool padded = pad_kv_len != nullptr;
   jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, max_kv_len, bias, ws);
   if (s != JFA_OK) return s;
   if (f32 && D > 64) return fail(JFA_ERR_UNSUPPORTED, "fp32 tensors support D = 32 or 64");
@@ -339,6 +340,7 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a.dbp_sq = (float*)(w + L.dbp_sq);
   a.dbpart = (float*)(w + L.dbpart);
   a.dbias = dbias;
+  a.kv_len = pad_kv_len;
   jfa::BwdArgs a_kv = a, a_q = a, a_sq = a;
   a_kv.items = (const int4*)(w + L.items_kv);
   a_kv.hdr = (PlanHeader*)(w + L.hdr_kv);
@@ -483,9 +485,11 @@ jfa_status jfa_fwd_padded(const void* q, const void* k, const void* v, const int
 }
 
 jfa_status jfa_bwd_padded(const void* q, const void* k, const void* v, const void* out, const float* lse,
-                          const void* dout, int B, int q_slot, int kv_slot, int H, int D, const float* bias,
-                          int causal, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+                          const void* dout, const int32_t* kv_lens, int B, int q_slot, int kv_slot, int H, int D,
+                          const float* bias, int causal, void* dq, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!kv_lens || !aligned(kv_lens, 4)))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "kv_lens must be non-NULL and 4-byte aligned");
   char* rest = nullptr;
   size_t rest_bytes = 0;
   jfa_status s = padded_setup(B, H, q_slot, kv_slot, D, workspace, workspace_bytes, stream, &rest, &rest_bytes);
@@ -493,7 +497,7 @@ jfa_status jfa_bwd_padded(const void* q, const void* k, const void* v, const voi
   const int32_t* qo = (const int32_t*)workspace;
   const int32_t* ko = (const int32_t*)((char*)workspace + align_up((size_t)(B + 1) * 4));
   return bwd_impl(false, q, k, v, out, lse, dout, qo, ko, B, H, D, (int64_t)B * q_slot, (int64_t)B * kv_slot, 0,
-                  bias, causal, dq, dk, dv, nullptr, rest, rest_bytes, stream, true);
+                  bias, causal, dq, dk, dv, nullptr, rest, rest_bytes, stream, B > 0 ? kv_lens : nullptr);
 }
 
 jfa_status jfa_offsets_from_lengths(const int32_t* lengths, int B, int32_t* offsets, void* stream) {

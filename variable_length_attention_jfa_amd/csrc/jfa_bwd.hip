@@ -652,6 +652,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
     const int k0 = a.kv_off[b], Lk = a.kv_off[b + 1] - k0;
     const int row0 = qt * BM;
     const int n_kv = a.causal ? cdiv(min(min(row0 + BM, Lq), Lk), BN) : cdiv(Lk, BN);
+    // keys at or past Lm are dropped (the padded-dense baseline's true key count)
+    const int Lm = a.kv_len ? min(max(a.kv_len[b], 0), Lk) : Lk;
 
     const size_t qrow = ((size_t)q0 * H + h) * C::ROWB, krow = ((size_t)k0 * H + h) * C::ROWB;
     const View qv = seq_view((const char*)a.q + qrow, Lq, gstride, C::ROWB);
@@ -700,8 +702,9 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
         const bool masked = a.causal && (key0 + BN - 1 > wr0);
         // Pad keys have K = V = 0, but P there is exp(bias - lse), which can
         // overflow for a row whose lse is very negative; 0 * inf would then
-        // leak into dQ through the zero K row. Drop them on the last block.
-        const bool padded = key0 + BN > Lk;
+        // leak into dQ through the zero K row. Drop them on the block(s) that
+        // hold them.
+        const bool padded = key0 + BN > Lm;
         const lds_t* kt = lds + s * C::STAGE;
         const lds_t* vt = kt + C::KTILE;
         // For D <= 64 the dP accumulation starts at -Delta (this lane's query),
@@ -731,7 +734,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
               float x = sc[kb][i] * a.scale2 - lse2;
               if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
               float p = __builtin_amdgcn_exp2f(x);
-              if (decltype(edge_c)::value && ((masked && kj > qi) || (padded && kj >= Lk))) p = 0.f;
+              if (decltype(edge_c)::value && ((masked && kj > qi) || (padded && kj >= Lm))) p = 0.f;
               dp[kb][i] = p * (kNegDelta ? dp[kb][i] : dp[kb][i] - dlt);
             }
           }
@@ -745,7 +748,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
               float x = sc[kb][i] * a.scale2 - lse2;
               if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
               float p = __builtin_amdgcn_exp2f(x);
-              if ((masked && kj > qi) || (padded && kj >= Lk)) p = 0.f;
+              if ((masked && kj > qi) || (padded && kj >= Lm)) p = 0.f;
               dp[kb][i] = p * (dp[kb][i] - dlt);
             }
           }

@@ -60,6 +60,7 @@ struct BwdArgs {
   int* gfirst_kv;
   float* dbpart;       // [ceil(B / kDbSeqBlock)][H][257]: sums over blocks of sequences
   float* dbias;        // [H][257] fp32 output
+  const int* kv_len;   // padded-dense baseline only: [B] true key count of each fixed-length slot
 };
 
 // Bias gradient: sequences per block of its first summing step.

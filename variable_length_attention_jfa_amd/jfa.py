@@ -28,7 +28,7 @@ KERNEL_FWD, KERNEL_BWD_DKDV, KERNEL_BWD_DQ, KERNEL_BWD_SQ, KERNEL_FWD_SQ = 0, 1,
 SQ_KERNELS = (KERNEL_BWD_SQ, KERNEL_FWD_SQ)  # short-query chunk lists (one list, two passes)
 DTYPE_BF16, DTYPE_F32 = 0, 1
 BIAS_RADIUS = 128
-ABI_VERSION = 3  # JFA_ABI_VERSION of include/jfa.h
+ABI_VERSION = 4  # JFA_ABI_VERSION of include/jfa.h
 WORKSPACE_ALIGN = 256
 PLAN_HEADER_BYTES = 2048
 PLAN_QUEUES = 8
@@ -52,8 +52,8 @@ _SIGS = {
                            _vp, _vp, _vp, _f32p, _vp, _sz, _vp]),
     "jfa_padded_workspace_bytes": (_sz, [_int, _int, _int, _int, _int]),
     "jfa_fwd_padded": (_int, [_vp, _vp, _vp, _i32p, _int, _int, _int, _int, _int, _f32p, _int, _vp, _f32p, _vp, _sz, _vp]),
-    "jfa_bwd_padded": (_int, [_vp, _vp, _vp, _vp, _f32p, _vp, _int, _int, _int, _int, _int, _f32p, _int, _vp, _vp, _vp,
-                              _vp, _sz, _vp]),
+    "jfa_bwd_padded": (_int, [_vp, _vp, _vp, _vp, _f32p, _vp, _i32p, _int, _int, _int, _int, _int, _f32p, _int, _vp,
+                              _vp, _vp, _vp, _sz, _vp]),
     "jfa_offsets_from_lengths": (_int, [_i32p, _int, _i32p, _vp]),
     "jfa_tile_config": (_int, [_int, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
     "jfa_build_plan": (_int, [_i32p, _i32p, _int, _int, _int, _int, _int, _int, _vp, _sz, _vp]),
@@ -248,9 +248,12 @@ def forward_padded(q, k, v, kv_lens, bias=None, causal: bool = False, out=None, 
     return out, lse
 
 
-def backward_padded(q, k, v, out, lse, dout, bias=None, causal: bool = False, dq=None, dk=None, dv=None):
+def backward_padded(q, k, v, out, lse, dout, kv_lens, bias=None, causal: bool = False, dq=None, dk=None, dv=None):
     """Padded-dense baseline backward (pad rows of q, k, v, dout must be zero); returns (dq, dk, dv)."""
     B, Sq, Sk, H, D = _padded_common(q, k, v, bias)
+    _check_tensor("kv_lens", kv_lens, torch.int32, 1)
+    if kv_lens.numel() != B:
+        raise ValueError("kv_lens must have B entries")
     _check_tensor("lse", lse, torch.float32, 3)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -264,7 +267,8 @@ def backward_padded(q, k, v, out, lse, dout, bias=None, causal: bool = False, dq
     if nbytes == 0:
         raise ValueError("invalid padded sizes")
     ws, wp = _workspace(nbytes, q.device)
-    st = L.jfa_bwd_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), B, Sq, Sk, H, D, _ptr(bias),
+    st = L.jfa_bwd_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(kv_lens), B, Sq, Sk, H, D,
+                          _ptr(bias),
                           int(causal), _ptr(dq), _ptr(dk), _ptr(dv), ctypes.c_void_p(wp), nbytes, _stream())
     _check("jfa_bwd_padded", st)
     return dq, dk, dv
