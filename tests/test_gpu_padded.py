@@ -32,8 +32,6 @@ def _check_padded(batch, label, extra_slot=0):
     tol = tol_for(batch)
     e_o, e_l, _, _ = compare_forward(batch, out, lse)
     r = compare_backward(batch, dq, dk, dv)
-    print(f"   fwd max|dO| beyond rounding={e_o:.3e} max|dlse|={e_l:.3e} bwd relL2 {r[0]:.2e}/{r[1]:.2e}/{r[2]:.2e}",
-          flush=True)
     assert e_o <= tol["out"] and e_l <= tol["lse"]
     assert max(r) <= tol["grad"], r
     assert torch.isfinite(dq.float()).all() and torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all()

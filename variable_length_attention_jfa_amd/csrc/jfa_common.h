@@ -201,6 +201,25 @@ __device__ __forceinline__ Frag<float> rfrag(const f32x16& s, int c, float*) {
   return f;
 }
 
+// Sum of the 8 values of a fragment added to acc, in the fragment's own
+// precision: for bf16 the rounded values the matrix product consumes (two per
+// v_dot2c_f32_bf16 against a pair of ones, fp32 accumulation).
+__device__ __forceinline__ float frag_sum(const Frag<bf16>& f, float acc) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){f.v[2 * e], f.v[2 * e + 1]}, one, acc, false);
+  return acc;
+}
+__device__ __forceinline__ float frag_sum(const Frag<float>& f, float acc) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc += f.lo[e] + f.hi[e];
+  return acc;
+}
+// The value a bf16 operand carries for x (round to nearest even), as fp32.
+__device__ __forceinline__ float as_operand(float x, bf16*) { return (float)(bf16)x; }
+__device__ __forceinline__ float as_operand(float x, float*) { return x; }
+
 // A whole-wave fragment parked in LDS (16 bytes per lane per 1 KB piece, lane
 // order), for handing an operand from one wave to another.
 __device__ __forceinline__ void put_frag(lds_t* p, const Frag<bf16>& f, int lane) {

@@ -153,8 +153,13 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
-    float m = kNegInit, l = 0.f;
-    float l_pre = 0.f;  // this half-wave's sum before the item's last block (cancellation guard)
+    // Two running sums per half-wave: l over the fp32 P (for lse) and lb over
+    // the bf16-rounded P the PV product consumes (O is normalised by it, so
+    // the weights applied to V sum to 1; a row with one key gets O = V
+    // exactly, which keeps the backward's Delta = dO . O consistent with dP).
+    constexpr bool kOpSum = sizeof(T) == 2;
+    float m = kNegInit, l = 0.f, lb = 0.f;
+    float l_pre = 0.f, lb_pre = 0.f;  // sums before the item's last block (cancellation guard)
     int last_tile = -1;
     bool last_masked = false;
 
@@ -217,10 +222,14 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
           const float alpha = __builtin_amdgcn_exp2f(m - mn);
           m = mn;
           l *= alpha;
+          lb *= alpha;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
         }
-        if (j + 1 == n_kv) l_pre = l;
+        if (j + 1 == n_kv) {
+          l_pre = l;
+          lb_pre = lb;
+        }
         if (plain) {
           const float nm = -m;
 #pragma unroll
@@ -247,6 +256,7 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
 #pragma unroll
         for (int kc = 0; kc < BN / 16; ++kc) {
           const Frag<T> pf = rfrag(sc[kc >> 1], kc & 1, (T*)0);
+          if constexpr (kOpSum) lb = frag_sum(pf, lb);
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) mma(o[db], tfrag<D>(vt, 16 * kc, 32 * db, lane, (T*)0), pf);
         }
@@ -256,22 +266,32 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
       __syncthreads();
     }
 
-    // Epilogue: combine the two half-wave partial sums, remove the pad terms.
+    // Epilogue: combine the two half-wave partial sums, remove the pad terms
+    // (from both sums, each as it was added: the bf16 sum took them rounded).
     float lt = l + other_half(l);
+    float lbt = kOpSum ? lb + other_half(lb) : lt;
     if (wave_on && last_tile >= 0 && !last_masked) {
       const int pad1 = (last_tile + 1) * BN;
       if (pad1 > Lk) {
-        float pads;
+        float pads, pads_b;
         if (!BIAS) {
-          pads = (float)(pad1 - Lk) * __builtin_amdgcn_exp2f(-m);
+          const float pe = __builtin_amdgcn_exp2f(-m);
+          pads = (float)(pad1 - Lk) * pe;
+          pads_b = (float)(pad1 - Lk) * as_operand(pe, (T*)0);
         } else {
-          float sub = 0.f;
-          for (int kj = Lk + g; kj < pad1; kj += 2)
-            sub += __builtin_amdgcn_exp2f(bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius] - m);
+          float sub = 0.f, subb = 0.f;
+          for (int kj = Lk + g; kj < pad1; kj += 2) {
+            const float pe =
+                __builtin_amdgcn_exp2f(bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius] - m);
+            sub += pe;
+            subb += as_operand(pe, (T*)0);
+          }
           pads = sub + other_half(sub);
+          pads_b = subb + other_half(subb);
         }
         const float full = lt;
         lt -= pads;
+        lbt -= pads_b;
         // Cancellation guard: the subtraction is exact in real arithmetic, but
         // in fp32 it loses the valid terms when they are tiny next to the pad
         // terms (every valid score far below the pad keys' score, which is the
@@ -285,7 +305,7 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
           const int key0 = last_tile * BN;
           // Plain dot products, one key row of the tile at a time (rare path:
           // kept small so that it adds nothing to the kernel's registers).
-          float sv = 0.f;
+          float sv = 0.f, svb = 0.f;
 #pragma unroll 1
           for (int r = g; r < BN; r += 2) {
             const int kj = key0 + r;
@@ -307,15 +327,21 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
             }
             float x = dot * a.scale2;
             if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
-            sv += __builtin_amdgcn_exp2f(x - m);
+            const float pe = __builtin_amdgcn_exp2f(x - m);
+            sv += pe;
+            svb += as_operand(pe, (T*)0);
           }
           const float fixed = l_pre + other_half(l_pre) + sv + other_half(sv);
-          if (cancel) lt = fixed;
+          const float fixedb = kOpSum ? lb_pre + other_half(lb_pre) + svb + other_half(svb) : fixed;
+          if (cancel) {
+            lt = fixed;
+            lbt = fixedb;
+          }
         }
       }
     }
     if (wave_on) {
-      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      const float inv = lbt > 0.f ? 1.0f / lbt : 0.f;
       const View ov = seq_view((char*)a.out + qrow, Lq, gstride, C::ROWB);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {

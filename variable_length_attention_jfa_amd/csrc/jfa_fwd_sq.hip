@@ -58,7 +58,7 @@ struct FsqTiles {
   // Epilogue, in the stage area: the combined O rows, then (m, l) per wave and lane.
   using OL = Tile<float, D>;
   static constexpr int ML_OFF = QM * OL::ROWB;
-  static_assert(ML_OFF + 4 * 32 * 8 <= 2 * STAGE, "epilogue fits the stage area");
+  static_assert(ML_OFF + 4 * 32 * 16 <= 2 * STAGE, "epilogue fits the stage area");
   static_assert((KT * CPR) % THREADS == 0, "tile pieces divide the workgroup");
   static_assert(KC % KT == 0, "chunks are whole tiles");
 };
@@ -143,8 +143,11 @@ __global__ __launch_bounds__(256, 2) void jfa_fsq_kernel(FwdArgs a) {
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
-    float m = kNegInit, l = 0.f;
-    float l_pre = 0.f;  // this half-wave's sum before its latest half-tile (cancellation guard)
+    // l sums the fp32 P (for lse), lb the bf16-rounded P the PV product
+    // consumes (the chunk's rows are normalised by it), as in the regular forward.
+    constexpr bool kOpSum = sizeof(T) == 2;
+    float m = kNegInit, l = 0.f, lb = 0.f;
+    float l_pre = 0.f, lb_pre = 0.f;  // sums before the latest half-tile (cancellation guard)
     int last_tile = -1;
     bool last_masked = false;
 
@@ -189,10 +192,12 @@ __global__ __launch_bounds__(256, 2) void jfa_fsq_kernel(FwdArgs a) {
           const float alpha = __builtin_amdgcn_exp2f(m - mn);
           m = mn;
           l *= alpha;
+          lb *= alpha;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
         }
         l_pre = l;
+        lb_pre = lb;
         if (plain) {
           const float nm = -m;
 #pragma unroll
@@ -212,6 +217,7 @@ __global__ __launch_bounds__(256, 2) void jfa_fsq_kernel(FwdArgs a) {
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
           const Frag<T> pf = rfrag(sc, kc, (T*)0);
+          if constexpr (kOpSum) lb = frag_sum(pf, lb);
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) mma(o[db], tfrag<D>(vt, 32 * kh + 16 * kc, 32 * db, lane, (T*)0), pf);
         }
@@ -222,21 +228,30 @@ __global__ __launch_bounds__(256, 2) void jfa_fsq_kernel(FwdArgs a) {
 
     // Row sum over both lane halves; remove the terms of keys past the end.
     float lt = l + other_half(l);
+    float lbt = kOpSum ? lb + other_half(lb) : lt;
     if (wave_on && last_tile >= 0 && !last_masked) {
       const int hk0 = kc0 + last_tile * KT + 32 * kh;  // first key of this wave's last half-tile
       const int pad1 = hk0 + 32;
       if (pad1 > Lk) {
-        float pads;
+        float pads, pads_b;
         if (!BIAS) {
-          pads = (float)(pad1 - Lk) * __builtin_amdgcn_exp2f(-m);
+          const float pe = __builtin_amdgcn_exp2f(-m);
+          pads = (float)(pad1 - Lk) * pe;
+          pads_b = (float)(pad1 - Lk) * as_operand(pe, (T*)0);
         } else {
-          float sub = 0.f;
-          for (int kj = Lk + g; kj < pad1; kj += 2)
-            sub += __builtin_amdgcn_exp2f(bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius] - m);
+          float sub = 0.f, subb = 0.f;
+          for (int kj = Lk + g; kj < pad1; kj += 2) {
+            const float pe =
+                __builtin_amdgcn_exp2f(bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius] - m);
+            sub += pe;
+            subb += as_operand(pe, (T*)0);
+          }
           pads = sub + other_half(sub);
+          pads_b = subb + other_half(subb);
         }
         const float full = lt;
         lt -= pads;
+        lbt -= pads_b;
         // Cancellation guard, as in the regular forward: when the remainder
         // keeps fewer than ~12 significant bits, the half-tile's valid terms
         // are summed again (plain dot products against the K rows still in
@@ -244,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void jfa_fsq_kernel(FwdArgs a) {
         const bool cancel = !(lt > full * 0x1p-12f);
         if (__any(cancel)) {
           const lds_t* kt = lds + (last_tile & 1) * C::STAGE;
-          float sv = 0.f;
+          float sv = 0.f, svb = 0.f;
 #pragma unroll 1
           for (int r = g; r < 32; r += 2) {
             const int kj = hk0 + r;
@@ -266,28 +281,37 @@ __global__ __launch_bounds__(256, 2) void jfa_fsq_kernel(FwdArgs a) {
             }
             float x = dot * a.scale2;
             if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
-            sv += __builtin_amdgcn_exp2f(x - m);
+            const float pe = __builtin_amdgcn_exp2f(x - m);
+            sv += pe;
+            svb += as_operand(pe, (T*)0);
           }
           const float fixed = l_pre + other_half(l_pre) + sv + other_half(sv);
-          if (cancel) lt = fixed;
+          const float fixedb = kOpSum ? lb_pre + other_half(lb_pre) + svb + other_half(svb) : fixed;
+          if (cancel) {
+            lt = fixed;
+            lbt = fixedb;
+          }
         }
       }
     }
     __syncthreads();  // the K tiles are read above; the merge below reuses their LDS
 
-    // Merge the two key halves of each query half: (m, l) through LDS, then
-    // the key-half-1 wave's weighted O^T, to which its partner adds its own.
+    // Merge the two key halves of each query half: (m, l, lb) through LDS,
+    // then the key-half-1 wave's weighted O^T, to which its partner adds its own.
     if (g == 0) {
-      mlx[(w * 32 + l32) * 2] = m;
-      mlx[(w * 32 + l32) * 2 + 1] = lt;
+      mlx[(w * 32 + l32) * 4] = m;
+      mlx[(w * 32 + l32) * 4 + 1] = lt;
+      mlx[(w * 32 + l32) * 4 + 2] = lbt;
     }
     __syncthreads();
     const int pw = w ^ 1;
-    const float mp = mlx[(pw * 32 + l32) * 2], lp = mlx[(pw * 32 + l32) * 2 + 1];
+    const float mp = mlx[(pw * 32 + l32) * 4], lp = mlx[(pw * 32 + l32) * 4 + 1];
+    const float lpb = mlx[(pw * 32 + l32) * 4 + 2];
     const float M = fmaxf(m, mp);
     const float cw = __builtin_amdgcn_exp2f(m - M), cp = __builtin_amdgcn_exp2f(mp - M);
-    const float L = lt * cw + lp * cp;
-    const float f = L > 0.f ? cw / L : 0.f;  // weight of this wave's O^T in the normalised row
+    const float L = lt * cw + lp * cp;     // fp32 sum: the chunk's lse
+    const float Lb = lbt * cw + lpb * cp;  // operand sum: the chunk's normalisation
+    const float f = Lb > 0.f ? cw / Lb : 0.f;  // weight of this wave's O^T in the normalised row
     using OL = typename C::OL;
     if (kh == 1) {
 #pragma unroll
