@@ -1,6 +1,7 @@
 """Builds libjfa.so (gfx950) from csrc/ with hipcc, in place.
 
     python -m variable_length_attention_jfa_amd.build [--jobs N] [--save-temps] [--define N=V --out PATH]
+    python -m variable_length_attention_jfa_amd.build --studies   (the design-study variants, on demand)
 
 Every source is compiled for gfx950 only, with packed fp32 VALU instructions
 disabled, then linked into variable_length_attention_jfa_amd/libjfa.so.
@@ -24,6 +25,28 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
+
+
+def source_hash() -> str:
+    """Hash of the kernel and header sources a build compiles."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (CSRC, os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".h")):
+                with open(os.path.join(d, name), "rb") as fh:
+                    h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def is_current(path: str) -> bool:
+    """A study variant at `path` exists and was built from the current sources
+    (its .srchash stamp, written by build(), matches)."""
+    stamp = path + ".srchash"
+    if not (os.path.exists(path) and os.path.exists(stamp)):
+        return False
+    with open(stamp) as fh:
+        return fh.read().strip() == source_hash()
 
 
 def _compile(src: str, save_temps: bool, objdir: str = BUILD, defines=()) -> str:
@@ -53,9 +76,24 @@ def build(jobs: int = 4, save_temps: bool = False, verbose: bool = True, defines
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, out)
+    if out != LIB:  # study variants carry the hash of the sources they were built from
+        with open(out + ".srchash", "w") as fh:
+            fh.write(source_hash() + "\n")
     if verbose:
         print(f"built {out}")
     return out
+
+
+def build_studies(jobs: int = 8) -> None:
+    """The design-study variants (each a whole library with other compile-time
+    choices, under _study/): -inf masking modes 1 and 2, the list-order and
+    grid variants of the scheduling study, and unswizzled LDS tiles. Their
+    GPU tests skip when they are not built."""
+    from . import mask_study, sched_study
+    mask_study.build_variants(jobs)
+    sched_study.build_variants(jobs)
+    build(jobs=jobs, defines=["JFA_LDS_SWIZZLE=0"], out=os.path.join(PKG, "_study", "libjfa_noswz.so"),
+          objdir=os.path.join(BUILD, "noswz"))
 
 
 def main(argv=None) -> int:
@@ -65,7 +103,11 @@ def main(argv=None) -> int:
     ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
                     help="extra preprocessor definition (study variants, e.g. JFA_LDS_SWIZZLE=0)")
     ap.add_argument("--out", default=LIB, help="library path (default: the package's libjfa.so)")
+    ap.add_argument("--studies", action="store_true", help="build the design-study variants instead")
     args = ap.parse_args(argv)
+    if args.studies:
+        build_studies(args.jobs)
+        return 0
     out = os.path.abspath(args.out)
     objdir = BUILD if out == LIB else os.path.join(BUILD, os.path.splitext(os.path.basename(out))[0])
     build(args.jobs, args.save_temps, defines=args.define, out=out, objdir=objdir)

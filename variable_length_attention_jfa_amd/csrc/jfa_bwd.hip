@@ -26,7 +26,10 @@
 //
 // Rows past a sequence's end load as zeros (Q = dO = 0 for pad queries,
 // K = V = 0 for pad keys), so every product they enter is zero: no jagged
-// mask is needed here. The causal mask zeroes P above the diagonal on the
+// mask is needed here. The one exception is P itself, exp(bias - lse), which
+// a large bias could overflow for a pad query (0 * inf in dS); pad queries
+// therefore get lse = +inf in the row constants staged in LDS, which makes
+// their P exactly 0. The causal mask zeroes P above the diagonal on the
 // blocks that straddle it.
 #include <type_traits>
 
@@ -112,6 +115,7 @@ template <typename T, int D>
 struct DkvStage {
   i32x4 c[DkvTiles<T, D>::NCH];
   i32x2 rc;
+  bool row_ok;  // this thread's row constant belongs to a query of the sequence
 };
 
 template <typename T, int D>
@@ -130,6 +134,7 @@ __device__ __forceinline__ void dkv_gload(const DkvItem& it, int jb, uint32_t gs
     }
   }
   if (tid < C::BMQ) st.rc = ld8(seq_view(it.rcbase + (size_t)r0 * H, rows, 8 * H, 8), 8 * H * tid);
+  st.row_ok = tid < rows;
 }
 
 template <typename T, int D>
@@ -144,8 +149,9 @@ __device__ __forceinline__ void dkv_swrite(int jb, int tid, const DkvStage<T, D>
       *(__attribute__((address_space(3))) i32x4*)(sl + (x < C::NQC ? 0 : C::QTILE) + C::TL::chunk(row, col)) = st.c[c];
     }
   }
-  if (tid < C::BMQ) {  // lse2 of the block's rows, then -Delta (the start of each dP accumulation)
-    ((__attribute__((address_space(3))) float*)(sl + C::RCOFF))[tid] = __int_as_float(st.rc[0]);
+  if (tid < C::BMQ) {  // lse2 of the block's rows, then -Delta (the start of each dP accumulation);
+    // rows past the sequence end get lse2 = +inf, so P = 0 there whatever the bias
+    ((__attribute__((address_space(3))) float*)(sl + C::RCOFF))[tid] = st.row_ok ? __int_as_float(st.rc[0]) : INFINITY;
     ((__attribute__((address_space(3))) float*)(sl + C::RCOFF))[C::BMQ + tid] = -__int_as_float(st.rc[1]);
   }
 }
@@ -460,6 +466,7 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
 
     i32x4 qr[C::CPT], dr[C::CPT];
     i32x2 lr = {};
+    bool lr_ok = false;  // the row constant belongs to a query of the sequence
     auto gload = [&](int qb) {
 #pragma unroll
       for (int c = 0; c < C::CPT; ++c) {
@@ -469,6 +476,7 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
         dr[c] = ld16(dov, off);
       }
       if (tid < BMQ) lr = ld8(rcv, (uint32_t)(qb * BMQ + tid) * 8 * H);
+      lr_ok = qb * BMQ + tid < Lq;
     };
     auto swrite = [&](int s) {
       lds_t* st = lds + s * C::STAGE;
@@ -479,8 +487,9 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
         *(__attribute__((address_space(3))) i32x4*)(st + o) = qr[c];
         *(__attribute__((address_space(3))) i32x4*)(st + C::QTILE + o) = dr[c];
       }
-      if (tid < BMQ) {  // lse2 of the block's rows, then -Delta (the start of each dP accumulation)
-        ((__attribute__((address_space(3))) float*)(st + 2 * C::QTILE))[tid] = __int_as_float(lr[0]);
+      if (tid < BMQ) {  // lse2 of the block's rows, then -Delta (the start of each dP accumulation);
+        // rows past the sequence end get lse2 = +inf, so P = 0 there whatever the bias
+        ((__attribute__((address_space(3))) float*)(st + 2 * C::QTILE))[tid] = lr_ok ? __int_as_float(lr[0]) : INFINITY;
         ((__attribute__((address_space(3))) float*)(st + 2 * C::QTILE))[BMQ + tid] = -__int_as_float(lr[1]);
       }
     };

@@ -179,6 +179,8 @@ __global__ __launch_bounds__(256, 2) void jfa_sq_kernel(BwdArgs a) {
           *(__attribute__((address_space(3))) i32x4*)((c * C::THREADS < QM * C::CPR ? qt : dot) + C::TL::chunk(row, col)) = r[c];
         }
       }
+      // queries past the sequence end: lse2 = +inf, so their P is 0 whatever the bias
+      if (tid >= Lq) rr[0] = __float_as_int(INFINITY);
       if (tid < QM) *(__attribute__((address_space(3))) i32x2*)((lds_t*)rc + 8 * tid) = rr;
     }
 
