@@ -1,6 +1,6 @@
 """Benchmark: jagged attention forward + backward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--all] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--also LIST] [--no-cpu-baseline]
 
 One step is the whole hot path over one synthetic batch already resident in
 HBM: jfa_fwd (work-list build + forward kernel) then jfa_bwd (three work
@@ -20,6 +20,12 @@ library's padded-dense kernels (a -inf key mask on every block, every block
 visited) and gives the jagged path's speedup and memory ratio over it;
 `cold_cache` times single steps after a 512 MiB write that empties the L2
 and Infinity Cache (median, p10, p90), next to the warm back-to-back `value`.
+Before the declared warm-up steps, untimed steps run for --prewarm-ms of wall
+time so that the clocks have settled whatever --warmup the caller gives
+(recorded as `prewarm`). `other_workloads` holds the same figures for the
+other four workloads (each with its own roofline entry: HBM GB/s for the
+asymmetric short-query workload, MFMA for the others; padded-dense baseline
+for the bf16 ones).
 """
 from __future__ import annotations
 
@@ -91,10 +97,13 @@ def recorded_traffic(kernel_label: str, workload: int):
     return None
 
 
-# Algorithmic flops per valid pair per head, as multiples of D, for each kernel:
-# forward QK^T + PV; dK/dV pass recomputes QK^T and dO V^T and forms dV, dK;
-# dQ pass recomputes QK^T and dO V^T and forms dQ.
-KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "fsq": 4, "dkdv": 8, "dq": 6, "sq": 10}
+# Algorithmic flops per valid pair per head, as multiples of D, credited to
+# each kernel: the backward's 10*D (QK^T recomputed once, dP = dO V^T, dV, dK,
+# dQ) is split as dK/dV pass 8*D (QK^T, dP, dV, dK) and dQ pass 2*D (dQ); the
+# dQ pass also executes QK^T and dP again (4*D more), which is recompute the
+# split design adds and is not counted (KERNEL_EXEC_FLOPS_PER_PAIR_D).
+KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "fsq": 4, "dkdv": 8, "dq": 2, "sq": 10}
+KERNEL_EXEC_FLOPS_PER_PAIR_D = {"forward": 4, "fsq": 4, "dkdv": 8, "dq": 6, "sq": 10}
 KERNEL_SEQS = {"forward": "long", "fsq": "short", "dkdv": "long", "dq": "long", "sq": "short"}
 
 
@@ -118,8 +127,23 @@ def cold_cache_steps(step, n, torch, flush_mib=512):
     return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
 
 
+def prewarm(step, torch, min_ms):
+    """Runs steps until at least min_ms of wall time has passed (the clocks
+    ramp up over the first tens of milliseconds of back-to-back work).
+    Returns (steps run, milliseconds)."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            el = (time.perf_counter() - t0) * 1e3
+            if el >= min_ms:
+                return n, el
+
+
 def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None, bias_grad=False, padded_steps=0,
-                 cold_steps=0):
+                 cold_steps=0, prewarm_ms=0.0):
     wl = gen.WORKLOADS[idx]
     batch = gen.make_batch(wl, seed=seed)
     dev = torch.device("cuda")
@@ -148,6 +172,7 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None,
         jfa.backward(q, k, v, out, lse, do, qo, ko, bias, wl.causal, dq=dq, dk=dk, dv=dv, bias_grad=bias_grad,
                      max_kv_len=max_kv)
 
+    pw = prewarm(step, torch, prewarm_ms) if prewarm_ms > 0 else (0, 0.0)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -181,7 +206,7 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None,
         "workload": wl.name, "B": wl.B, "H": wl.H, "D": wl.D, "dtype": wl.dtype, "causal": wl.causal,
         "bias": wl.bias, "seed": wl.seed if seed is None else seed, "total_q": batch.total_q,
         "total_kv": batch.total_kv, "max_kv_len": max_kv, "valid_pairs_per_head": pairs,
-        "ms_per_step": ms_step,
+        "ms_per_step": ms_step, "prewarm": {"steps": pw[0], "ms": pw[1]},
         "tflops_step": (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12,
         "fwd_ms_kernels": fwd_ms, "bwd_ms_kernels": bwd_ms,
         "fwd_tflops": fwd_flops / (fwd_ms * 1e-3) / 1e12,
@@ -200,18 +225,20 @@ def run_workload(idx, steps, warmup, torch, jfa, gen, with_cpu=False, seed=None,
     avg_ms = kt[dom][0] / kt[dom][1]
     kpairs = valid_pairs(batch.q_lengths, batch.kv_lengths, wl.causal, KERNEL_SEQS[dom])
     alg = KERNEL_FLOPS_PER_PAIR_D[dom] * wl.D * wl.H * kpairs
+    executed = KERNEL_EXEC_FLOPS_PER_PAIR_D[dom] * wl.D * wl.H * kpairs
     alg_bytes = algorithmic_bytes(dom, batch)
     label = f"jfa_{'fwd' if dom == 'forward' else dom}_kernel<{wl.dtype},D={wl.D}{',bias' if wl.bias else ''}>"
-    hbm = alg / max(alg_bytes, 1) < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    hbm = executed / max(alg_bytes, 1) < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     if hbm:
         achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                "mfma_frac": alg / (avg_ms * 1e-3) / 1e12 / peak}
     else:
         achieved = alg / (avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
     res["roofline"] = {"kernel": label, **roof, "traffic": recorded_traffic(label, idx), "traffic_unit": "bytes/launch",
                        "avg_launch_ms": avg_ms, "algorithmic_flops_per_launch": alg,
-                       "algorithmic_bytes_per_launch": alg_bytes}
+                       "executed_flops_per_launch": executed, "algorithmic_bytes_per_launch": alg_bytes}
     if padded_steps > 0 and wl.dtype == "bf16":  # the padded-dense kernels are bf16 only
         res["padded_baseline"] = run_padded(batch, d=dict(q=q, k=k, v=v, do=do, bias=bias, out=out, lse=lse, dq=dq),
                                             steps=padded_steps, jfa_ms=ms_step, jfa_fwd_ms=fwd_ms, jfa_bwd_ms=bwd_ms,
@@ -294,33 +321,92 @@ def algorithmic_bytes(kernel: str, batch) -> int:
     return 2 * tq + 2 * tk + 2 * rows + tq   # dq: q, k, v, dout, lse, delta in; dq out
 
 
-def cpu_baseline(batch, budget_s=15.0):
-    """fp64 oracle (fwd + bwd) on (b, h) pairs in a fixed order until the budget is spent."""
+def _cpu_worker(wl_idx, seed, pairs, barrier, results):
+    """One process of the CPU baseline: regenerates the batch from its seed
+    (the same bytes the GPU gets), waits for the other processes, then times
+    the oracle's forward and backward on its share of the (b, h) slices."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    wl = batch.wl
-    B, H = len(batch.q_lengths), wl.H
+    from variable_length_attention_jfa_amd import inputs as gen
+    wl = gen.WORKLOADS[wl_idx]
+    batch = gen.make_batch(wl, seed=seed)
+    args = (batch.q, batch.k, batch.v)
+    barrier.wait()
+    t0 = time.perf_counter()
+    out, lse = oracle.forward(*args, batch.q_offsets, batch.kv_offsets, batch.bias, wl.causal, pairs=pairs)
+    t1 = time.perf_counter()
+    barrier.wait()
+    t2 = time.perf_counter()
+    oracle.backward(*args, batch.dout, batch.q_offsets, batch.kv_offsets, batch.bias, wl.causal, pairs=pairs,
+                    out=out, lse=lse)
+    t3 = time.perf_counter()
+    results.put((t1 - t0, t3 - t2, len(pairs)))
+
+
+def cpu_baseline(wl_idx, seed=None, budget_gflop=600.0, max_procs=16):
+    """The fp64 oracle on the host cores: one process per core (at most
+    max_procs, the host share of one GPU), one BLAS thread each, the (b, h)
+    slices split longest-first over the processes. The sample is the whole
+    workload if its forward + backward stays under budget_gflop, else
+    slices in a fixed shuffled order up to that budget. The forward and the
+    backward (given the forward's O and lse) are timed separately as the
+    slowest process's time, all processes starting each phase together.
+    Runs before the GPU is touched: the processes are started fresh
+    (spawn), never forked from a process holding GPU state."""
+    import multiprocessing as mp
+    from variable_length_attention_jfa_amd import inputs as gen
+    wl = gen.WORKLOADS[wl_idx]
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    ql = wl.q_len.sample(rng, wl.B)
+    kl = wl.kv_len.sample(rng, wl.B) if wl.kv_len is not None else ql
+    B, H = len(ql), wl.H
     order = [(b, h) for h in range(H) for b in range(B)]
-    rng = np.random.default_rng(0)
-    rng.shuffle(order)
-    done, flops, t0 = 0, 0.0, time.perf_counter()
+    np.random.default_rng(0).shuffle(order)
+    pair_gflop = {}
+    chosen, total = [], 0.0
     for b, h in order:
-        oracle.backward(batch.q, batch.k, batch.v, batch.dout, batch.q_offsets, batch.kv_offsets, batch.bias,
-                        wl.causal, pairs=[(b, h)])  # runs the forward internally
-        lq, lk = int(batch.q_lengths[b]), int(batch.kv_lengths[b])
-        p = valid_pairs(np.array([lq]), np.array([lk]), wl.causal)
-        flops += 14.0 * wl.D * p  # 4*D forward + 10*D backward per pair
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
+        p = valid_pairs(np.array([ql[b]]), np.array([kl[b]]), wl.causal)
+        f = 14.0 * wl.D * p / 1e9
+        if chosen and total + f > budget_gflop:
             break
-    el = time.perf_counter() - t0
-    return {"value": flops / el / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 numpy oracle forward+backward on {done} of {B * H} (b, h) slices of the same "
-                      f"workload ({flops / 1e9:.1f} valid-pair GFLOP in {el:.1f} s)"}
+        chosen.append((b, h))
+        pair_gflop[(b, h)] = f
+        total += f
+    cores = max(1, min(len(os.sched_getaffinity(0)), max_procs))
+    nproc = min(cores, len(chosen))
+    shares = [[] for _ in range(nproc)]
+    load = [0.0] * nproc
+    for bh in sorted(chosen, key=lambda x: -pair_gflop[x]):  # longest first onto the least-loaded process
+        i = int(np.argmin(load))
+        shares[i].append(bh)
+        load[i] += pair_gflop[bh]
+    saved = {k: os.environ.get(k) for k in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    try:
+        ctx = mp.get_context("spawn")
+        barrier, results = ctx.Barrier(nproc), ctx.Queue()
+        procs = [ctx.Process(target=_cpu_worker, args=(wl_idx, seed, sh, barrier, results)) for sh in shares]
+        for pr in procs:
+            pr.start()
+        got = [results.get(timeout=600) for _ in procs]
+        for pr in procs:
+            pr.join()
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    t_fwd = max(g[0] for g in got)
+    t_bwd = max(g[1] for g in got)
+    pairs = sum(valid_pairs(np.array([ql[b]]), np.array([kl[b]]), wl.causal) for b, _ in chosen)
+    fwd_f, bwd_f = 4.0 * wl.D * pairs, 10.0 * wl.D * pairs
+    return {"value": (fwd_f + bwd_f) / (t_fwd + t_bwd) / 1e12, "unit": "TFLOPS", "cores": nproc, "kind": "oracle",
+            "fwd_tflops": fwd_f / t_fwd / 1e12, "bwd_tflops": bwd_f / t_bwd / 1e12, "fwd_s": t_fwd, "bwd_s": t_bwd,
+            "sample": f"fp64 numpy oracle, {nproc} processes x 1 BLAS thread, on {len(chosen)} of {B * H} (b, h) "
+                      f"slices of the same workload ({'all of it' if len(chosen) == B * H else 'a shuffled subset'}; "
+                      f"{(fwd_f + bwd_f) / 1e9:.1f} valid-pair GFLOP): forward {t_fwd:.2f} s, backward given "
+                      f"the forward's O and lse {t_bwd:.2f} s (slowest process of each phase)"}
 
 
 def main(argv=None):
@@ -329,12 +415,15 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=200, help="untimed steps first (the clocks settle within about 50 ms)")
     ap.add_argument("--workload", type=int, default=2, help="workload number 1..5 (default 2)")
-    ap.add_argument("--also", type=str, default="3", help="comma list of extra workloads reported alongside")
+    ap.add_argument("--also", type=str, default="1,3,4,5", help="comma list of extra workloads reported alongside")
     ap.add_argument("--all", action="store_true", help="also report workloads 1..5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-padded", action="store_true", help="skip the padded-dense baseline")
     ap.add_argument("--lib", default=None, help="run another build of the library (study variants)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=600.0,
+                    help="GFLOP of oracle work (forward + backward) the CPU baseline's sample may hold")
+    ap.add_argument("--prewarm-ms", type=float, default=300.0,
+                    help="wall time of untimed steps before the --warmup steps (clock ramp-up)")
     ap.add_argument("--bias-grad", action="store_true",
                     help="the backward also returns the bias-table gradient (workloads with a bias)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -345,6 +434,13 @@ def main(argv=None):
               f"(the library computes one GPU's share; sharding across GPUs is not implemented)",
               file=sys.stderr)
         return 2
+
+    # The CPU baseline first, before anything touches the GPU: its worker
+    # processes start from a clean interpreter.
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, budget_gflop=args.cpu_budget)
+        print(f"[bench] cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
 
     import torch
     from variable_length_attention_jfa_amd import inputs as gen
@@ -371,7 +467,8 @@ def main(argv=None):
         return 2
     pad_steps = 0 if args.no_padded else max(3, min(20, args.steps // 10))
     main_res = run_workload(args.workload, args.steps, args.warmup, torch, jfa, gen, bias_grad=args.bias_grad,
-                            padded_steps=pad_steps, cold_steps=max(5, min(50, args.steps // 6)))
+                            padded_steps=pad_steps, cold_steps=max(5, min(50, args.steps // 6)),
+                            prewarm_ms=args.prewarm_ms)
     pb = main_res.get("padded_baseline")
     print(f"[bench] workload {args.workload}: {main_res['tflops_step']:.1f} TFLOP/s fwd+bwd, "
           f"fwd {main_res['fwd_tflops']:.1f} bwd {main_res['bwd_tflops']:.1f}"
@@ -382,20 +479,20 @@ def main(argv=None):
     for i in extra_ids:
         if i == args.workload:
             continue
-        r = run_workload(i, max(3, args.steps // 2), 2, torch, jfa, gen, padded_steps=pad_steps)
+        r = run_workload(i, max(3, args.steps // 2), 2, torch, jfa, gen, padded_steps=pad_steps,
+                         prewarm_ms=min(100.0, args.prewarm_ms))
         r.pop("_batch")
         pb = r.get("padded_baseline")
+        rf = r["roofline"]
         print(f"[bench] workload {i}: fwd {r['fwd_tflops']:.1f} ({r['fwd_pct_peak']:.1f}%) "
-              f"bwd {r['bwd_tflops']:.1f} ({r['bwd_pct_peak']:.1f}%)"
+              f"bwd {r['bwd_tflops']:.1f} ({r['bwd_pct_peak']:.1f}%); {rf['kernel']} {rf['achieved']:.1f} "
+              f"{rf['unit']} ({100 * rf['frac']:.1f}% of {rf['bound']})"
               + (f"; padded-dense {pb['ms_per_step']:.2f} ms/step, speedup {pb['speedup_step']:.2f}x, "
                  f"memory {pb['memory_ratio']:.2f}x" if pb else ""), file=sys.stderr, flush=True)
         extras.append(r)
         torch.cuda.empty_cache()
 
     batch = main_res.pop("_batch")
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(batch, args.cpu_budget)
 
     wl = batch.wl
     line = {
@@ -406,6 +503,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": main_res["ms_per_step"],
+        "prewarm": main_res["prewarm"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

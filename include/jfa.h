@@ -186,7 +186,11 @@ jfa_status jfa_bwd_padded(const void* q, const void* k, const void* v, const voi
  * jagged tensors ("Jagged Flash Attention (JFA)", section "Definition"). */
 jfa_status jfa_offsets_from_lengths(const int32_t* lengths, int B, int32_t* offsets, void* stream);
 
-/* Tile shape of a kernel: *tile_m query rows and *tile_n keys. For
+/* Tile shape of a kernel: *tile_m query rows and *tile_n keys. Tiles are
+ * the work items of the persistent, longest-first scheduling ("Jagged Flash
+ * Attention (JFA)", sections "Why standard FlashAttention falls short", on
+ * short sequences leaving compute units idle, and "Four generations", item 3,
+ * persistent kernels). For
  * JFA_KERNEL_FWD and JFA_KERNEL_BWD_DQ an item is one tile of tile_m query
  * rows and its cost counts tile_n-key blocks; for JFA_KERNEL_BWD_DKDV an item
  * is one tile of tile_n keys and its cost counts tile_m-row query blocks; for
@@ -194,7 +198,9 @@ jfa_status jfa_offsets_from_lengths(const int32_t* lengths, int B, int32_t* offs
  * of a sequence with at most tile_m queries. */
 jfa_status jfa_tile_config(int kernel, int D, int dtype, int* tile_m, int* tile_n);
 
-/* Builds the longest-first work lists the given kernel runs on, into
+/* Builds the longest-first work lists the given kernel runs on (the
+ * scheduling of "Jagged Flash Attention (JFA)", sections "Why standard
+ * FlashAttention falls short" and "Four generations", item 3), into
  * `workspace`: a JFA_PLAN_HEADER_BYTES header of int32 {count, status, nq,
  * pad, start[8], qcount[8], ...; queue q's ticket at int32 index 32 * (q + 1)}
  * followed by `count` items of four
@@ -215,7 +221,9 @@ jfa_status jfa_tile_config(int kernel, int D, int dtype, int* tile_m, int* tile_
 jfa_status jfa_build_plan(const int32_t* q_offsets, const int32_t* kv_offsets, int B, int H, int D, int dtype,
                           int causal, int kernel, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes jfa_build_plan needs for that kernel. */
+/* Workspace bytes jfa_build_plan needs for that kernel: the list header and
+ * at most H * (ceil(total / tile) + B) items of the work list above (same
+ * passages). Returns 0 for invalid sizes. */
 size_t jfa_plan_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, int D, int dtype, int kernel);
 
 /* Launch timing, for benchmarks and profiling. While enabled, every kernel

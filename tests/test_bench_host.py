@@ -68,9 +68,13 @@ def test_algorithmic_bytes():
 
 
 def test_flops_per_pair_table():
-    # forward QK^T + PV; dK/dV recomputes S and dP and forms dV, dK; dQ
-    # recomputes S and dP and forms dQ; the short-query owner forms all five once
-    assert bench.KERNEL_FLOPS_PER_PAIR_D == {"forward": 4, "fsq": 4, "dkdv": 8, "dq": 6, "sq": 10}
+    # credited: forward QK^T + PV; the backward's 10*D split as dK/dV (S, dP,
+    # dV, dK) and dQ (dQ only); the short-query owner forms all five once
+    assert bench.KERNEL_FLOPS_PER_PAIR_D == {"forward": 4, "fsq": 4, "dkdv": 8, "dq": 2, "sq": 10}
+    assert bench.KERNEL_FLOPS_PER_PAIR_D["dkdv"] + bench.KERNEL_FLOPS_PER_PAIR_D["dq"] == 10
+    assert bench.KERNEL_FLOPS_PER_PAIR_D["sq"] == 10
+    # executed: the dQ pass recomputes S and dP (4*D) before forming dQ
+    assert bench.KERNEL_EXEC_FLOPS_PER_PAIR_D["dq"] == 6
 
 
 def test_recorded_traffic_reads_matching_lines(tmp_path, monkeypatch):
