@@ -133,6 +133,26 @@ jfa_status jfa_bwd(const void* q, const void* k, const void* v, const void* out,
                    void* dq, void* dk, void* dv, float* dbias, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same parameters and results as jfa_fwd
+ * (bit-identical outputs: the same kernels) without workspace and
+ * workspace_bytes: the scratch is a fixed JFA_NOALLOC_SCRATCH_BYTES device
+ * array inside the library, one per GPU, held until the process ends. The
+ * call allocates nothing (no hipMalloc, no allocating library routine).
+ * A call whose work list needs more scratch than that returns
+ * JFA_ERR_WORKSPACE with the size it needs: the list takes 16 bytes per item
+ * (at most H * (ceil(total_q / 128) + B) items), and, unless max_kv_len is in
+ * 1 .. 1024, the short-query chunk rows add about
+ * H * (ceil(total_kv / 1024) + B) * (256 * D + 272) bytes. Every call on one
+ * GPU uses that GPU's one array: calls that overlap on one GPU (several
+ * streams, several host threads) race and must be serialised by the
+ * caller. */
+#define JFA_NOALLOC_SCRATCH_BYTES (32u << 20)
+jfa_status jfa_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                           const int32_t* kv_offsets, int B, int H, int D, int64_t total_q, int64_t total_kv,
+                           int max_kv_len, const float* bias, int causal, void* out, float* lse, void* stream);
+
 /* fp32 twins: identical parameters, every tensor of element type fp32;
  * D must be 32 or 64 (JFA_ERR_UNSUPPORTED for 128). */
 jfa_status jfa_fwd_f32(const void* q, const void* k, const void* v, const int32_t* q_offsets,
@@ -244,7 +264,7 @@ const char* jfa_last_error(void);
 
 /* Version of the argument lists above; a binding compares it with the one it
  * was written for before calling anything else. */
-#define JFA_ABI_VERSION 4
+#define JFA_ABI_VERSION 5
 int jfa_abi_version(void);
 
 #ifdef __cplusplus

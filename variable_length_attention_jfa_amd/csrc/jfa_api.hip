@@ -132,10 +132,12 @@ struct FwdLayout {
   size_t hdr = 0, hdr_sq = sizeof(PlanHeader), items = 0, items_sq = 0, gfirst = 0, op = 0, lsep = 0, total = 0;
   int64_t cap = 0, cap_sq = 0;
 };
-FwdLayout fwd_layout(int B, int H, int64_t tq, int64_t tk, int D) {
+// short_on = false: a layout without the short-query regions (their pass does
+// not run), for callers that know it, such as jfa_fwd_noalloc.
+FwdLayout fwd_layout(int B, int H, int64_t tq, int64_t tk, int D, bool short_on = true) {
   FwdLayout L;
   L.cap = max_items(B, H, tq, 128);  // smallest forward tile: an upper bound for every variant
-  L.cap_sq = max_items(B, H, tk, jfa::kSqKC);
+  L.cap_sq = short_on ? max_items(B, H, tk, jfa::kSqKC) : 0;
   L.items = 2 * sizeof(PlanHeader);
   L.items_sq = L.items + align_up((size_t)L.cap * 16);
   L.gfirst = L.items_sq + align_up((size_t)L.cap_sq * 16);
@@ -204,13 +206,16 @@ jfa_status check_common(const void* q, const void* k, const void* v, const int32
 // short-query passes nor the subtraction of pad terms.
 jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const int32_t* qo, const int32_t* ko,
                     int B, int H, int D, int64_t tq, int64_t tk, int max_kv_len, const float* bias, int causal,
-                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream, const int32_t* pad_kv_len = nullptr) {
+                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream, const int32_t* pad_kv_len = nullptr,
+                    bool compact = false) {
   jfa_status s = check_common(q, k, v, qo, ko, B, H, D, tq, tk, max_kv_len, bias, ws);
   if (s != JFA_OK) return s;
   if (f32 && D > 64) return fail(JFA_ERR_UNSUPPORTED, "fp32 tensors support D = 32 or 64");
   if ((tq > 0 && (!out || !lse))) return fail(JFA_ERR_INVALID_ARGUMENT, "out/lse must not be NULL");
   if (!aligned(out, 16) || !aligned(lse, 4)) return fail(JFA_ERR_INVALID_ARGUMENT, "out must be 16-byte aligned");
-  const FwdLayout L = fwd_layout(B, H, tq, tk, D);
+  // compact: the short-query regions only when that pass runs (the caller
+  // sized the workspace for this call, not by jfa_fwd_workspace_bytes)
+  const FwdLayout L = fwd_layout(B, H, tq, tk, D, !compact || (short_pass_on(max_kv_len) && !pad_kv_len));
   if (ws_bytes < L.total)
     return fail(JFA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
   DeviceInfo* dev = nullptr;
@@ -417,9 +422,60 @@ bool tile_of(int kernel, int D, int dtype, int* tm, int* tn) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free forward. Its scratch (work-list headers, items, short-query
+// chunk rows) is this file-scope device array; each GPU the library runs on
+// holds its own copy until the process ends. Host code never passes the
+// array's name to a kernel (in host code it is a host-side stand-in, not a
+// device address): the device address is fetched once per device with
+// hipGetSymbolAddress, with that device current, and kept in
+// g_scratch_ptr. The plan kernel rewrites every header field and ticket the
+// kernels read, so nothing needs clearing between calls; calls that overlap
+// on one GPU share the array and race.
+constexpr size_t kNoAllocScratchBytes = (size_t)JFA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+jfa_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(JFA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(JFA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::call_once(g_scratch_once[dev], [dev]() {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess)
+    return fail(JFA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(g_scratch_err[dev]));
+  *out = g_scratch_ptr[dev];
+  return JFA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+jfa_status jfa_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                           const int32_t* kv_offsets, int B, int H, int D, int64_t total_q,
+                           int64_t total_kv, int max_kv_len, const float* bias, int causal, void* out,
+                           float* lse, void* stream) {
+  if (max_kv_len < 0) return fail(JFA_ERR_INVALID_ARGUMENT, "max_kv_len must be >= 0 (0: unknown)");
+  if (!valid_sizes(B, H, total_q, total_kv, D))
+    return fail(JFA_ERR_INVALID_ARGUMENT, "invalid sizes: B=%d, H=%d, D=%d, total_q=%lld, total_kv=%lld", B, H, D,
+                (long long)total_q, (long long)total_kv);
+  const size_t need = fwd_layout(B, H, total_q, total_kv, D, short_pass_on(max_kv_len)).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(JFA_ERR_WORKSPACE,
+                "jfa_fwd_noalloc: this call needs %zu bytes of scratch, more than its fixed %zu; pass a key-count "
+                "bound of at most 1024 (max_kv_len) if it holds, or call jfa_fwd with a workspace",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  jfa_status s = scratch_ptr(&ws);
+  if (s != JFA_OK) return s;
+  return fwd_impl(false, q, k, v, q_offsets, kv_offsets, B, H, D, total_q, total_kv, max_kv_len, bias, causal, out,
+                  lse, ws, kNoAllocScratchBytes, stream, nullptr, /*compact=*/true);
+}
 
 size_t jfa_fwd_workspace_bytes(int B, int H, int64_t total_q, int64_t total_kv, int D, int causal) {
   (void)causal;

@@ -28,7 +28,7 @@ KERNEL_FWD, KERNEL_BWD_DKDV, KERNEL_BWD_DQ, KERNEL_BWD_SQ, KERNEL_FWD_SQ = 0, 1,
 SQ_KERNELS = (KERNEL_BWD_SQ, KERNEL_FWD_SQ)  # short-query chunk lists (one list, two passes)
 DTYPE_BF16, DTYPE_F32 = 0, 1
 BIAS_RADIUS = 128
-ABI_VERSION = 4  # JFA_ABI_VERSION of include/jfa.h
+ABI_VERSION = 5  # JFA_ABI_VERSION of include/jfa.h
 WORKSPACE_ALIGN = 256
 PLAN_HEADER_BYTES = 2048
 PLAN_QUEUES = 8
@@ -44,6 +44,8 @@ _SIGS = {
     "jfa_bwd_workspace_bytes": (_sz, [_int, _int, _i64, _i64, _int, _int]),
     "jfa_fwd": (_int, [_vp, _vp, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _int, _f32p, _int, _vp, _f32p, _vp, _sz,
                        _vp]),
+    "jfa_fwd_noalloc": (_int, [_vp, _vp, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _int, _f32p, _int, _vp, _f32p,
+                               _vp]),
     "jfa_fwd_f32": (_int, [_vp, _vp, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _int, _f32p, _int, _vp, _f32p, _vp,
                            _sz, _vp]),
     "jfa_bwd": (_int, [_vp, _vp, _vp, _vp, _f32p, _vp, _i32p, _i32p, _int, _int, _int, _i64, _i64, _int, _f32p, _int,
@@ -177,6 +179,24 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: torch.
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets), B, H, D, Tq, Tk, int(max_kv_len), _ptr(bias),
             int(causal), _ptr(out), _ptr(lse), ctypes.c_void_p(wp), nbytes, _stream())
     _check("jfa_fwd", st)
+    return out, lse
+
+
+def forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: torch.Tensor,
+                    kv_offsets: torch.Tensor, bias: Optional[torch.Tensor], causal: bool, out: torch.Tensor,
+                    lse: torch.Tensor, max_kv_len: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """jfa_fwd_noalloc: the forward with the library's fixed scratch instead of a
+    workspace (bf16; out and lse are the caller's, nothing is allocated)."""
+    B, H, D, Tq, Tk = _common(q, k, v, q_offsets, kv_offsets, bias)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("jfa_fwd_noalloc takes bfloat16 tensors")
+    _check_tensor("out", out, q.dtype, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    _check_shape("out", out, q.shape)
+    _check_shape("lse", lse, (Tq, H))
+    st = lib().jfa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets), B, H, D, Tq, Tk,
+                               int(max_kv_len), _ptr(bias), int(causal), _ptr(out), _ptr(lse), _stream())
+    _check("jfa_fwd_noalloc", st)
     return out, lse
 
 
