@@ -471,3 +471,42 @@ def test_large_positive_bias_bin(D, causal):
     batch = gen.make_batch(wl, q_lengths=ql, kv_lengths=kl)
     batch.bias[:, 128 + 40] = 90.0  # bins are clip(i - j, -128, 128) + 128
     _check(batch, label=f"large bias bin D={D} causal={causal}")
+
+
+_BWD_DQ_CASES = {
+    "small_cfg2": lambda: gen.make_batch(SMALL[2]),
+    "bf16_d32_causal_bias_asym": lambda: gen.make_batch(gen.Workload(
+        "dqd", 4, 2, 32, "bf16", True, True, gen.LengthDist("uniform", 1, 300), gen.LengthDist("uniform", 1, 330),
+        seed=131)),
+    "bf16_d64_causal": lambda: gen.make_batch(gen.Workload(
+        "dqd", 4, 2, 64, "bf16", True, False, gen.LengthDist("uniform", 1, 400), seed=132)),
+    "f32_d32_bias_asym": lambda: gen.make_batch(gen.Workload(
+        "dqd", 4, 2, 32, "f32", False, True, gen.LengthDist("uniform", 1, 200), gen.LengthDist("uniform", 1, 260),
+        seed=133)),
+    "edges": lambda: gen.make_batch(gen.Workload("dqd", 8, 2, 64, "bf16", False, False, gen.LengthDist("fixed", 1, 1),
+                                                 seed=134),
+                                    q_lengths=[0, 5, 1, 63, 64, 65, 128, 129], kv_lengths=[3, 0, 1, 63, 64, 65, 128, 129]),
+    "short_query_mix": lambda: gen.make_batch(gen.Workload("dqd", 6, 2, 64, "bf16", False, True,
+                                                           gen.LengthDist("fixed", 1, 1), seed=135),
+                                              q_lengths=[64, 65, 1, 33, 17, 40], kv_lengths=[2500, 70, 1024, 1025, 0, 131]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_BWD_DQ_CASES))
+@pytest.mark.parametrize("mode", [1, 2])
+def test_backward_dq_design_variants(mode, case):
+    """The backward-design study builds (dQ fused into the dK/dV pass: 1 with
+    fp32 atomic adds, 2 with per-key-tile partials summed in key-tile order)
+    match the oracle like the split passes."""
+    path = os.path.join(os.path.dirname(jfa.LIB_PATH), "_study", f"libjfa_bwddq{mode}.so")
+    if not build.is_current(path):
+        pytest.skip(STUDY_SKIP)
+    batch = _BWD_DQ_CASES[case]()
+    saved = jfa.LIB_PATH
+    try:
+        jfa._LIB = None
+        jfa.LIB_PATH = path
+        _check(batch, label=f"backward dQ design {mode} {case}")
+    finally:
+        jfa._LIB = None
+        jfa.LIB_PATH = saved

@@ -87,13 +87,17 @@ def build(jobs: int = 4, save_temps: bool = False, verbose: bool = True, defines
 def build_studies(jobs: int = 8) -> None:
     """The design-study variants (each a whole library with other compile-time
     choices, under _study/): -inf masking modes 1 and 2, the list-order and
-    grid variants of the scheduling study, and unswizzled LDS tiles. Their
-    GPU tests skip when they are not built."""
+    grid variants of the scheduling study, unswizzled LDS tiles, and the
+    backward with dQ fused into the dK/dV pass (atomic adds, ordered
+    partials). Their GPU tests skip when they are not built."""
     from . import mask_study, sched_study
     mask_study.build_variants(jobs)
     sched_study.build_variants(jobs)
     build(jobs=jobs, defines=["JFA_LDS_SWIZZLE=0"], out=os.path.join(PKG, "_study", "libjfa_noswz.so"),
           objdir=os.path.join(BUILD, "noswz"))
+    for mode in (1, 2):  # dQ fused into the dK/dV pass: atomic adds, ordered partials
+        build(jobs=jobs, defines=[f"JFA_BWD_DQ={mode}"], out=os.path.join(PKG, "_study", f"libjfa_bwddq{mode}.so"),
+              objdir=os.path.join(BUILD, f"bwddq{mode}"))
 
 
 def main(argv=None) -> int:

@@ -154,7 +154,8 @@ FwdLayout fwd_layout(int B, int H, int64_t tq, int64_t tk, int D, bool short_on 
 // short-query item, and their sums per (block of 4 sequences, head).
 struct BwdLayout {
   size_t hdr_kv = 0, hdr_q = sizeof(PlanHeader), hdr_sq = 2 * sizeof(PlanHeader), rowc = 0, items_kv = 0,
-         items_q = 0, items_sq = 0, gfirst = 0, gfirst_kv = 0, dqp = 0, dbp_kv = 0, dbp_sq = 0, dbpart = 0, total = 0;
+         items_q = 0, items_sq = 0, gfirst = 0, gfirst_kv = 0, dqp = 0, dbp_kv = 0, dbp_sq = 0, dbpart = 0, dqacc = 0,
+         total = 0;
   int64_t cap_kv = 0, cap_q = 0, cap_sq = 0;
 };
 BwdLayout bwd_layout(int B, int H, int64_t tq, int64_t tk, int D) {
@@ -172,7 +173,13 @@ BwdLayout bwd_layout(int B, int H, int64_t tq, int64_t tk, int D) {
   L.dbp_kv = L.dqp + align_up((size_t)L.cap_sq * jfa::kSqQMax * D * 4);
   L.dbp_sq = L.dbp_kv + align_up((size_t)L.cap_kv * JFA_BIAS_LEN * 4);
   L.dbpart = L.dbp_sq + align_up((size_t)L.cap_sq * JFA_BIAS_LEN * 4);
-  L.total = L.dbpart + align_up((size_t)((B + jfa::kDbSeqBlock - 1) / jfa::kDbSeqBlock) * H * JFA_BIAS_LEN * 4);
+  L.dqacc = L.dbpart + align_up((size_t)((B + jfa::kDbSeqBlock - 1) / jfa::kDbSeqBlock) * H * JFA_BIAS_LEN * 4);
+  // study builds that fuse dQ into the dK/dV pass (rows of up to 128 bytes):
+  // an fp32 accumulator, or one partial plane per key tile (at most
+  // ceil(Tk / 128) tiles in any sequence)
+  const int mode = jfa::bwd_dq_mode(false, D) ? jfa::bwd_dq_mode(false, D) : jfa::bwd_dq_mode(true, D);
+  const size_t plane = align_up((size_t)tq * H * D * 4);
+  L.total = L.dqacc + (mode == 1 ? plane : mode == 2 ? plane * (size_t)cdiv64(tk, jfa::kDkvTN) : 0);
   return L;
 }
 
@@ -231,7 +238,7 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.H = H;
   pa.causal = causal ? 1 : 0;
   const bool short_on = short_pass_on(max_kv_len) && !pad_kv_len;
-  pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::fwd_tile_rows(f32, D), jfa::kFwdTN,
+  pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::fwd_tile_rows(f32, D), jfa::fwd_tile_keys(f32, D),
                 jfa::kPassQ, jfa::kPlanQueues, short_on ? jfa::kSqQMax : -1, nullptr};
   pa.pass[1] = {(int4*)(w + L.items_sq), (PlanHeader*)(w + L.hdr_sq), (long)L.cap_sq, jfa::kSqQMax, jfa::kSqKC,
                 jfa::kPassSQ, jfa::kPlanQueues, -1, (int*)(w + L.gfirst)};
@@ -312,10 +319,13 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.causal = causal ? 1 : 0;
   const bool short_on = short_pass_on(max_kv_len) && !padded;
   const int short_q = short_on ? jfa::kSqQMax : -1;
+  // study builds with dQ fused into the dK/dV pass: the dQ pass gets no items
+  // (its launch still sums the short-query partial dQ)
+  const int dq_mode = jfa::bwd_dq_mode(f32, D);
   pa.pass[0] = {(int4*)(w + L.items_kv), (PlanHeader*)(w + L.hdr_kv), (long)L.cap_kv, jfa::dkv_tile_rows(f32, D),
                 jfa::kDkvTN, jfa::kPassKV, jfa::kPlanQueues, short_q, (int*)(w + L.gfirst_kv)};
-  pa.pass[1] = {(int4*)(w + L.items_q), (PlanHeader*)(w + L.hdr_q), (long)L.cap_q, jfa::kDqTM, jfa::kDqTN,
-                jfa::kPassQ, jfa::kPlanQueues, short_q, nullptr};
+  pa.pass[1] = {(int4*)(w + L.items_q), (PlanHeader*)(w + L.hdr_q), dq_mode ? 0L : (long)L.cap_q, jfa::kDqTM,
+                jfa::kDqTN, jfa::kPassQ, jfa::kPlanQueues, short_q, nullptr};
   pa.pass[2] = {(int4*)(w + L.items_sq), (PlanHeader*)(w + L.hdr_sq), (long)L.cap_sq, jfa::kSqQMax, jfa::kSqKC,
                 jfa::kPassSQ, jfa::kPlanQueues, -1, (int*)(w + L.gfirst)};
   jfa::BwdArgs a{};
@@ -346,6 +356,7 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
   a.dbpart = (float*)(w + L.dbpart);
   a.dbias = dbias;
   a.kv_len = pad_kv_len;
+  a.dqacc = dq_mode ? (float*)(w + L.dqacc) : nullptr;
   jfa::BwdArgs a_kv = a, a_q = a, a_sq = a;
   a_kv.items = (const int4*)(w + L.items_kv);
   a_kv.hdr = (PlanHeader*)(w + L.hdr_kv);
@@ -362,10 +373,14 @@ jfa_status bwd_impl(bool f32, const void* q, const void* k, const void* v, const
     e = timed(kKindSq, st, [&] {
       return jfa::launch_sq(f32, D, a_sq, has_bias, dbias != nullptr, (long)L.cap_sq, dev->num_cus, st);
     });
+  if (e == hipSuccess && dq_mode == 1)
+    e = timed(kKindDkdv, st, [&] { return jfa::launch_dqacc_zero(a.dqacc, (long)tq * H * D, st); });
   if (e == hipSuccess)
     e = timed(kKindDkdv, st, [&] {
       return jfa::launch_dkdv(f32, D, a_kv, has_bias, dbias != nullptr, (long)L.cap_kv, dev->num_cus, st);
     });
+  if (e == hipSuccess && dq_mode)
+    e = timed(kKindDq, st, [&] { return jfa::launch_dq_fused_out(f32, D, a, st); });
   if (e == hipSuccess)
     e = timed(kKindDq, st, [&] { return jfa::launch_dq(f32, D, a_q, has_bias, (long)L.cap_q, dev->num_cus, st); });
   if (e == hipSuccess && dbias) e = timed(kKindDbias, st, [&] { return jfa::launch_dbias(a, st); });
@@ -413,7 +428,10 @@ jfa_status padded_setup(int B, int H, int q_slot, int kv_slot, int D, void* ws, 
 
 bool tile_of(int kernel, int D, int dtype, int* tm, int* tn) {
   switch (kernel) {
-    case JFA_KERNEL_FWD: *tm = jfa::fwd_tile_rows(dtype == JFA_DTYPE_F32, D); *tn = jfa::kFwdTN; return true;
+    case JFA_KERNEL_FWD:
+      *tm = jfa::fwd_tile_rows(dtype == JFA_DTYPE_F32, D);
+      *tn = jfa::fwd_tile_keys(dtype == JFA_DTYPE_F32, D);
+      return true;
     case JFA_KERNEL_BWD_DKDV: *tm = jfa::dkv_tile_rows(dtype == JFA_DTYPE_F32, D); *tn = jfa::kDkvTN; return true;
     case JFA_KERNEL_BWD_DQ: *tm = jfa::kDqTM; *tn = jfa::kDqTN; return true;
     case JFA_KERNEL_BWD_SQ:

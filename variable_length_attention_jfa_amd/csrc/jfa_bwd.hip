@@ -46,6 +46,37 @@ namespace jfa {
 #endif
 template <typename T> constexpr bool kPHalf = JFA_P_BF16 && sizeof(T) == 2;
 
+// Where dQ is formed (a study of the backward's design; the library is 0).
+//   0  the split passes: dK/dV per key tile, then dQ per query tile, with S
+//      and dP formed again ("Jagged Flash Attention (JFA)", "Four
+//      generations", item 2: no atomic writes, each output written once)
+//   1  dQ fused into the dK/dV pass, each key tile's dQ = dS K added into an
+//      fp32 accumulator with atomic adds (the design item 2 replaces)
+//   2  dQ fused into the dK/dV pass, each key tile's dQ stored as a partial
+//      and the partials of a query row summed in key-tile order by a later
+//      kernel (one owner per (sequence, head, key tile), deterministic)
+// Modes 1 and 2 cover the one-role dK/dV kernel (rows of up to 128 bytes);
+// wider rows keep the split passes.
+#ifndef JFA_BWD_DQ
+#define JFA_BWD_DQ 0
+#endif
+constexpr int kBwdDq = JFA_BWD_DQ;
+static_assert(kBwdDq >= 0 && kBwdDq <= 2, "backward dQ design");
+
+// Four consecutive values (columns col .. col+3) of one row of a tile of W
+// columns of T.
+template <typename T, int W>
+__device__ __forceinline__ void tile_put4(lds_t* tile, int row, int col, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    bf16x2 lo = {(bf16)a, (bf16)b}, hi = {(bf16)c, (bf16)d};
+    *(__attribute__((address_space(3))) i32x2*)(tile + Tile<bf16, W>::byte(row, col * 2)) =
+        (i32x2){__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+  } else {
+    *(__attribute__((address_space(3))) f32x4*)(tile + Tile<float, W>::byte(row, col * 4)) = (f32x4){a, b, c, d};
+  }
+}
+
 
 
 
@@ -405,7 +436,15 @@ struct Dkv1Tiles {
   static constexpr int CPR = ROWB / 16;
   static constexpr int CPT = BMQ * CPR / THREADS;
   static constexpr int BIAS_OFF = 2 * STAGE;
-  static constexpr int LDS = BIAS_OFF + 1040;
+  // fused dQ (study modes 1, 2): the block's dS as [key][query] and the
+  // item's K tile [key][D]
+  static constexpr bool FUSED = kBwdDq != 0;
+  static constexpr int DST_OFF = BIAS_OFF + 1040;
+  static constexpr int DST_BYTES = FUSED ? BNK * BMQ * (int)sizeof(T) : 0;
+  static constexpr int KT_OFF = DST_OFF + DST_BYTES;
+  static constexpr int KT_BYTES = FUSED ? BNK * ROWB : 0;
+  static constexpr int LDS = KT_OFF + KT_BYTES;
+  static constexpr int KCPT = BNK * CPR / THREADS;  // K tile pieces per thread
   static_assert((BMQ * CPR) % THREADS == 0, "tile pieces divide the workgroup");
   static_assert(BMQ == kDkv1TM && BNK == kDkvTN, "tile shape published to the planner");
 };
@@ -463,6 +502,18 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
       kf[kk] = gfrag(kv, (uint32_t)kj * gstride + (16 * kk + 8 * g) * ES, (T*)0);
       vf[kk] = gfrag(vv, (uint32_t)kj * gstride + (16 * kk + 8 * g) * ES, (T*)0);
     }
+    lds_t* dst_t = lds + C::DST_OFF;  // fused dQ: dS^T of the block, [key][query]
+    lds_t* k_t = lds + C::KT_OFF;     // fused dQ: the item's keys, [key][D]
+    if constexpr (C::FUSED) {
+      // the item's 128 keys (rows past the end load as zeros); the barrier
+      // after the first Q/dO block orders these writes before any read
+#pragma unroll
+      for (int c = 0; c < C::KCPT; ++c) {
+        const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
+        *(__attribute__((address_space(3))) i32x4*)(k_t + C::TL::chunk(row, col)) =
+            ld16(kv, (uint32_t)(key_tile0 + row) * gstride + col * 16);
+      }
+    }
 
     i32x4 qr[C::CPT], dr[C::CPT];
     i32x2 lr = {};
@@ -517,7 +568,13 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
       for (int sb = 0; sb < BMQ / 32; ++sb) {
         const int qs0 = qb * BMQ + 32 * sb;  // first query of this 32-row sub-block
         const bool active = wave_on && qs0 < Lq && (!a.causal || qs0 + 31 >= kw0);
-        if (!active) continue;
+        if (!active) {
+          if constexpr (C::FUSED) {  // no pair of this quarter is visible: its dS is 0
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tile_put4<T, BMQ>(dst_t, 32 * w + l32, 32 * sb + 8 * r + 4 * g, 0.f, 0.f, 0.f, 0.f);
+          }
+          continue;
+        }
         const bool masked = a.causal && qs0 < kw0 + 31;
         // dP starts at -Delta of its rows (rows 8k + 4g .. 8k + 4g + 3 of the
         // sub-block are elements 4k .. 4k + 3), so dP - Delta comes out of
@@ -558,6 +615,17 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
           if (kj >= Lk) ds = (f32x16){};
           db_block(db, ds, qs0 - kw0, lane);
         }
+        if constexpr (C::FUSED) {
+          // dS^T of this quarter for the fused dQ product (key row 32w + l32,
+          // query columns 32sb + res_row(i, g)). Keys past the end are 0: their
+          // K row is 0, but their dS = -P Delta has P = exp(bias - lse), which
+          // overflows for a row whose lse is very negative (0 * inf in dQ).
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            tile_put4<T, BMQ>(dst_t, 32 * w + l32, 32 * sb + 8 * r + 4 * g, kj < Lk ? dp[4 * r] : 0.f,
+                              kj < Lk ? dp[4 * r + 1] : 0.f, kj < Lk ? dp[4 * r + 2] : 0.f,
+                              kj < Lk ? dp[4 * r + 3] : 0.f);
+        }
         prio_mfma();
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -570,6 +638,32 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
           }
         }
         prio_valu();
+      }
+      if constexpr (C::FUSED) {
+        // dQ of the block's 64 queries from this item's 128 keys:
+        // dQ = dS K, one 32 x 32 tile (query half, D block) per wave
+        __syncthreads();  // every wave's dS^T is in LDS
+        constexpr int NT = 2 * (D / 32);  // tiles of the block
+        if (w < NT) {
+          const int qh = w & 1, dh = w >> 1;
+          f32x16 acc = (f32x16){};
+#pragma unroll
+          for (int ks = 0; ks < BNK / 16; ++ks)
+            mma(acc, tfrag<BMQ>(dst_t, 16 * ks, 32 * qh, lane, (T*)0), tfrag<D>(k_t, 16 * ks, 32 * dh, lane, (T*)0));
+          // lane: column d = 32 dh + l32, elements i: query qb*BMQ + 32 qh + res_row(i, g)
+          const int d = 32 * dh + l32;
+          float* base = a.dqacc + ((size_t)q0 * H + h) * D + d;
+          if constexpr (kBwdDq == 2) base += (size_t)kt * a.tq * H * D;  // this key tile's partial
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qi = qb * BMQ + 32 * qh + res_row(i, g);
+            if (qi < Lq) {
+              float* p = base + (size_t)qi * H * D;
+              if constexpr (kBwdDq == 1) __hip_atomic_fetch_add(p, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              else *p = acc[i];
+            }
+          }
+        }
       }
       if (qb + 1 < nq) swrite((qb + 1 - qb0) & 1);
       __syncthreads();
@@ -622,7 +716,15 @@ struct DqTiles {
   static constexpr int THREADS = 256;
   using TL = Tile<T, D>;
   static constexpr int ROWB = TL::ROWB;
-  static constexpr int KTILE = BN * ROWB;
+  // Rows of up to 128 bytes: K and V with padded rows (pad_nat: the natural
+  // reads of S^T = K Q^T and dP^T = V dO^T are conflict-free, K's transposed
+  // reads for dQ partly two-way), each tile whole KBs for the direct loads,
+  // and the block taken in halves of 32 keys; with the fewer registers this
+  // leaves, three workgroups share a CU. Wider rows: the permuted tiles
+  // (Tile::swz), conflict-free for both read patterns, two workgroups.
+  static constexpr bool PAD = ROWB <= 128;
+  static constexpr int KS = PAD ? pad_nat(ROWB) : ROWB;
+  static constexpr int KTILE = PAD ? PaddedDma<BN, ROWB, KS>::NBLK * 1024 : BN * ROWB;
   static constexpr int STAGE = 2 * KTILE;
   static constexpr int CPR = ROWB / 16;
   static constexpr int CPT = BN * CPR / THREADS;
@@ -691,8 +793,13 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
     const DmaView vd = dma_view((const char*)a.v + krow, Lk, gstride, C::ROWB);
     auto issue = [&](int j) {
       lds_t* st = lds + (j & 1) * C::STAGE;
-      dma_tile<T, D, BN, 4>(kd, gstride, j * BN, st, w, lane);
-      dma_tile<T, D, BN, 4>(vd, gstride, j * BN, st + C::KTILE, w, lane);
+      if constexpr (C::PAD) {
+        dma_padded_tile<BN, C::ROWB, C::KS, 4>(kd, gstride, j * BN, st, w, lane);
+        dma_padded_tile<BN, C::ROWB, C::KS, 4>(vd, gstride, j * BN, st + C::KTILE, w, lane);
+      } else {
+        dma_tile<T, D, BN, 4>(kd, gstride, j * BN, st, w, lane);
+        dma_tile<T, D, BN, 4>(vd, gstride, j * BN, st + C::KTILE, w, lane);
+      }
     };
     if (n_kv > 0) issue(0);
     wait_vmem();  // Q, dO, lse, Delta and the first K/V block have landed
@@ -720,57 +827,94 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
         // so dP - Delta comes out of the matrix cores; at D = 128 the 16
         // registers this takes are not free.
         constexpr bool kNegDelta = D <= 64;
-        f32x16 sc[BN / 32], dp[BN / 32];
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-          sc[kb] = (f32x16){};
-#pragma unroll
-          for (int i = 0; i < 16; ++i) dp[kb][i] = kNegDelta ? -dlt : 0.f;
-#pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk) {
-            mma(sc[kb], lfrag<D>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), qf[kk]);
-            mma(dp[kb], lfrag<D>(vt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), df[kk]);
-          }
-        }
-        // Element tests only on blocks at the causal diagonal or the sequence end
-        // (at D = 128 a second copy of the loop costs more than the tests save).
-        auto softmax = [&](auto edge_c) {
+        if constexpr (C::PAD) {
+          // The block in halves of 32 keys: scores, dP, dS and the half's dQ
+          // products before the next half, so one half's S and dP are live.
 #pragma unroll
           for (int kb = 0; kb < BN / 32; ++kb) {
+            f32x16 sc = (f32x16){}, dp;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int kj = key0 + 32 * kb + res_row(i, g);
-              float x = sc[kb][i] * a.scale2 - lse2;
-              if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
-              float p = __builtin_amdgcn_exp2f(x);
-              if (decltype(edge_c)::value && ((masked && kj > qi) || (padded && kj >= Lm))) p = 0.f;
-              dp[kb][i] = p * (kNegDelta ? dp[kb][i] : dp[kb][i] - dlt);
+            for (int i = 0; i < 16; ++i) dp[i] = kNegDelta ? -dlt : 0.f;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+              mma(sc, prfrag<C::KS>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), qf[kk]);
+              mma(dp, prfrag<C::KS>(vt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), df[kk]);
+            }
+            // element tests only on blocks at the causal diagonal or the sequence end
+            auto softmax = [&](auto edge_c) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int kj = key0 + 32 * kb + res_row(i, g);
+                float x = sc[i] * a.scale2 - lse2;
+                if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+                float p = __builtin_amdgcn_exp2f(x);
+                if (decltype(edge_c)::value && ((masked && kj > qi) || (padded && kj >= Lm))) p = 0.f;
+                dp[i] = p * (kNegDelta ? dp[i] : dp[i] - dlt);
+              }
+            };
+            if (masked || padded) softmax(std::true_type{});
+            else softmax(std::false_type{});
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const Frag<T> sf = rfrag(dp, c, (T*)0);
+#pragma unroll
+              for (int db = 0; db < D / 32; ++db)
+                mma(dq[db], ptfrag<C::KS>(kt, 32 * kb + 16 * c, 32 * db, lane, (T*)0), sf);
             }
           }
-        };
-        if constexpr (D > 64) {
-#pragma unroll
-          for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int kj = key0 + 32 * kb + res_row(i, g);
-              float x = sc[kb][i] * a.scale2 - lse2;
-              if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
-              float p = __builtin_amdgcn_exp2f(x);
-              if ((masked && kj > qi) || (padded && kj >= Lm)) p = 0.f;
-              dp[kb][i] = p * (dp[kb][i] - dlt);
-            }
-          }
-        } else if (masked || padded) {
-          softmax(std::true_type{});
         } else {
-          softmax(std::false_type{});
-        }
+          f32x16 sc[BN / 32], dp[BN / 32];
 #pragma unroll
-        for (int kc = 0; kc < BN / 16; ++kc) {
-          const Frag<T> sf = rfrag(dp[kc >> 1], kc & 1, (T*)0);
+          for (int kb = 0; kb < BN / 32; ++kb) {
+            sc[kb] = (f32x16){};
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) mma(dq[db], tfrag<D>(kt, 16 * kc, 32 * db, lane, (T*)0), sf);
+            for (int i = 0; i < 16; ++i) dp[kb][i] = kNegDelta ? -dlt : 0.f;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+              mma(sc[kb], lfrag<D>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), qf[kk]);
+              mma(dp[kb], lfrag<D>(vt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), df[kk]);
+            }
+          }
+          // Element tests only on blocks at the causal diagonal or the sequence end
+          // (at D = 128 a second copy of the loop costs more than the tests save).
+          auto softmax = [&](auto edge_c) {
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int kj = key0 + 32 * kb + res_row(i, g);
+                float x = sc[kb][i] * a.scale2 - lse2;
+                if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+                float p = __builtin_amdgcn_exp2f(x);
+                if (decltype(edge_c)::value && ((masked && kj > qi) || (padded && kj >= Lm))) p = 0.f;
+                dp[kb][i] = p * (kNegDelta ? dp[kb][i] : dp[kb][i] - dlt);
+              }
+            }
+          };
+          if constexpr (D > 64) {
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int kj = key0 + 32 * kb + res_row(i, g);
+                float x = sc[kb][i] * a.scale2 - lse2;
+                if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+                float p = __builtin_amdgcn_exp2f(x);
+                if ((masked && kj > qi) || (padded && kj >= Lm)) p = 0.f;
+                dp[kb][i] = p * (dp[kb][i] - dlt);
+              }
+            }
+          } else if (masked || padded) {
+            softmax(std::true_type{});
+          } else {
+            softmax(std::false_type{});
+          }
+#pragma unroll
+          for (int kc = 0; kc < BN / 16; ++kc) {
+            const Frag<T> sf = rfrag(dp[kc >> 1], kc & 1, (T*)0);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) mma(dq[db], tfrag<D>(kt, 16 * kc, 32 * db, lane, (T*)0), sf);
+          }
         }
       }
       wait_vmem();
@@ -793,6 +937,38 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
 }
 
 // ---------------------------------------------------------------------------
+// Fused-dQ study modes (kBwdDq 1, 2): the fp32 accumulator is zeroed before
+// the dK/dV launch (mode 1, a fill kernel), and afterwards one kernel writes
+// dQ = scale * (the accumulator, or the sum of the key tiles' partials in
+// key-tile order) for every sequence that took the dK/dV pass.
+__global__ __launch_bounds__(256) void jfa_dqacc_zero_kernel(float* acc, long n) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) acc[i] = 0.f;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void jfa_dq_fused_out_kernel(BwdArgs a, int D) {
+  const int b = blockIdx.y;
+  const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
+  const int Lk = a.kv_off[b + 1] - a.kv_off[b];
+  if (a.gfirst != nullptr && short_query(Lq, Lk)) return;  // the short-query pass writes these rows
+  const int H = a.H;
+  const long per_row = (long)H * D, n = (long)Lq * per_row;
+  const int nkt = cdiv(Lk, kDkvTN);
+  const size_t plane = (size_t)a.tq * H * D;  // one key tile's partials
+  for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long)gridDim.x * 256) {
+    const int i = (int)(e / per_row);
+    const size_t at = (size_t)q0 * per_row + e;
+    float v = 0.f;
+    if constexpr (kBwdDq == 1) {
+      v = a.dqacc[at];
+    } else {
+      const int last = a.causal ? min(nkt, i / kDkvTN + 1) : nkt;  // key tiles whose item visited row i
+      for (int t = 0; t < last; ++t) v += a.dqacc[t * plane + at];
+    }
+    ((T*)a.dq)[at] = (T)(v * a.scale);
+  }
+}
+
 template <typename K>
 static long persistent_grid(K kern, int& occ, long max_items, int num_cus, int threads = 256) {
   if (occ == 0) {
@@ -887,6 +1063,28 @@ hipError_t launch_dbias(const BwdArgs& a, hipStream_t st) {
   const long nc = (a.B + kDbSeqBlock - 1) / kDbSeqBlock;
   if (nc > 0) hipLaunchKernelGGL(jfa_dbias_part_kernel, dim3((unsigned)(nc * a.H)), dim3(256), 0, st, a);
   if (a.H > 0) hipLaunchKernelGGL(jfa_dbias_kernel, dim3((unsigned)a.H), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+int bwd_dq_mode(bool f32, int D) {
+  if (kBwdDq == 0) return 0;
+  const bool one = f32 ? (D == 32 ? DkvShape<float, 32>::one_role : DkvShape<float, 64>::one_role)
+                       : (D == 32 ? DkvShape<bf16, 32>::one_role
+                                  : D == 64 ? DkvShape<bf16, 64>::one_role : DkvShape<bf16, 128>::one_role);
+  return one ? kBwdDq : 0;
+}
+
+hipError_t launch_dqacc_zero(float* acc, long n, hipStream_t st) {
+  const long g = max(1L, min(4096L, (n + 255) / 256));
+  hipLaunchKernelGGL(jfa_dqacc_zero_kernel, dim3((unsigned)g), dim3(256), 0, st, acc, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_fused_out(bool f32, int D, const BwdArgs& a, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  const dim3 grid(16, (unsigned)a.B);
+  if (f32) hipLaunchKernelGGL(jfa_dq_fused_out_kernel<float>, grid, dim3(256), 0, st, a, D);
+  else hipLaunchKernelGGL(jfa_dq_fused_out_kernel<bf16>, grid, dim3(256), 0, st, a, D);
   return hipGetLastError();
 }
 

@@ -186,6 +186,57 @@ __device__ __forceinline__ Frag<float> tfrag(const lds_t* tile, int rowbase, int
   return f;
 }
 
+// Padded-row LDS tiles: row r at byte r * S, no permutation, so every
+// fragment of a tile is one per-lane base address plus an immediate offset
+// (no per-fragment address registers). Strides:
+//   natural reads (16 lanes per cycle, 16 consecutive rows, one 16-byte
+//   column): S = 16 * odd puts the rows in distinct 4-bank groups; rows of
+//   an even number of 16-byte chunks padded by 16 bytes (pad_nat);
+//   transposing reads (4 consecutive rows x 64 bytes per cycle): S = 64 * odd
+//   puts the rows in distinct 16-bank groups; rows of an odd number of
+//   64-byte quarters as they are, others padded by 64 bytes (pad_tr).
+constexpr int pad_nat(int rowb) { return rowb + 16; }
+constexpr int pad_tr(int rowb) { return (rowb / 64) % 2 == 1 ? rowb : rowb + 64; }
+
+// 8 consecutive elements (row r, elements col .. col+7) of a padded-row tile.
+template <int S>
+__device__ __forceinline__ Frag<bf16> prfrag(const lds_t* tile, int r, int col, bf16*) {
+  Frag<bf16> f;
+  f.v = *(const __attribute__((address_space(3))) bf16x8*)(tile + r * S + col * 2);
+  return f;
+}
+template <int S>
+__device__ __forceinline__ Frag<float> prfrag(const lds_t* tile, int r, int col, float*) {
+  Frag<float> f;
+  f.lo = *(const __attribute__((address_space(3))) f32x4*)(tile + r * S + col * 4);
+  f.hi = *(const __attribute__((address_space(3))) f32x4*)(tile + r * S + col * 4 + 16);
+  return f;
+}
+// Transposed fragment (k down the rows, as tfrag) of a padded-row tile.
+template <int S>
+__device__ __forceinline__ Frag<bf16> ptfrag(const lds_t* tile, int rowbase, int colbase, int lane, bf16*) {
+  const int g = lane >> 5;
+  const int row = rowbase + 4 * g + ((lane & 15) >> 2);
+  const int b = (colbase + ((lane & 31) >> 4) * 16 + (lane & 3) * 4) * 2;
+  s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + row * S + b));
+  s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + (row + 8) * S + b));
+  Frag<bf16> f;
+  bf16x4 x4 = __builtin_bit_cast(bf16x4, x), y4 = __builtin_bit_cast(bf16x4, y);
+  f.v = (bf16x8){x4[0], x4[1], x4[2], x4[3], y4[0], y4[1], y4[2], y4[3]};
+  return f;
+}
+template <int S>
+__device__ __forceinline__ Frag<float> ptfrag(const lds_t* tile, int rowbase, int colbase, int lane, float*) {
+  const int g = lane >> 5;
+  const int b = (colbase + (lane & 31)) * 4;
+  Frag<float> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f.lo[e] = *(const __attribute__((address_space(3))) float*)(tile + (rowbase + 4 * g + e) * S + b);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f.hi[e] = *(const __attribute__((address_space(3))) float*)(tile + (rowbase + 8 + 4 * g + e) * S + b);
+  return f;
+}
+
 // Fragment from half (c = 0 or 1) of a 32x32 fp32 result: elements 8c .. 8c+7,
 // i.e. rows 16c + {4g..4g+3, 8+4g..8+4g+3} of that result.
 __device__ __forceinline__ Frag<bf16> rfrag(const f32x16& s, int c, bf16*) {
@@ -354,6 +405,29 @@ constexpr int dma_loads_per_wave() {
   return ROWS * Tile<T, D>::ROWB / 1024 >= WAVES ? ROWS * Tile<T, D>::ROWB / 1024 / WAVES : 1;
 }
 
+// Direct loads into a padded-row tile (row r at byte r * S of an LDS region
+// of NBLK whole KBs): 1 KB block k holds LDS bytes [1024 k, 1024 k + 1024),
+// so lane l fills byte P = 1024 k + 16 l: row P / S, byte P % S of it. Lanes
+// whose slot is a row's padding, or past the tile's ROWS rows, get an offset
+// beyond the view's range and write zeros.
+template <int ROWS, int ROWB, int S>
+struct PaddedDma {
+  static constexpr int NBLK = (ROWS * S + 1023) / 1024;
+};
+template <int ROWS, int ROWB, int S, int WAVES>
+__device__ __forceinline__ void dma_padded_tile(const DmaView& v, uint32_t gstride, int row0, lds_t* tile, int wave,
+                                                int lane) {
+  constexpr int NBLK = PaddedDma<ROWS, ROWB, S>::NBLK;
+#pragma unroll
+  for (int i = 0; i < (NBLK + WAVES - 1) / WAVES; ++i) {
+    const int k = wave + i * WAVES;
+    if (k >= NBLK) break;  // wave-uniform
+    const int P = k * 1024 + 16 * lane, r = P / S, cb = P % S;
+    const uint32_t goff = (r < ROWS && cb < ROWB) ? (uint32_t)(row0 + r) * gstride + (uint32_t)cb : 0xFFFFFFF0u;
+    dma16(v, tile + k * 1024, goff);
+  }
+}
+
 // s_waitcnt with vmcnt = n (0..63), expcnt and lgkmcnt left alone. The count
 // must be a compile-time constant, so small runtime values are dispatched.
 template <int N>
@@ -397,6 +471,22 @@ __device__ __forceinline__ void wait_vmem() {
 // 0.5-1% slower with it and do not use it.
 __device__ __forceinline__ void prio_mfma() { __builtin_amdgcn_s_setprio(1); }
 __device__ __forceinline__ void prio_valu() { __builtin_amdgcn_s_setprio(0); }
+
+// Instruction interleave for the scheduler, N times: DS LDS reads, MF matrix
+// products, VA other vector ALU instructions (a pattern, not a count: a group
+// takes what is left when fewer remain). Placed at the end of a code region
+// whose matrix products and VALU work are independent, it makes the
+// compiler issue them alternately, so one wave's VALU work runs while its
+// products occupy the matrix core.
+template <int DS, int MF, int VA, int N>
+__device__ __forceinline__ void sched_pattern() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if constexpr (DS > 0) __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+    if constexpr (VA > 0) __builtin_amdgcn_sched_group_barrier(0x002, VA, 0);
+  }
+}
 
 // Work-list header in the caller's workspace: kMaxQueues queues stored one
 // after the other in the item array (one queue per XCD). Each queue's ticket

@@ -44,6 +44,22 @@ namespace jfa {
 #define JFA_SCHED_PERSISTENT 1
 #endif
 
+// Workgroups per CU the register budget is held to: rows of up to 128 bytes
+// (JFA_FWD_BLOCKS; the compiler's allocation gives bf16 at D <= 64 three
+// waves per SIMD at 2) and rows of 256 bytes (JFA_FWD_WIDE_BLOCKS); wider
+// rows one. Tile-shape study choices, as are the block widths (jfa_kernels.h)
+// and JFA_FWD_WIDE_DMA (1: rows of 256 bytes and more arrive by direct loads
+// into LDS, 0: staged through registers).
+#ifndef JFA_FWD_BLOCKS
+#define JFA_FWD_BLOCKS 2
+#endif
+#ifndef JFA_FWD_WIDE_BLOCKS
+#define JFA_FWD_WIDE_BLOCKS 2
+#endif
+#ifndef JFA_FWD_WIDE_DMA
+#define JFA_FWD_WIDE_DMA 0
+#endif
+
 constexpr int kFwdMaskMode = JFA_FWD_MASK_MODE;
 constexpr bool kSchedPersistent = JFA_SCHED_PERSISTENT != 0;
 static_assert(kFwdMaskMode >= 0 && kFwdMaskMode <= 2, "mask mode");
@@ -51,18 +67,25 @@ static_assert(kFwdMaskMode >= 0 && kFwdMaskMode <= 2, "mask mode");
 template <typename T, int D>
 struct FwdTiles {
   static constexpr int BM = 128;  // query rows per item (4 waves x 32)
-  static constexpr int BN = 64;   // keys per block
+  static constexpr int BN = FwdKeys<T, D>::value;  // keys per block
   static constexpr int THREADS = 256;
   using TL = Tile<T, D>;
   static constexpr int ROWB = TL::ROWB;
-  static constexpr int KTILE = BN * ROWB;
-  static constexpr int STAGE = 2 * KTILE;  // K then V
+  // K and V tiles with padded rows: K read naturally (S^T = K Q^T), V read
+  // transposed (O^T += V^T P^T); see pad_nat / pad_tr
+  static constexpr int KS = pad_nat(ROWB), VS = pad_tr(ROWB);
+  // Rows of 256 bytes and more arrive by direct loads into LDS (their staging
+  // registers would cost a wave per SIMD); each tile then spans whole KBs.
+  static constexpr bool DMA = ROWB >= 256 && JFA_FWD_WIDE_DMA;
+  static constexpr int KTILE = DMA ? PaddedDma<BN, ROWB, KS>::NBLK * 1024 : BN * KS;
+  static constexpr int VTILE = DMA ? PaddedDma<BN, ROWB, VS>::NBLK * 1024 : BN * VS;
+  static constexpr int STAGE = KTILE + VTILE;  // K then V
   static constexpr int CPR = ROWB / 16;              // 16-byte pieces per row
   static constexpr int CPT = BN * CPR / THREADS;     // pieces per thread per tile
   static constexpr int BIAS_OFF = 2 * STAGE;
   static constexpr int LDS = BIAS_OFF + 1040;
   static_assert((BN * CPR) % THREADS == 0, "tile pieces divide the workgroup");
-  static_assert(BM == FwdRows<T, D>::value && BN == kFwdTN, "tile shape published to the planner");
+  static_assert(BM == FwdRows<T, D>::value, "tile shape published to the planner");
 };
 
 // PADDED: the padded-dense baseline. Every sequence occupies a fixed-length
@@ -70,10 +93,9 @@ struct FwdTiles {
 // slot is visited, and keys at or past the sequence's true length
 // (a.kv_len[b]) are masked with -inf on every block, element by element, as a
 // conventional kernel over padded tensors does.
-// Resident waves per SIMD the register budget is held to (the compiler's
-// allocation gives bf16 at D <= 64 three).
+
 template <typename T, int D> constexpr int fwd_min_waves() {
-  return D * sizeof(T) >= 512 ? 1 : 2;
+  return D * sizeof(T) >= 512 ? 1 : D * sizeof(T) >= 256 ? JFA_FWD_WIDE_BLOCKS : JFA_FWD_BLOCKS;
 }
 
 template <typename T, int D, bool BIAS, bool PADDED = false>
@@ -124,8 +146,16 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = gfrag(qv, (uint32_t)qi * gstride + (16 * kk + 8 * g) * ES, (T*)0);
 
-    i32x4 kr[C::CPT], vr[C::CPT];
+    i32x4 kr[C::DMA ? 1 : C::CPT], vr[C::DMA ? 1 : C::CPT];
+    const DmaView kd = dma_view((const char*)a.k + krow, Lk, gstride, C::ROWB);
+    const DmaView vd = dma_view((const char*)a.v + krow, Lk, gstride, C::ROWB);
     auto gload = [&](int j) {
+      if constexpr (C::DMA) {  // block j straight into stage j & 1
+        lds_t* st = lds + (j & 1) * C::STAGE;
+        dma_padded_tile<BN, C::ROWB, C::KS, 4>(kd, gstride, j * BN, st, w, lane);
+        dma_padded_tile<BN, C::ROWB, C::VS, 4>(vd, gstride, j * BN, st + C::KTILE, w, lane);
+        return;
+      }
 #pragma unroll
       for (int c = 0; c < C::CPT; ++c) {
         const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
@@ -135,12 +165,15 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
       }
     };
     auto swrite = [&](int s) {
+      if constexpr (C::DMA) {  // the direct loads of this stage have landed
+        wait_vmem();
+        return;
+      }
 #pragma unroll
       for (int c = 0; c < C::CPT; ++c) {
         const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
-        const int o = C::TL::chunk(row, col);
-        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + o) = kr[c];
-        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + C::KTILE + o) = vr[c];
+        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + row * C::KS + col * 16) = kr[c];
+        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + C::KTILE + row * C::VS + col * 16) = vr[c];
       }
     };
     if (n_kv > 0) {
@@ -184,7 +217,7 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
           sc[kb] = (f32x16){};
 #pragma unroll
           for (int kk = 0; kk < D / 16; ++kk)
-            mma(sc[kb], lfrag<D>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), qf[kk]);
+            mma(sc[kb], prfrag<C::KS>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), qf[kk]);
         }
         prio_valu();
         // Scores in log2 units: x = s * scale * log2(e) (+ bias * log2(e)).
@@ -258,7 +291,7 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
           const Frag<T> pf = rfrag(sc[kc >> 1], kc & 1, (T*)0);
           if constexpr (kOpSum) lb = frag_sum(pf, lb);
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) mma(o[db], tfrag<D>(vt, 16 * kc, 32 * db, lane, (T*)0), pf);
+          for (int db = 0; db < D / 32; ++db) mma(o[db], ptfrag<C::VS>(vt, 16 * kc, 32 * db, lane, (T*)0), pf);
         }
         prio_valu();
       }
@@ -313,7 +346,7 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
             float dot = 0.f;
 #pragma unroll 1
             for (int c = 0; c < C::CPR; ++c) {
-              const i32x4 kq = *(const __attribute__((address_space(3))) i32x4*)(kt + C::TL::chunk(r, c));
+              const i32x4 kq = *(const __attribute__((address_space(3))) i32x4*)(kt + r * C::KS + c * 16);
               const i32x4 qq = ld16(qv, (uint32_t)qi * gstride + c * 16);
               if constexpr (sizeof(T) == 2) {
                 const bf16x8 k8 = __builtin_bit_cast(bf16x8, kq), q8 = __builtin_bit_cast(bf16x8, qq);
@@ -375,6 +408,11 @@ static hipError_t launch_fwd_t(const FwdArgs& a, bool bias, long max_items, int 
   const long grid = kSchedPersistent ? max(1L, min(max_items, (long)num_cus * occ)) : max(1L, max_items);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+int fwd_tile_keys(bool f32, int D) {
+  if (f32) return D == 32 ? FwdKeys<float, 32>::value : FwdKeys<float, 64>::value;
+  return D == 32 ? FwdKeys<bf16, 32>::value : (D == 64 ? FwdKeys<bf16, 64>::value : FwdKeys<bf16, 128>::value);
 }
 
 int fwd_tile_rows(bool f32, int D) {

@@ -60,6 +60,8 @@ struct BwdArgs {
   int* gfirst_kv;
   float* dbpart;       // [ceil(B / kDbSeqBlock)][H][257]: sums over blocks of sequences
   float* dbias;        // [H][257] fp32 output
+  float* dqacc;        // study designs with dQ fused into the dK/dV pass: fp32 [Tq, H, D] accumulator (1)
+                       // or [key tile][Tq, H, D] partials (2); null in the library
   const int* kv_len;   // padded-dense baseline only: [B] true key count of each fixed-length slot
 };
 
@@ -101,8 +103,20 @@ __host__ __device__ inline bool short_query(int Lq, int Lk) { return Lq <= kSqQM
 // workgroup (32 query rows each) depend on the element type and D.
 template <typename T, int D> struct FwdWaves { static constexpr int value = 4; };
 template <typename T, int D> struct FwdRows { static constexpr int value = 32 * FwdWaves<T, D>::value; };
-constexpr int kFwdTN = 64;
+// Keys per block of the forward, for rows of up to 128 bytes (JFA_FWD_BN)
+// and for wider ones (JFA_FWD_WIDE_BN): compile-time choices of the
+// tile-shape study (the library takes the defaults).
+#ifndef JFA_FWD_BN
+#define JFA_FWD_BN 64
+#endif
+#ifndef JFA_FWD_WIDE_BN
+#define JFA_FWD_WIDE_BN 64
+#endif
+template <typename T, int D> struct FwdKeys {
+  static constexpr int value = D * (int)sizeof(T) >= 256 ? JFA_FWD_WIDE_BN : JFA_FWD_BN;
+};
 int fwd_tile_rows(bool f32, int D);
+int fwd_tile_keys(bool f32, int D);
 // dK/dV pass: rows of 128 bytes or less (bf16 D <= 64, fp32 D = 32) use the
 // one-role kernel with 64-row query blocks, wider rows the two-role kernel
 // with 32-row blocks.
@@ -122,6 +136,13 @@ hipError_t launch_dq(bool f32, int D, const BwdArgs& a, bool bias, long max_item
 hipError_t launch_sq(bool f32, int D, const BwdArgs& a, bool bias, bool dbias, long max_items, int num_cus,
                      hipStream_t st);
 hipError_t launch_dbias(const BwdArgs& a, hipStream_t st);
+// Design of the backward's dQ (a compile-time study choice; 0 = the split
+// passes): 1 or 2 when that build fuses dQ into the dK/dV pass for this
+// element type and D. Then the dQ pass gets no items, the accumulator is
+// zeroed first (1) and launch_dq_fused_out writes dQ after the dK/dV pass.
+int bwd_dq_mode(bool f32, int D);
+hipError_t launch_dqacc_zero(float* acc, long n, hipStream_t st);
+hipError_t launch_dq_fused_out(bool f32, int D, const BwdArgs& a, hipStream_t st);
 hipError_t launch_plan(const PlanArgs& a, int npass, hipStream_t st);
 // The backward's lists (passes of p) and Delta of every row (a.rowc), one launch.
 hipError_t launch_bwd_prep(const PlanArgs& p, int npass, bool f32, int D, const BwdArgs& a, hipStream_t st);
