@@ -67,7 +67,7 @@ def test_small_workload_parity(cfg):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("causal,bias,asym", [(False, False, False), (True, False, False), (False, True, True),
-                                              (True, True, True)])
+                                              (True, False, True), (True, True, True)])
 def test_feature_grid(dtype, D, causal, bias, asym):
     if dtype == "f32" and D == 128:
         batch = gen.make_batch(gen.Workload("grid", 2, 1, D, dtype, causal, bias, gen.LengthDist("uniform", 1, 30)))
@@ -285,6 +285,43 @@ def test_masking_study_variants(mode, cfg):
         jfa._LIB = None
         jfa.LIB_PATH = path
         _check(gen.make_batch(SMALL[cfg]), with_bwd=False, label=f"masking mode {mode} cfg{cfg}")
+    finally:
+        jfa._LIB = None
+        jfa.LIB_PATH = saved
+
+
+_TILE_CASES = {
+    # sizes spanning several tiles and ragged tails; causal, bias and
+    # asymmetric lengths; every D the variants change
+    "small_cfg2": lambda: gen.make_batch(SMALL[2]),
+    "small_cfg3": lambda: gen.make_batch(SMALL[3]),
+    "d128_causal_bias_asym": lambda: gen.make_batch(
+        gen.Workload("tile", 6, 2, 128, "bf16", True, True, gen.LengthDist("fixed", 1, 1), seed=91),
+        q_lengths=[300, 70, 1, 0, 257, 640], kv_lengths=[300, 40, 1, 5, 700, 640]),
+    "d64_causal_bias_asym": lambda: gen.make_batch(
+        gen.Workload("tile", 6, 2, 64, "bf16", True, True, gen.LengthDist("fixed", 1, 1), seed=92),
+        q_lengths=[300, 70, 1, 0, 257, 640], kv_lengths=[300, 40, 1, 5, 700, 640]),
+    "edges_d128": lambda: gen.make_batch(
+        gen.Workload("tile", 6, 2, 128, "bf16", False, False, gen.LengthDist("fixed", 1, 1), seed=93),
+        q_lengths=[63, 64, 65, 255, 256, 257], kv_lengths=[63, 64, 65, 255, 256, 257]),
+}
+
+
+@pytest.mark.parametrize("variant", ["n128", "b3", "pf0", "wdma", "w32b3", "pp", "pp64"])
+@pytest.mark.parametrize("case", sorted(_TILE_CASES))
+def test_tile_study_variants(variant, case):
+    """Every variant of the forward's tile-shape study computes the forward
+    the oracle does (the study variants change tile shapes, the ring and the
+    schedule, not the arithmetic of a row)."""
+    from variable_length_attention_jfa_amd import tile_study
+    path = tile_study.lib_path(variant)
+    if not build.is_current(path):
+        pytest.skip(STUDY_SKIP)
+    saved = jfa.LIB_PATH
+    try:
+        jfa._LIB = None
+        jfa.LIB_PATH = path
+        _check(_TILE_CASES[case](), with_bwd=False, label=f"tile variant {variant} {case}")
     finally:
         jfa._LIB = None
         jfa.LIB_PATH = saved

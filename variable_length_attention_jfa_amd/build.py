@@ -89,10 +89,12 @@ def build_studies(jobs: int = 8) -> None:
     choices, under _study/): -inf masking modes 1 and 2, the list-order and
     grid variants of the scheduling study, unswizzled LDS tiles, and the
     backward with dQ fused into the dK/dV pass (atomic adds, ordered
-    partials). Their GPU tests skip when they are not built."""
-    from . import mask_study, sched_study
+    partials), and the forward's tile-shape variants. Their GPU tests skip
+    when they are not built."""
+    from . import mask_study, sched_study, tile_study
     mask_study.build_variants(jobs)
     sched_study.build_variants(jobs)
+    tile_study.build_variants(jobs)
     build(jobs=jobs, defines=["JFA_LDS_SWIZZLE=0"], out=os.path.join(PKG, "_study", "libjfa_noswz.so"),
           objdir=os.path.join(BUILD, "noswz"))
     for mode in (1, 2):  # dQ fused into the dK/dV pass: atomic adds, ordered partials

@@ -238,7 +238,7 @@ jfa_status fwd_impl(bool f32, const void* q, const void* k, const void* v, const
   pa.H = H;
   pa.causal = causal ? 1 : 0;
   const bool short_on = short_pass_on(max_kv_len) && !pad_kv_len;
-  pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::fwd_tile_rows(f32, D), jfa::fwd_tile_keys(f32, D),
+  pa.pass[0] = {(int4*)(w + L.items), (PlanHeader*)(w + L.hdr), (long)L.cap, jfa::fwd_tile_rows(f32, D, pad_kv_len != nullptr), jfa::fwd_tile_keys(f32, D),
                 jfa::kPassQ, jfa::kPlanQueues, short_on ? jfa::kSqQMax : -1, nullptr};
   pa.pass[1] = {(int4*)(w + L.items_sq), (PlanHeader*)(w + L.hdr_sq), (long)L.cap_sq, jfa::kSqQMax, jfa::kSqKC,
                 jfa::kPassSQ, jfa::kPlanQueues, -1, (int*)(w + L.gfirst)};

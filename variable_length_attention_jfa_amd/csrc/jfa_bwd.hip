@@ -695,9 +695,14 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
 
 // dK/dV kernel: one role per wave for rows of up to 128 bytes, score and
 // gradient wave pairs for wider rows.
+// Widest rows (bytes) the one-role kernel takes; wider ones go to the paired
+// kernel (a compile-time choice; the library keeps 128).
+#ifndef JFA_DKV_ONE_ROLE_ROWB
+#define JFA_DKV_ONE_ROLE_ROWB 128
+#endif
 template <typename T, int D>
 struct DkvShape {
-  static constexpr bool one_role = D * sizeof(T) <= 128;
+  static constexpr bool one_role = D * sizeof(T) <= JFA_DKV_ONE_ROLE_ROWB;
   static constexpr int threads = one_role ? Dkv1Tiles<T, D>::THREADS : 512;
 };
 

@@ -488,6 +488,24 @@ __device__ __forceinline__ void sched_pattern() {
   }
 }
 
+// Operand prefetch for a run of N matrix products whose operands come from
+// LDS, DS reads per product: the first AHEAD products' reads are issued up
+// front, then each product is followed by the reads of the one AHEAD places
+// later, so AHEAD products' operands are in flight instead of each read
+// being waited for right before its product.
+template <int N, int DS, int AHEAD>
+__device__ __forceinline__ void sched_prefetch() {
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, DS, 1);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, DS, 1);
+  }
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+}
+
 // Work-list header in the caller's workspace: kMaxQueues queues stored one
 // after the other in the item array (one queue per XCD). Each queue's ticket
 // sits on its own 128-byte line, away from the read-only words, so that the

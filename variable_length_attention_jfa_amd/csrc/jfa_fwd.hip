@@ -59,6 +59,16 @@ namespace jfa {
 #ifndef JFA_FWD_WIDE_DMA
 #define JFA_FWD_WIDE_DMA 0
 #endif
+// Matrix products whose LDS operands are read ahead of them, for rows of 256
+// bytes and more (0: the compiler's order, which waits for each product's
+// reads right before it).
+#ifndef JFA_FWD_PREFETCH
+#define JFA_FWD_PREFETCH 2
+#endif
+// The same for the two-group kernel (at least 1).
+#ifndef JFA_FWD_PP_AHEAD
+#define JFA_FWD_PP_AHEAD 2
+#endif
 
 constexpr int kFwdMaskMode = JFA_FWD_MASK_MODE;
 constexpr bool kSchedPersistent = JFA_SCHED_PERSISTENT != 0;
@@ -85,7 +95,9 @@ struct FwdTiles {
   static constexpr int BIAS_OFF = 2 * STAGE;
   static constexpr int LDS = BIAS_OFF + 1040;
   static_assert((BN * CPR) % THREADS == 0, "tile pieces divide the workgroup");
-  static_assert(BM == FwdRows<T, D>::value, "tile shape published to the planner");
+  // the two-group shapes take this kernel only for the padded-dense baseline,
+  // which plans with 128-row tiles
+  static_assert(FwdPingPong<T, D>::value || BM == FwdRows<T, D>::value, "tile shape published to the planner");
 };
 
 // PADDED: the padded-dense baseline. Every sequence occupies a fixed-length
@@ -219,6 +231,7 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
           for (int kk = 0; kk < D / 16; ++kk)
             mma(sc[kb], prfrag<C::KS>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), qf[kk]);
         }
+        if constexpr (JFA_FWD_PREFETCH > 0 && sizeof(T) == 2 && C::ROWB >= 256) sched_prefetch<(BN / 32) * (D / 16), 1, JFA_FWD_PREFETCH>();
         prio_valu();
         // Scores in log2 units: x = s * scale * log2(e) (+ bias * log2(e)).
         float mx = -INFINITY;
@@ -293,6 +306,7 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) mma(o[db], ptfrag<C::VS>(vt, 16 * kc, 32 * db, lane, (T*)0), pf);
         }
+        if constexpr (JFA_FWD_PREFETCH > 0 && sizeof(T) == 2 && C::ROWB >= 256) sched_prefetch<(BN / 16) * (D / 32), 2, JFA_FWD_PREFETCH>();
         prio_valu();
       }
       if (j + 1 < n_kv) swrite((j + 1) & 1);
@@ -395,18 +409,343 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
   }
 }
 
+// Two-group forward for bf16 rows of 256 bytes (D = 128). Eight waves and
+// 256 query rows per item: waves 0-3 (group 0) and 4-7 (group 1) own 32
+// rows each, so the two waves that share a SIMD sit in different groups.
+// The work of a key block is cut into a matrix phase (the PV product of the
+// block before, then QK^T of this block) and a vector phase (the online
+// softmax of this block), and the two groups run them half a block apart,
+// with a workgroup barrier between phases: while one group's waves issue
+// MFMAs the other's run the softmax. Without the barriers the two waves of a
+// SIMD fall into the same phase and take turns on one unit at a time. The
+// arithmetic per row is that of jfa_fwd_kernel, in the same order.
+//
+// Step s (s = 0 .. n_kv) works on K block s and V block s-1, one LDS stage:
+//   phase 2s  : group 0 matrix (PV s-1, QK^T s), group 1 vector (softmax s-1)
+//   phase 2s+1: group 0 vector (softmax s),      group 1 matrix (PV s-1, QK^T s)
+// Step s+1's tiles are loaded into registers at the start of step s and
+// written to the other stage at its end.
+template <int D, bool BIAS>
+__global__ __launch_bounds__(512, 1) void jfa_fwd_pp_kernel(FwdArgs a) {
+  using T = bf16;
+  static_assert(kFwdMaskMode == 0, "the two-group kernel subtracts the pad terms");
+  constexpr int THREADS = 512, BM = 256, BN = 64, ES = 2;
+  constexpr int ROWB = Tile<T, D>::ROWB, KS = pad_nat(ROWB), VS = pad_tr(ROWB);
+  constexpr int KTILE = PaddedDma<BN, ROWB, KS>::NBLK * 1024, STAGE = KTILE + PaddedDma<BN, ROWB, VS>::NBLK * 1024;
+  constexpr int CPR = ROWB / 16;  // 16-byte pieces per row
+  constexpr int BIAS_OFF = 2 * STAGE, LDS = BIAS_OFF + 1040;
+  static_assert(BM == FwdRows<T, D>::value && BN == FwdKeys<T, D>::value, "tile shape published to the planner");
+  static_assert(kShortLds <= LDS, "combining step fits the LDS");
+  __shared__ __attribute__((aligned(16))) char smem[LDS];
+  __shared__ QueueCursor qcur;
+  lds_t* lds = (lds_t*)smem;
+  __attribute__((address_space(3))) float* bias_lds = (__attribute__((address_space(3))) float*)(lds + BIAS_OFF);
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool grp0 = w < 4;
+  const int H = a.H;
+  const uint32_t gstride = (uint32_t)H * ROWB;
+  for_short_groups(a.gfirst, a.B * H, lds, [&](int gi) { fsq_merge<T, D, THREADS>(a, gi, lds); });
+  load_queues(a.hdr, &qcur);
+  TicketState tk;
+
+  for (;;) {
+    const int it = next_item(a.hdr, &qcur, tk);
+    if (it < 0) break;
+    const int4 item = a.items[it];
+    const int b = item.x, h = item.y, qt = item.z;
+    const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
+    const int k0 = a.kv_off[b], Lk = a.kv_off[b + 1] - k0;
+    const int row0 = qt * BM;
+    const int n_kv = a.causal ? cdiv(min(min(row0 + BM, Lq), Lk), BN) : cdiv(Lk, BN);
+
+    const size_t qrow = ((size_t)q0 * H + h) * ROWB, krow = ((size_t)k0 * H + h) * ROWB;
+    const View qv = seq_view((const char*)a.q + qrow, Lq, gstride, ROWB);
+    const View kv = seq_view((const char*)a.k + krow, Lk, gstride, ROWB);
+    const View vv = seq_view((const char*)a.v + krow, Lk, gstride, ROWB);
+    if (BIAS) {
+      for (int i = tid; i < kBiasLen; i += THREADS) bias_lds[i] = a.bias[h * kBiasLen + i] * kLog2e;
+    }
+
+    const int wr0 = row0 + 32 * w;  // first query row of this wave
+    const bool wave_on = wr0 < Lq;
+    const int qi = wr0 + l32;
+    Frag<T> qf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = gfrag(qv, (uint32_t)qi * gstride + (16 * kk + 8 * g) * ES, (T*)0);
+
+    // Step s stages K block s (s < n_kv) and V block s-1 (s >= 1) in LDS
+    // stage s & 1, by direct loads (no staging registers); s is uniform.
+    // Rows past the sequence's end and the row padding read as zeros.
+    const DmaView kd = dma_view((const char*)a.k + krow, Lk, gstride, ROWB);
+    const DmaView vd = dma_view((const char*)a.v + krow, Lk, gstride, ROWB);
+    auto load_step = [&](int s) {
+      lds_t* st = lds + (s & 1) * STAGE;
+      // the lane id read afresh, so that the per-lane offsets are recomputed
+      // on each step (a few VALU ops) rather than held in registers
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      if (s < n_kv) dma_padded_tile<BN, ROWB, KS, 8>(kd, gstride, s * BN, st, w, ln);
+      if (s >= 1) dma_padded_tile<BN, ROWB, VS, 8>(vd, gstride, (s - 1) * BN, st + KTILE, w, ln);
+    };
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = (f32x16){};
+    f32x16 sc[BN / 32];  // S^T of a block, then its P until the next matrix phase
+    // l: sum of the fp32 P (for lse); lb: sum of the bf16-rounded P the PV
+    // product consumes (O is normalised by it), added when PV rounds them
+    float m = kNegInit, l = 0.f, lb = 0.f;
+    float l_pre = 0.f, lb_pre = 0.f;  // sums before the item's last block (cancellation guard)
+    int last_tile = -1;
+    bool last_masked = false;
+    // this wave's rows see block j (j < n_kv)
+    auto active = [&](int j) { return wave_on && (!a.causal || j * BN <= wr0 + 31); };
+
+    auto pv = [&](int s) {  // PV of block s-1 (its P in sc), V tile of step s
+      const lds_t* vt = lds + (s & 1) * STAGE + KTILE;
+#pragma unroll
+      for (int kc = 0; kc < BN / 16; ++kc) {
+        const Frag<T> pf = rfrag(sc[kc >> 1], kc & 1, (T*)0);
+        lb = frag_sum(pf, lb);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) mma(o[db], ptfrag<VS>(vt, 16 * kc, 32 * db, lane, (T*)0), pf);
+      }
+      sched_prefetch<(BN / 16) * (D / 32), 2, JFA_FWD_PP_AHEAD>();  // operands AHEAD products ahead, no more
+    };
+    auto qk = [&](int s) {  // S^T of block s, K tile of step s
+      const lds_t* kt = lds + (s & 1) * STAGE;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        sc[kb] = (f32x16){};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+          mma(sc[kb], prfrag<KS>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), qf[kk]);
+      }
+      sched_prefetch<(BN / 32) * (D / 16), 1, JFA_FWD_PP_AHEAD>();
+    };
+    // matrix phase of step s (1 <= s < n_kv)
+    auto matrix = [&](int s) {
+      if (active(s - 1)) pv(s);
+      if (active(s)) qk(s);
+    };
+
+    auto vector = [&](int j) {
+      if (!active(j)) return;
+      const int key0 = j * BN;
+      const bool masked = a.causal && (key0 + BN - 1 > wr0);  // with the subtraction, masked blocks are causal ones
+      last_tile = j;
+      last_masked = masked;
+      float mx = -INFINITY;
+      const bool plain = !BIAS && !masked;
+      if (plain) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+        mx = half_max(mx) * a.scale2;
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kj = key0 + 32 * kb + res_row(i, g);
+            float x = sc[kb][i] * a.scale2;
+            if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+            if (masked && (kj > qi || kj >= Lk)) x = -INFINITY;  // a masked block also drops its pad keys
+            sc[kb][i] = x;
+            mx = fmaxf(mx, x);
+          }
+        }
+        mx = half_max(mx);
+      }
+      const bool grow = mx > m + kRescaleSlack;
+      if (__any(grow)) {
+        const float mn = grow ? mx : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        m = mn;
+        l *= alpha;
+        lb *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      }
+      if (j + 1 == n_kv) {
+        l_pre = l;
+        lb_pre = lb;
+      }
+      if (plain) {
+        const float nm = -m;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][i], a.scale2, nm));
+            sc[kb][i] = p;
+            l += p;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(sc[kb][i] - m);
+            sc[kb][i] = p;
+            l += p;
+          }
+        }
+      }
+    };
+
+    // Steps 0 .. n_kv in 2 n_kv + 2 phases; step 0 (QK^T of block 0) and
+    // step n_kv (PV of the last block) are written out, steps 1 .. n_kv - 1
+    // are the loop. Loads of step s + 1 go out at the start of step s and
+    // land in LDS at its end. One loop per group, each a straight sequence
+    // of its two phases; both pass the same barriers.
+    if (n_kv > 0) load_step(0);
+    wait_vmem();
+    __syncthreads();
+    if (n_kv > 0) {
+      // step 0
+      load_step(1);
+      if (grp0 && active(0)) qk(0);
+      __syncthreads();
+      if (grp0) vector(0);
+      else if (active(0)) qk(0);
+      wait_vmem();
+      __syncthreads();
+      // steps 1 .. n_kv - 1
+      if (grp0) {
+        for (int s = 1; s < n_kv; ++s) {
+          load_step(s + 1);
+          matrix(s);
+          __syncthreads();
+          vector(s);
+          wait_vmem();
+          __syncthreads();
+        }
+      } else {
+        for (int s = 1; s < n_kv; ++s) {
+          load_step(s + 1);
+          vector(s - 1);
+          __syncthreads();
+          matrix(s);
+          wait_vmem();
+          __syncthreads();
+        }
+      }
+      // step n_kv: PV of the last block
+      if (grp0) {
+        if (active(n_kv - 1)) pv(n_kv);
+      } else {
+        vector(n_kv - 1);
+      }
+      __syncthreads();
+      if (!grp0 && active(n_kv - 1)) pv(n_kv);
+    }
+
+    // Epilogue as in jfa_fwd_kernel. The last block of a row that still needs
+    // the pad terms removed is never a causal (masked) block, so it is block
+    // n_kv - 1, whose K tile (stage (n_kv - 1) & 1) no later step overwrote.
+    float lt = l + other_half(l);
+    float lbt = lb + other_half(lb);
+    if (wave_on && last_tile >= 0 && !last_masked) {
+      const int pad1 = (last_tile + 1) * BN;
+      if (pad1 > Lk) {
+        float pads, pads_b;
+        if (!BIAS) {
+          const float pe = __builtin_amdgcn_exp2f(-m);
+          pads = (float)(pad1 - Lk) * pe;
+          pads_b = (float)(pad1 - Lk) * as_operand(pe, (T*)0);
+        } else {
+          float sub = 0.f, subb = 0.f;
+          for (int kj = Lk + g; kj < pad1; kj += 2) {
+            const float pe =
+                __builtin_amdgcn_exp2f(bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius] - m);
+            sub += pe;
+            subb += as_operand(pe, (T*)0);
+          }
+          pads = sub + other_half(sub);
+          pads_b = subb + other_half(subb);
+        }
+        const float full = lt;
+        lt -= pads;
+        lbt -= pads_b;
+        // cancellation guard (see jfa_fwd_kernel)
+        const bool cancel = !(lt > full * 0x1p-12f);
+        if (__any(cancel)) {
+          const lds_t* kt = lds + (last_tile & 1) * STAGE;
+          const int key0 = last_tile * BN;
+          float sv = 0.f, svb = 0.f;
+#pragma unroll 1
+          for (int r = g; r < BN; r += 2) {
+            const int kj = key0 + r;
+            if (kj >= Lk) break;
+            float dot = 0.f;
+#pragma unroll 1
+            for (int c = 0; c < CPR; ++c) {
+              const i32x4 kq = *(const __attribute__((address_space(3))) i32x4*)(kt + r * KS + c * 16);
+              const i32x4 qq = ld16(qv, (uint32_t)qi * gstride + c * 16);
+              const bf16x8 k8 = __builtin_bit_cast(bf16x8, kq), q8 = __builtin_bit_cast(bf16x8, qq);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) dot += (float)k8[e] * (float)q8[e];
+            }
+            float x = dot * a.scale2;
+            if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+            const float pe = __builtin_amdgcn_exp2f(x - m);
+            sv += pe;
+            svb += as_operand(pe, (T*)0);
+          }
+          const float fixed = l_pre + other_half(l_pre) + sv + other_half(sv);
+          const float fixedb = lb_pre + other_half(lb_pre) + svb + other_half(svb);
+          if (cancel) {
+            lt = fixed;
+            lbt = fixedb;
+          }
+        }
+      }
+    }
+    if (wave_on) {
+      const float inv = lbt > 0.f ? 1.0f / lbt : 0.f;
+      const View ov = seq_view((char*)a.out + qrow, Lq, gstride, ROWB);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = 32 * db + 8 * r + 4 * g;
+          store4(ov, (uint32_t)qi * gstride + d * ES, o[db][4 * r] * inv, o[db][4 * r + 1] * inv,
+                 o[db][4 * r + 2] * inv, o[db][4 * r + 3] * inv, (T*)0);
+        }
+      }
+      if (g == 0) {
+        const float lse = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+        const View lv = seq_view(a.lse + (size_t)q0 * H + h, Lq, (uint32_t)H * 4, 4);
+        st4f(lv, (uint32_t)qi * H * 4, lse);
+      }
+    }
+    if constexpr (!kSchedPersistent) break;  // one item per workgroup
+  }
+}
+
 template <typename T, int D, bool PADDED = false>
 static hipError_t launch_fwd_t(const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
-  auto kern = bias ? jfa_fwd_kernel<T, D, true, PADDED> : jfa_fwd_kernel<T, D, false, PADDED>;
+  constexpr bool PP = FwdPingPong<T, D>::value && !PADDED;
+  constexpr int threads = PP ? 512 : 256;
+  void (*kern)(FwdArgs);
+  if constexpr (PP)
+    kern = bias ? jfa_fwd_pp_kernel<D, true> : jfa_fwd_pp_kernel<D, false>;
+  else
+    kern = bias ? jfa_fwd_kernel<T, D, true, PADDED> : jfa_fwd_kernel<T, D, false, PADDED>;
   static int occ_b = 0, occ_n = 0;
   int& occ = bias ? occ_b : occ_n;
   if (occ == 0) {
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, 256, 0);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, 0);
     if (e != hipSuccess) return e;
     if (occ < 1) occ = 1;
   }
   const long grid = kSchedPersistent ? max(1L, min(max_items, (long)num_cus * occ)) : max(1L, max_items);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -415,7 +754,8 @@ int fwd_tile_keys(bool f32, int D) {
   return D == 32 ? FwdKeys<bf16, 32>::value : (D == 64 ? FwdKeys<bf16, 64>::value : FwdKeys<bf16, 128>::value);
 }
 
-int fwd_tile_rows(bool f32, int D) {
+int fwd_tile_rows(bool f32, int D, bool padded) {
+  if (padded) return FwdTiles<bf16, 128>::BM;  // every D: the 4-wave kernel's 128 rows
   if (f32) return D == 32 ? FwdRows<float, 32>::value : FwdRows<float, 64>::value;
   return D == 32 ? FwdRows<bf16, 32>::value : (D == 64 ? FwdRows<bf16, 64>::value : FwdRows<bf16, 128>::value);
 }

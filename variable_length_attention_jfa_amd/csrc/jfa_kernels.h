@@ -100,8 +100,22 @@ constexpr int kSqQMax = 64, kSqKC = 1024, kSqKT = 64;
 __host__ __device__ inline bool short_query(int Lq, int Lk) { return Lq <= kSqQMax && Lk > kSqKC; }
 
 // Tile shapes (query rows x keys) of each kernel. The forward's waves per
-// workgroup (32 query rows each) depend on the element type and D.
-template <typename T, int D> struct FwdWaves { static constexpr int value = 4; };
+// workgroup (32 query rows each) depend on the element type and D. The
+// two-group kernel (8 waves in two groups that alternate matrix and vector
+// phases, 256 rows per item) is a compile-time study choice for bf16 D = 128
+// (JFA_FWD_PINGPONG) and D = 64 (JFA_FWD_PINGPONG_NARROW); the library
+// builds the 4-wave kernel for every shape.
+#ifndef JFA_FWD_PINGPONG
+#define JFA_FWD_PINGPONG 0
+#endif
+#ifndef JFA_FWD_PINGPONG_NARROW
+#define JFA_FWD_PINGPONG_NARROW 0
+#endif
+template <typename T, int D> struct FwdPingPong {
+  static constexpr bool value = sizeof(T) == 2 && ((D == 128 && JFA_FWD_PINGPONG != 0) ||
+                                                   (D == 64 && JFA_FWD_PINGPONG_NARROW != 0));
+};
+template <typename T, int D> struct FwdWaves { static constexpr int value = FwdPingPong<T, D>::value ? 8 : 4; };
 template <typename T, int D> struct FwdRows { static constexpr int value = 32 * FwdWaves<T, D>::value; };
 // Keys per block of the forward, for rows of up to 128 bytes (JFA_FWD_BN)
 // and for wider ones (JFA_FWD_WIDE_BN): compile-time choices of the
@@ -115,7 +129,8 @@ template <typename T, int D> struct FwdRows { static constexpr int value = 32 * 
 template <typename T, int D> struct FwdKeys {
   static constexpr int value = D * (int)sizeof(T) >= 256 ? JFA_FWD_WIDE_BN : JFA_FWD_BN;
 };
-int fwd_tile_rows(bool f32, int D);
+// padded: the padded-dense baseline, which always takes the 4-wave kernel.
+int fwd_tile_rows(bool f32, int D, bool padded = false);
 int fwd_tile_keys(bool f32, int D);
 // dK/dV pass: rows of 128 bytes or less (bf16 D <= 64, fp32 D = 32) use the
 // one-role kernel with 64-row query blocks, wider rows the two-role kernel

@@ -30,7 +30,7 @@ __device__ __forceinline__ void for_short_groups(const int* gfirst, int ngroups,
     if (threadIdx.x == 0) *count = 0;
     __syncthreads();
     const int k = base + (int)threadIdx.x;
-    if (k < per) {
+    if (threadIdx.x < 256 && k < per) {  // the list holds 256 groups
       const int gi = (int)blockIdx.x + k * (int)gridDim.x;
       if (gfirst[gi] >= 0) list[atomicAdd(count, 1)] = gi;
     }
@@ -46,11 +46,11 @@ __device__ __forceinline__ void for_short_groups(const int* gfirst, int ngroups,
 // ln 2, with the chunks in list order. The first 64 threads find each row's
 // max and sum of weights, the weights go through LDS in batches of 16
 // chunks, and every thread accumulates four columns of its rows, the chunk
-// loop unrolled so that loads overlap.
-template <typename T, int D>
+// loop unrolled so that loads overlap. NT: threads of the workgroup.
+template <typename T, int D, int NT = 256>
 __device__ __forceinline__ void fsq_merge(const FwdArgs& a, int gi, lds_t* lds) {
-  constexpr int QM = kSqQMax, DV = D / 4, NB = kMergeNB, EPT = QM * DV / 256;
-  static_assert(QM * DV % 256 == 0, "row quads divide the workgroup");
+  constexpr int QM = kSqQMax, DV = D / 4, NB = kMergeNB, EPT = QM * DV / NT;
+  static_assert(QM * DV % NT == 0, "row quads divide the workgroup");
   __attribute__((address_space(3))) float* wl = (__attribute__((address_space(3))) float*)lds;  // [NB][QM]
   __attribute__((address_space(3))) float* mrow = wl + NB * QM;
   __attribute__((address_space(3))) float* srow = mrow + QM;
@@ -76,14 +76,14 @@ __device__ __forceinline__ void fsq_merge(const FwdArgs& a, int gi, lds_t* lds) 
   for (int j = 0; j < EPT; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
   for (int c0 = 0; c0 < n; c0 += NB) {
     const int nb = min(NB, n - c0);
-    for (int i = tid; i < nb * QM; i += 256) {
+    for (int i = tid; i < nb * QM; i += NT) {
       const int c = i / QM, q = i % QM;
       wl[c * QM + q] = q < Lq && srow[q] > 0.f ? __builtin_amdgcn_exp2f(lp[(c0 + c) * QM + q] - mrow[q]) / srow[q] : 0.f;
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-      const int e = tid + 256 * j, q = e / DV, d = (e % DV) * 4;
+      const int e = tid + NT * j, q = e / DV, d = (e % DV) * 4;
       if (q < Lq) {
         const float* src = a.op + ((size_t)(first + c0) * QM + q) * D + d;
 #pragma unroll 4
@@ -94,7 +94,7 @@ __device__ __forceinline__ void fsq_merge(const FwdArgs& a, int gi, lds_t* lds) 
   }
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
-    const int e = tid + 256 * j, q = e / DV, d = (e % DV) * 4;
+    const int e = tid + NT * j, q = e / DV, d = (e % DV) * 4;
     if (q < Lq) {
       T* dst = (T*)a.out + ((size_t)(q0 + q) * a.H + h) * D + d;
 #pragma unroll
