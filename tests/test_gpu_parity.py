@@ -530,12 +530,13 @@ _BWD_DQ_CASES = {
 
 
 @pytest.mark.parametrize("case", sorted(_BWD_DQ_CASES))
-@pytest.mark.parametrize("mode", [1, 2])
-def test_backward_dq_design_variants(mode, case):
-    """The backward-design study builds (dQ fused into the dK/dV pass: 1 with
-    fp32 atomic adds, 2 with per-key-tile partials summed in key-tile order)
-    match the oracle like the split passes."""
-    path = os.path.join(os.path.dirname(jfa.LIB_PATH), "_study", f"libjfa_bwddq{mode}.so")
+@pytest.mark.parametrize("variant", ["bwddq1", "bwddq2", "dkvpaired"])
+def test_backward_dq_design_variants(variant, case):
+    """The backward-design study builds (dQ fused into the dK/dV pass: bwddq1
+    with fp32 atomic adds, bwddq2 with per-key-tile partials summed in
+    key-tile order; dkvpaired: the paired dK/dV kernel for 128-byte rows too)
+    match the oracle like the library's passes."""
+    path = os.path.join(os.path.dirname(jfa.LIB_PATH), "_study", f"libjfa_{variant}.so")
     if not build.is_current(path):
         pytest.skip(STUDY_SKIP)
     batch = _BWD_DQ_CASES[case]()
@@ -543,7 +544,7 @@ def test_backward_dq_design_variants(mode, case):
     try:
         jfa._LIB = None
         jfa.LIB_PATH = path
-        _check(batch, label=f"backward dQ design {mode} {case}")
+        _check(batch, label=f"backward design {variant} {case}")
     finally:
         jfa._LIB = None
         jfa.LIB_PATH = saved

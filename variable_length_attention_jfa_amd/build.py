@@ -89,7 +89,8 @@ def build_studies(jobs: int = 8) -> None:
     choices, under _study/): -inf masking modes 1 and 2, the list-order and
     grid variants of the scheduling study, unswizzled LDS tiles, and the
     backward with dQ fused into the dK/dV pass (atomic adds, ordered
-    partials), and the forward's tile-shape variants. Their GPU tests skip
+    partials), the paired dK/dV kernel for 128-byte rows, and the forward's
+    tile-shape variants. Their GPU tests skip
     when they are not built."""
     from . import mask_study, sched_study, tile_study
     mask_study.build_variants(jobs)
@@ -100,6 +101,9 @@ def build_studies(jobs: int = 8) -> None:
     for mode in (1, 2):  # dQ fused into the dK/dV pass: atomic adds, ordered partials
         build(jobs=jobs, defines=[f"JFA_BWD_DQ={mode}"], out=os.path.join(PKG, "_study", f"libjfa_bwddq{mode}.so"),
               objdir=os.path.join(BUILD, f"bwddq{mode}"))
+    # the paired (two-role) dK/dV kernel for 128-byte rows as well
+    build(jobs=jobs, defines=["JFA_DKV_ONE_ROLE_ROWB=64"], out=os.path.join(PKG, "_study", "libjfa_dkvpaired.so"),
+          objdir=os.path.join(BUILD, "dkvpaired"))
 
 
 def main(argv=None) -> int:
