@@ -301,13 +301,16 @@ _TILE_CASES = {
     "d64_causal_bias_asym": lambda: gen.make_batch(
         gen.Workload("tile", 6, 2, 64, "bf16", True, True, gen.LengthDist("fixed", 1, 1), seed=92),
         q_lengths=[300, 70, 1, 0, 257, 640], kv_lengths=[300, 40, 1, 5, 700, 640]),
+    "edges_d64_causal": lambda: gen.make_batch(
+        gen.Workload("tile", 8, 2, 64, "bf16", True, False, gen.LengthDist("fixed", 1, 1), seed=94),
+        q_lengths=[31, 32, 33, 63, 64, 65, 255, 257], kv_lengths=[31, 32, 33, 63, 64, 65, 255, 257]),
     "edges_d128": lambda: gen.make_batch(
         gen.Workload("tile", 6, 2, 128, "bf16", False, False, gen.LengthDist("fixed", 1, 1), seed=93),
         q_lengths=[63, 64, 65, 255, 256, 257], kv_lengths=[63, 64, 65, 255, 256, 257]),
 }
 
 
-@pytest.mark.parametrize("variant", ["n128", "b3", "pf0", "wdma", "w32b3", "pp", "pp64"])
+@pytest.mark.parametrize("variant", ["n128", "n32", "r64", "b3", "pf0", "wdma", "w32b3", "pp", "pp64"])
 @pytest.mark.parametrize("case", sorted(_TILE_CASES))
 def test_tile_study_variants(variant, case):
     """Every variant of the forward's tile-shape study computes the forward

@@ -97,7 +97,8 @@ struct FwdTiles {
   static_assert((BN * CPR) % THREADS == 0, "tile pieces divide the workgroup");
   // the two-group shapes take this kernel only for the padded-dense baseline,
   // which plans with 128-row tiles
-  static_assert(FwdPingPong<T, D>::value || BM == FwdRows<T, D>::value, "tile shape published to the planner");
+  static_assert(FwdPingPong<T, D>::value || FwdRows64<T, D>::value || BM == FwdRows<T, D>::value,
+                "tile shape published to the planner");
 };
 
 // PADDED: the padded-dense baseline. Every sequence occupies a fixed-length
@@ -728,12 +729,293 @@ __global__ __launch_bounds__(512, 1) void jfa_fwd_pp_kernel(FwdArgs a) {
   }
 }
 
+// Study kernel: 64 query rows per wave, as two 32-row halves, for bf16 rows
+// of up to 128 bytes. Four waves, 256 rows per item; the K/V ring, the
+// per-row arithmetic and its order are those of jfa_fwd_kernel, but every K
+// and V fragment read from LDS feeds the MFMAs of both halves (half the LDS
+// reads per product), at the price of twice the accumulators per wave.
+template <int D, bool BIAS>
+__global__ __launch_bounds__(256, 2) void jfa_fwd_r64_kernel(FwdArgs a) {
+  using T = bf16;
+  using C = FwdTiles<T, D>;
+  static_assert(kFwdMaskMode == 0 && D <= 64, "study kernel: subtraction of pad terms, rows of up to 128 bytes");
+  constexpr int NH = 2, BM = 256, BN = C::BN, ES = 2;
+  static_assert(BM == FwdRows<T, D>::value, "tile shape published to the planner");
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ QueueCursor qcur;
+  lds_t* lds = (lds_t*)smem;
+  __attribute__((address_space(3))) float* bias_lds = (__attribute__((address_space(3))) float*)(lds + C::BIAS_OFF);
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.H;
+  const uint32_t gstride = (uint32_t)H * C::ROWB;
+  for_short_groups(a.gfirst, a.B * H, lds, [&](int gi) { fsq_merge<T, D>(a, gi, lds); });
+  load_queues(a.hdr, &qcur);
+  TicketState tk;
+
+  for (;;) {
+    const int it = next_item(a.hdr, &qcur, tk);
+    if (it < 0) break;
+    const int4 item = a.items[it];
+    const int b = item.x, h = item.y, qt = item.z;
+    const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
+    const int k0 = a.kv_off[b], Lk = a.kv_off[b + 1] - k0;
+    const int row0 = qt * BM;
+    const int n_kv = a.causal ? cdiv(min(min(row0 + BM, Lq), Lk), BN) : cdiv(Lk, BN);
+    const size_t qrow = ((size_t)q0 * H + h) * C::ROWB, krow = ((size_t)k0 * H + h) * C::ROWB;
+    const View qv = seq_view((const char*)a.q + qrow, Lq, gstride, C::ROWB);
+    const View kv = seq_view((const char*)a.k + krow, Lk, gstride, C::ROWB);
+    const View vv = seq_view((const char*)a.v + krow, Lk, gstride, C::ROWB);
+    if (BIAS) {
+      for (int i = tid; i < kBiasLen; i += C::THREADS) bias_lds[i] = a.bias[h * kBiasLen + i] * kLog2e;
+    }
+
+    const int wr0 = row0 + 64 * w;  // half hh holds rows wr0 + 32 hh .. + 31
+    Frag<T> qf[NH][D / 16];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        qf[hh][kk] = gfrag(qv, (uint32_t)(wr0 + 32 * hh + l32) * gstride + (16 * kk + 8 * g) * ES, (T*)0);
+
+    i32x4 kr[C::CPT], vr[C::CPT];
+    auto gload = [&](int j) {
+#pragma unroll
+      for (int c = 0; c < C::CPT; ++c) {
+        const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
+        const uint32_t off = (uint32_t)(j * BN + row) * gstride + col * 16;
+        kr[c] = ld16(kv, off);
+        vr[c] = ld16(vv, off);
+      }
+    };
+    auto swrite = [&](int s) {
+#pragma unroll
+      for (int c = 0; c < C::CPT; ++c) {
+        const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
+        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + row * C::KS + col * 16) = kr[c];
+        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + C::KTILE + row * C::VS + col * 16) = vr[c];
+      }
+    };
+    if (n_kv > 0) {
+      gload(0);
+      swrite(0);
+    }
+    wait_vmem();
+    __syncthreads();
+
+    f32x16 o[NH][D / 32];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[hh][db] = (f32x16){};
+    float m[NH], l[NH], lb[NH], l_pre[NH], lb_pre[NH];
+    int last_tile[NH];
+    bool last_masked[NH];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      m[hh] = kNegInit;
+      l[hh] = lb[hh] = l_pre[hh] = lb_pre[hh] = 0.f;
+      last_tile[hh] = -1;
+      last_masked[hh] = false;
+    }
+
+    for (int j = 0; j < n_kv; ++j) {
+      const int s = j & 1;
+      if (j + 1 < n_kv) gload(j + 1);
+      const int key0 = j * BN;
+      bool act[NH];
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) act[hh] = wr0 + 32 * hh < Lq && (!a.causal || key0 <= wr0 + 32 * hh + 31);
+      if (act[0] || act[1]) {
+        const lds_t* kt = lds + s * C::STAGE;
+        const lds_t* vt = kt + C::KTILE;
+        f32x16 sc[NH][BN / 32];
+        prio_mfma();
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh) sc[hh][kb] = (f32x16){};
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) {
+            const Frag<T> kf = prfrag<C::KS>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0);
+            mma(sc[0][kb], kf, qf[0][kk]);
+            if (act[1]) mma(sc[1][kb], kf, qf[1][kk]);
+          }
+        }
+        prio_valu();
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+          if (!act[hh]) continue;
+          const int hr0 = wr0 + 32 * hh, qi = hr0 + l32;
+          const bool masked = a.causal && (key0 + BN - 1 > hr0);
+          last_tile[hh] = j;
+          last_masked[hh] = masked;
+          float mx = -INFINITY;
+          const bool plain = !BIAS && !masked;
+          if (plain) {
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[hh][kb][i]);
+            mx = half_max(mx) * a.scale2;
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int kj = key0 + 32 * kb + res_row(i, g);
+                float x = sc[hh][kb][i] * a.scale2;
+                if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+                if (masked && (kj > qi || kj >= Lk)) x = -INFINITY;
+                sc[hh][kb][i] = x;
+                mx = fmaxf(mx, x);
+              }
+            }
+            mx = half_max(mx);
+          }
+          const bool grow = mx > m[hh] + kRescaleSlack;
+          if (__any(grow)) {
+            const float mn = grow ? mx : m[hh];
+            const float alpha = __builtin_amdgcn_exp2f(m[hh] - mn);
+            m[hh] = mn;
+            l[hh] *= alpha;
+            lb[hh] *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[hh][db] *= alpha;
+          }
+          if (j + 1 == n_kv) {
+            l_pre[hh] = l[hh];
+            lb_pre[hh] = lb[hh];
+          }
+          const float nm = -m[hh];
+#pragma unroll
+          for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float p = plain ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hh][kb][i], a.scale2, nm))
+                                    : __builtin_amdgcn_exp2f(sc[hh][kb][i] - m[hh]);
+              sc[hh][kb][i] = p;
+              l[hh] += p;
+            }
+          }
+        }
+        prio_mfma();
+#pragma unroll
+        for (int kc = 0; kc < BN / 16; ++kc) {
+          const Frag<T> p0 = rfrag(sc[0][kc >> 1], kc & 1, (T*)0);
+          const Frag<T> p1 = rfrag(sc[1][kc >> 1], kc & 1, (T*)0);
+          if (act[0]) lb[0] = frag_sum(p0, lb[0]);
+          if (act[1]) lb[1] = frag_sum(p1, lb[1]);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const Frag<T> vf = ptfrag<C::VS>(vt, 16 * kc, 32 * db, lane, (T*)0);
+            if (act[0]) mma(o[0][db], vf, p0);
+            if (act[1]) mma(o[1][db], vf, p1);
+          }
+        }
+        prio_valu();
+      }
+      if (j + 1 < n_kv) swrite((j + 1) & 1);
+      __syncthreads();
+    }
+
+    // epilogue per half, as in jfa_fwd_kernel (the cancellation guard reads
+    // K of block last_tile, still in LDS: a row's last unmasked block is the
+    // item's last block)
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      const int hr0 = wr0 + 32 * hh, qi = hr0 + l32;
+      const bool half_on = hr0 < Lq;
+      float lt = l[hh] + other_half(l[hh]);
+      float lbt = lb[hh] + other_half(lb[hh]);
+      if (half_on && last_tile[hh] >= 0 && !last_masked[hh]) {
+        const int pad1 = (last_tile[hh] + 1) * BN;
+        if (pad1 > Lk) {
+          float pads, pads_b;
+          if (!BIAS) {
+            const float pe = __builtin_amdgcn_exp2f(-m[hh]);
+            pads = (float)(pad1 - Lk) * pe;
+            pads_b = (float)(pad1 - Lk) * as_operand(pe, (T*)0);
+          } else {
+            float sub = 0.f, subb = 0.f;
+            for (int kj = Lk + g; kj < pad1; kj += 2) {
+              const float pe =
+                  __builtin_amdgcn_exp2f(bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius] - m[hh]);
+              sub += pe;
+              subb += as_operand(pe, (T*)0);
+            }
+            pads = sub + other_half(sub);
+            pads_b = subb + other_half(subb);
+          }
+          const float full = lt;
+          lt -= pads;
+          lbt -= pads_b;
+          const bool cancel = !(lt > full * 0x1p-12f);
+          if (__any(cancel)) {
+            const lds_t* kt = lds + (last_tile[hh] & 1) * C::STAGE;
+            const int key0 = last_tile[hh] * BN;
+            float sv = 0.f, svb = 0.f;
+#pragma unroll 1
+            for (int r = g; r < BN; r += 2) {
+              const int kj = key0 + r;
+              if (kj >= Lk) break;
+              float dot = 0.f;
+#pragma unroll 1
+              for (int c = 0; c < C::CPR; ++c) {
+                const i32x4 kq = *(const __attribute__((address_space(3))) i32x4*)(kt + r * C::KS + c * 16);
+                const i32x4 qq = ld16(qv, (uint32_t)qi * gstride + c * 16);
+                const bf16x8 k8 = __builtin_bit_cast(bf16x8, kq), q8 = __builtin_bit_cast(bf16x8, qq);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot += (float)k8[e] * (float)q8[e];
+              }
+              float x = dot * a.scale2;
+              if (BIAS) x += bias_lds[min(max(qi - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+              const float pe = __builtin_amdgcn_exp2f(x - m[hh]);
+              sv += pe;
+              svb += as_operand(pe, (T*)0);
+            }
+            const float fixed = l_pre[hh] + other_half(l_pre[hh]) + sv + other_half(sv);
+            const float fixedb = lb_pre[hh] + other_half(lb_pre[hh]) + svb + other_half(svb);
+            if (cancel) {
+              lt = fixed;
+              lbt = fixedb;
+            }
+          }
+        }
+      }
+      if (half_on) {
+        const float inv = lbt > 0.f ? 1.0f / lbt : 0.f;
+        const View ov = seq_view((char*)a.out + qrow, Lq, gstride, C::ROWB);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int d = 32 * db + 8 * r + 4 * g;
+            store4(ov, (uint32_t)qi * gstride + d * ES, o[hh][db][4 * r] * inv, o[hh][db][4 * r + 1] * inv,
+                   o[hh][db][4 * r + 2] * inv, o[hh][db][4 * r + 3] * inv, (T*)0);
+          }
+        }
+        if (g == 0) {
+          const float lse = lt > 0.f ? (m[hh] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+          const View lv = seq_view(a.lse + (size_t)q0 * H + h, Lq, (uint32_t)H * 4, 4);
+          st4f(lv, (uint32_t)qi * H * 4, lse);
+        }
+      }
+    }
+    if constexpr (!kSchedPersistent) break;
+  }
+}
+
 template <typename T, int D, bool PADDED = false>
 static hipError_t launch_fwd_t(const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
   constexpr bool PP = FwdPingPong<T, D>::value && !PADDED;
+  constexpr bool R64 = FwdRows64<T, D>::value && !PADDED;
   constexpr int threads = PP ? 512 : 256;
   void (*kern)(FwdArgs);
-  if constexpr (PP)
+  if constexpr (R64)
+    kern = bias ? jfa_fwd_r64_kernel<D, true> : jfa_fwd_r64_kernel<D, false>;
+  else if constexpr (PP)
     kern = bias ? jfa_fwd_pp_kernel<D, true> : jfa_fwd_pp_kernel<D, false>;
   else
     kern = bias ? jfa_fwd_kernel<T, D, true, PADDED> : jfa_fwd_kernel<T, D, false, PADDED>;
@@ -755,7 +1037,7 @@ int fwd_tile_keys(bool f32, int D) {
 }
 
 int fwd_tile_rows(bool f32, int D, bool padded) {
-  if (padded) return FwdTiles<bf16, 128>::BM;  // every D: the 4-wave kernel's 128 rows
+  if (padded) return FwdTiles<bf16, 128>::BM;  // every D: jfa_fwd_kernel's 128 rows
   if (f32) return D == 32 ? FwdRows<float, 32>::value : FwdRows<float, 64>::value;
   return D == 32 ? FwdRows<bf16, 32>::value : (D == 64 ? FwdRows<bf16, 64>::value : FwdRows<bf16, 128>::value);
 }

@@ -115,11 +115,21 @@ template <typename T, int D> struct FwdPingPong {
   static constexpr bool value = sizeof(T) == 2 && ((D == 128 && JFA_FWD_PINGPONG != 0) ||
                                                    (D == 64 && JFA_FWD_PINGPONG_NARROW != 0));
 };
+// 64 query rows per wave (two 32-row halves sharing each K and V fragment)
+// for bf16 D <= 64: another study choice (JFA_FWD_ROWS_PER_WAVE = 64).
+#ifndef JFA_FWD_ROWS_PER_WAVE
+#define JFA_FWD_ROWS_PER_WAVE 32
+#endif
+template <typename T, int D> struct FwdRows64 {
+  static constexpr bool value = JFA_FWD_ROWS_PER_WAVE == 64 && sizeof(T) == 2 && D <= 64;
+};
 template <typename T, int D> struct FwdWaves { static constexpr int value = FwdPingPong<T, D>::value ? 8 : 4; };
-template <typename T, int D> struct FwdRows { static constexpr int value = 32 * FwdWaves<T, D>::value; };
-// Keys per block of the forward, for rows of up to 128 bytes (JFA_FWD_BN)
-// and for wider ones (JFA_FWD_WIDE_BN): compile-time choices of the
-// tile-shape study (the library takes the defaults).
+template <typename T, int D> struct FwdRows {
+  static constexpr int value = (FwdRows64<T, D>::value ? 64 : 32) * FwdWaves<T, D>::value;
+};
+// Keys per block of the forward, for rows of 128 bytes (JFA_FWD_BN), for
+// wider ones (JFA_FWD_WIDE_BN) and 64 for narrower ones: compile-time
+// choices of the tile-shape study (the library takes the defaults).
 #ifndef JFA_FWD_BN
 #define JFA_FWD_BN 64
 #endif
@@ -127,7 +137,8 @@ template <typename T, int D> struct FwdRows { static constexpr int value = 32 * 
 #define JFA_FWD_WIDE_BN 64
 #endif
 template <typename T, int D> struct FwdKeys {
-  static constexpr int value = D * (int)sizeof(T) >= 256 ? JFA_FWD_WIDE_BN : JFA_FWD_BN;
+  static constexpr int value =
+      D * (int)sizeof(T) >= 256 ? JFA_FWD_WIDE_BN : (D * (int)sizeof(T) == 128 ? JFA_FWD_BN : 64);
 };
 // padded: the padded-dense baseline, which always takes the 4-wave kernel.
 int fwd_tile_rows(bool f32, int D, bool padded = false);

@@ -8,7 +8,10 @@ Variant "lib" is the library as built: 4 waves x 32 query rows per item,
 for rows of 256 bytes (bf16 D = 128) the LDS operands of two matrix products
 read ahead. The others are the same sources compiled with other choices:
 
-    n128     128-key blocks for rows of up to 128 bytes (bf16 D <= 64)
+    n128     128-key blocks for rows of 128 bytes (bf16 D = 64)
+    n32      32-key blocks for rows of 128 bytes: fewer registers, 4 waves per SIMD
+    r64      64 query rows per wave (two halves sharing every K and V fragment),
+             256 rows per item, for bf16 D <= 64
     b3       launch bound of 3 workgroups per CU for bf16 D = 64 rows
     pf0      D = 128 operand reads in the compiler's order (no read-ahead)
     wdma     D = 128 K/V ring filled by direct loads into LDS
@@ -37,7 +40,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 VARIANTS = {
     "lib": ("library: 4 waves, 64-key blocks, register-staged ring, D=128 read-ahead 2", ()),
-    "n128": ("128-key blocks (bf16 D <= 64)", ("JFA_FWD_BN=128",)),
+    "n128": ("128-key blocks (bf16 D = 64)", ("JFA_FWD_BN=128",)),
+    "n32": ("32-key blocks (bf16 D = 64): 127 VGPRs, 4 waves per SIMD", ("JFA_FWD_BN=32",)),
+    "r64": ("64 query rows per wave, 256 per item (bf16 D <= 64)", ("JFA_FWD_ROWS_PER_WAVE=64",)),
     "b3": ("3 workgroups per CU bound (bf16 D = 64)", ("JFA_FWD_BLOCKS=3",)),
     "pf0": ("D = 128 operand reads in compiler order", ("JFA_FWD_PREFETCH=0",)),
     "wdma": ("D = 128 ring by direct loads to LDS", ("JFA_FWD_WIDE_DMA=1",)),
