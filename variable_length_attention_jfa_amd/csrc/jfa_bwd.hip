@@ -38,6 +38,25 @@
 #include "jfa_dbias.h"
 #include "jfa_short.h"
 
+// Matrix products (bf16) whose LDS operands are read this many products
+// ahead of them; 0 leaves the compiler's order, which waits for each
+// product's reads right before it. Measured choices: two ahead in the dQ
+// kernel at D = 128 (dQ -6 to -7%) and in the one-role dK/dV kernel (-2%);
+// none in the paired dK/dV kernel (+6% with two) and the dQ kernel's rows of
+// up to 128 bytes (no change).
+#ifndef JFA_DQ_PREFETCH
+#define JFA_DQ_PREFETCH 2
+#endif
+#ifndef JFA_DKV_PREFETCH
+#define JFA_DKV_PREFETCH 0
+#endif
+#ifndef JFA_DQ_NARROW_PREFETCH
+#define JFA_DQ_NARROW_PREFETCH 0
+#endif
+#ifndef JFA_DKV1_PREFETCH
+#define JFA_DKV1_PREFETCH 2
+#endif
+
 namespace jfa {
 
 // P handed from score wave to gradient wave in bf16 (bf16 inputs) or fp32.
@@ -241,6 +260,7 @@ __device__ __forceinline__ void dkv_score_role(const BwdArgs& a, lds_t* lds, Que
         f32x16 sc = (f32x16){};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) mma(sc, lfrag<D>(qt, l32, 16 * kk + 8 * g, (T*)0), kf[kk]);
+        if constexpr (JFA_DKV_PREFETCH > 0 && sizeof(T) == 2) sched_prefetch<D / 16, 1, JFA_DKV_PREFETCH>();
         // P = exp2(S * scale * log2(e) - lse2 (+ bias)), zero above the diagonal
         // (the element test only on blocks that straddle it)
         auto softmax = [&](auto mask_c) {
@@ -276,6 +296,7 @@ __device__ __forceinline__ void dkv_score_role(const BwdArgs& a, lds_t* lds, Que
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) mma(dv[db], tfrag<D>(dot, 16 * c, 32 * db, lane, (T*)0), pf);
         }
+        if constexpr (JFA_DKV_PREFETCH > 0 && sizeof(T) == 2) sched_prefetch<2 * (D / 32), 2, JFA_DKV_PREFETCH>();
       }
       if (jb + 2 < it.nblk) dkv_swrite<T, D>(jb + 2, tid, stg, lds);
       __syncthreads();
@@ -346,6 +367,7 @@ __device__ __forceinline__ void dkv_grad_role(const BwdArgs& a, lds_t* lds, Queu
         }
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) mma(dp, lfrag<D>(dot, l32, 16 * kk + 8 * g, (T*)0), vf[kk]);
+        if constexpr (JFA_DKV_PREFETCH > 0 && sizeof(T) == 2) sched_prefetch<D / 16, 1, JFA_DKV_PREFETCH>();
         const lds_t* pb = lds + C::PBUF + ((jp & 1) * C::PAIRS + pair) * C::PBLK;
         f32x16 p;
         if constexpr (kPHalf<T>) {
@@ -380,6 +402,7 @@ __device__ __forceinline__ void dkv_grad_role(const BwdArgs& a, lds_t* lds, Queu
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) mma(dk[db], tfrag<D>(qt, 16 * c, 32 * db, lane, (T*)0), sf);
         }
+        if constexpr (JFA_DKV_PREFETCH > 0 && sizeof(T) == 2) sched_prefetch<2 * (D / 32), 2, JFA_DKV_PREFETCH>();
       }
       if (jb + 2 < it.nblk) dkv_swrite<T, D>(jb + 2, tid, stg, lds);
       __syncthreads();
@@ -592,6 +615,7 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
           mma(sc, lfrag<D>(qt, 32 * sb + l32, 16 * kk + 8 * g, (T*)0), kf[kk]);
           mma(dp, lfrag<D>(dot, 32 * sb + l32, 16 * kk + 8 * g, (T*)0), vf[kk]);
         }
+        if constexpr (JFA_DKV1_PREFETCH > 0 && sizeof(T) == 2) sched_prefetch<2 * (D / 16), 1, JFA_DKV1_PREFETCH>();
         prio_valu();
         // sc[i] = S[query 32sb + res_row(i,g)][key kj]; the element test for
         // the causal mask only on blocks that straddle the diagonal
@@ -637,6 +661,7 @@ __device__ __forceinline__ void dkv_one_role(const BwdArgs& a) {
             mma(dk[db], tfrag<D>(qt, 32 * sb + 16 * c, 32 * db, lane, (T*)0), sf);
           }
         }
+        if constexpr (JFA_DKV1_PREFETCH > 0 && sizeof(T) == 2) sched_prefetch<4 * (D / 32), 2, JFA_DKV1_PREFETCH>();
         prio_valu();
       }
       if constexpr (C::FUSED) {
@@ -845,6 +870,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
               mma(sc, prfrag<C::KS>(kt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), qf[kk]);
               mma(dp, prfrag<C::KS>(vt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), df[kk]);
             }
+            if constexpr (JFA_DQ_NARROW_PREFETCH > 0 && sizeof(T) == 2)
+              sched_prefetch<2 * (D / 16), 1, JFA_DQ_NARROW_PREFETCH>();
             // element tests only on blocks at the causal diagonal or the sequence end
             auto softmax = [&](auto edge_c) {
 #pragma unroll
@@ -866,6 +893,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
               for (int db = 0; db < D / 32; ++db)
                 mma(dq[db], ptfrag<C::KS>(kt, 32 * kb + 16 * c, 32 * db, lane, (T*)0), sf);
             }
+            if constexpr (JFA_DQ_NARROW_PREFETCH > 0 && sizeof(T) == 2)
+              sched_prefetch<2 * (D / 32), 2, JFA_DQ_NARROW_PREFETCH>();
           }
         } else {
           f32x16 sc[BN / 32], dp[BN / 32];
@@ -880,6 +909,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
               mma(dp[kb], lfrag<D>(vt, 32 * kb + l32, 16 * kk + 8 * g, (T*)0), df[kk]);
             }
           }
+          if constexpr (JFA_DQ_PREFETCH > 0 && D > 64 && sizeof(T) == 2)
+            sched_prefetch<2 * (BN / 32) * (D / 16), 1, JFA_DQ_PREFETCH>();
           // Element tests only on blocks at the causal diagonal or the sequence end
           // (at D = 128 a second copy of the loop costs more than the tests save).
           auto softmax = [&](auto edge_c) {
@@ -920,6 +951,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D >= 64 ? 1 : 2)) void jfa_
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) mma(dq[db], tfrag<D>(kt, 16 * kc, 32 * db, lane, (T*)0), sf);
           }
+          if constexpr (JFA_DQ_PREFETCH > 0 && D > 64 && sizeof(T) == 2)
+            sched_prefetch<(BN / 16) * (D / 32), 2, JFA_DQ_PREFETCH>();
         }
       }
       wait_vmem();
