@@ -145,6 +145,28 @@ def test_many_short_sequences():
     _check(gen.make_batch(wl), label="B=4096 short")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_largest_batch(causal):
+    """B at its maximum (JFA_MAX_BATCH = 8192) with empty and short
+    sequences: lists of 8192 groups per head, one item per sequence."""
+    wl = gen.Workload("maxb", 8192, 2, 64, "bf16", causal, False, gen.LengthDist("uniform", 0, 6), seed=12 + causal)
+    _check(gen.make_batch(wl), label=f"B=8192 causal={causal}")
+
+
+def test_many_heads():
+    """Hundreds of heads (B x H groups far above B) with ragged lengths and a bias table per head."""
+    wl = gen.Workload("manyh", 12, 384, 64, "bf16", True, True, gen.LengthDist("uniform", 1, 70), seed=14)
+    _check(gen.make_batch(wl), label="H=384")
+
+
+def test_long_sequence_d64_noncausal():
+    """One 8192-token sequence at D = 64 without a mask: 64 query tiles over
+    128 key blocks each, next to a 3-token one (gradients compared whole and
+    per (b, h))."""
+    wl = gen.Workload("long64", 2, 1, 64, "bf16", False, False, gen.LengthDist("fixed", 1, 1), seed=15)
+    _check(gen.make_batch(wl, q_lengths=[8192, 3], kv_lengths=[8192, 3]), label="L=8192 D=64")
+
+
 @pytest.mark.parametrize("cfg", [2, 3, 4])
 def test_deterministic_bitwise(cfg):
     batch = gen.make_batch(SMALL[cfg])
