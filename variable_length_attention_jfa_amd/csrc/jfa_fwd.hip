@@ -410,22 +410,24 @@ __global__ __launch_bounds__(256, (fwd_min_waves<T, D>())) void jfa_fwd_kernel(F
   }
 }
 
-// Two-group forward for bf16 rows of 256 bytes (D = 128). Eight waves and
-// 256 query rows per item: waves 0-3 (group 0) and 4-7 (group 1) own 32
-// rows each, so the two waves that share a SIMD sit in different groups.
-// The work of a key block is cut into a matrix phase (the PV product of the
-// block before, then QK^T of this block) and a vector phase (the online
-// softmax of this block), and the two groups run them half a block apart,
-// with a workgroup barrier between phases: while one group's waves issue
-// MFMAs the other's run the softmax. Without the barriers the two waves of a
-// SIMD fall into the same phase and take turns on one unit at a time. The
-// arithmetic per row is that of jfa_fwd_kernel, in the same order.
+// Study kernel (JFA_FWD_PINGPONG for bf16 D = 128, JFA_FWD_PINGPONG_NARROW
+// for D = 64): a two-group forward. Eight waves and 256 query rows per item:
+// waves 0-3 (group 0) and 4-7 (group 1) own 32 rows each, and the two waves
+// that share a SIMD sit in different groups. The work of a key block is cut
+// into a matrix phase (the PV product of the block before, then QK^T of this
+// block) and a vector phase (the online softmax of this block), and the two
+// groups run them half a block apart, with a workgroup barrier between
+// phases, so that while one group's waves issue MFMAs the other's run the
+// softmax. The arithmetic per row is that of jfa_fwd_kernel, in the same
+// order. Measured slower than jfa_fwd_kernel: in a vector phase one wave per
+// SIMD issues VALU alone, which reaches about two thirds of the port's rate,
+// and in a matrix phase one group's LDS operand reads all queue at once.
 //
 // Step s (s = 0 .. n_kv) works on K block s and V block s-1, one LDS stage:
 //   phase 2s  : group 0 matrix (PV s-1, QK^T s), group 1 vector (softmax s-1)
 //   phase 2s+1: group 0 vector (softmax s),      group 1 matrix (PV s-1, QK^T s)
-// Step s+1's tiles are loaded into registers at the start of step s and
-// written to the other stage at its end.
+// Step s+1's tiles are requested by direct loads into the other stage at the
+// start of step s and waited for at its end.
 template <int D, bool BIAS>
 __global__ __launch_bounds__(512, 1) void jfa_fwd_pp_kernel(FwdArgs a) {
   using T = bf16;
@@ -733,7 +735,8 @@ __global__ __launch_bounds__(512, 1) void jfa_fwd_pp_kernel(FwdArgs a) {
 // of up to 128 bytes. Four waves, 256 rows per item; the K/V ring, the
 // per-row arithmetic and its order are those of jfa_fwd_kernel, but every K
 // and V fragment read from LDS feeds the MFMAs of both halves (half the LDS
-// reads per product), at the price of twice the accumulators per wave.
+// reads per product), at the price of twice the accumulators per wave:
+// 228-256 VGPRs, two waves per SIMD, measured slower than jfa_fwd_kernel.
 template <int D, bool BIAS>
 __global__ __launch_bounds__(256, 2) void jfa_fwd_r64_kernel(FwdArgs a) {
   using T = bf16;
