@@ -67,15 +67,10 @@ def valid_pairs(q_lengths, kv_lengths, causal, which="all"):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources; HBM byte counts recorded for other sources are stale."""
-    import hashlib
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "variable_length_attention_jfa_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as fh:
-                h.update(name.encode() + b"\0" + fh.read())
-    return h.hexdigest()[:12]
+    """Hash of the kernel and header sources (the one the study builds are stamped
+    with); HBM byte counts recorded for other sources are stale."""
+    from variable_length_attention_jfa_amd import build
+    return build.source_hash()[:12]
 
 
 def recorded_traffic(kernel_label: str, workload: int):

@@ -323,6 +323,9 @@ _TILE_CASES = {
     "d64_causal_bias_asym": lambda: gen.make_batch(
         gen.Workload("tile", 6, 2, 64, "bf16", True, True, gen.LengthDist("fixed", 1, 1), seed=92),
         q_lengths=[300, 70, 1, 0, 257, 640], kv_lengths=[300, 40, 1, 5, 700, 640]),
+    "d32_causal_bias_asym": lambda: gen.make_batch(
+        gen.Workload("tile", 6, 2, 32, "bf16", True, True, gen.LengthDist("fixed", 1, 1), seed=95),
+        q_lengths=[300, 70, 1, 0, 257, 640], kv_lengths=[300, 40, 1, 5, 700, 640]),
     "edges_d64_causal": lambda: gen.make_batch(
         gen.Workload("tile", 8, 2, 64, "bf16", True, False, gen.LengthDist("fixed", 1, 1), seed=94),
         q_lengths=[31, 32, 33, 63, 64, 65, 255, 257], kv_lengths=[31, 32, 33, 63, 64, 65, 255, 257]),
@@ -332,7 +335,7 @@ _TILE_CASES = {
 }
 
 
-@pytest.mark.parametrize("variant", ["n128", "n32", "r64", "b3", "pf0", "wdma", "w32b3", "pp", "pp64"])
+@pytest.mark.parametrize("variant", ["n128", "n32", "r64", "b3", "pf0", "wdma", "w32b3", "pp", "pp64", "m16"])
 @pytest.mark.parametrize("case", sorted(_TILE_CASES))
 def test_tile_study_variants(variant, case):
     """Every variant of the forward's tile-shape study computes the forward

@@ -1010,13 +1010,382 @@ __global__ __launch_bounds__(256, 2) void jfa_fwd_r64_kernel(FwdArgs a) {
   }
 }
 
+// Study kernel (JFA_FWD_MFMA16, bf16 D <= 64): the forward with
+// v_mfma_f32_16x16x32_bf16 products in place of 32x32x16. The items (128
+// query rows), the 64-key blocks and the register-staged two-stage ring are
+// the library's; each wave holds its 32 query rows as two 16-column tiles,
+// and per block
+//   S^T = K Q^T     4 key tiles x 2 query tiles, D/32 products of 16 cycles
+//                   each (K rows read naturally from LDS, Q in VGPRs)
+//   softmax         lane l holds keys 4(l/16)..+3 of every key tile for query
+//                   column l%16: 16 scores per lane and query tile; the four
+//                   16-lane rows are combined with a permlane16 and a
+//                   permlane32 swap
+//   O^T += V^T P^T  D/16 x 2 tiles, two 32-key products each; the P^T operand
+//                   comes straight from the score registers (its 8 k-slots are
+//                   keys 4r..4r+3 of two consecutive key tiles), V^T from
+//                   transposing reads in the same key order, over V rows
+//                   padded to an odd multiple of 32 bytes (8 consecutive rows
+//                   x 32 bytes per cycle without bank conflicts)
+#ifndef JFA_FWD_MFMA16
+#define JFA_FWD_MFMA16 0
+#endif
+// its launch bound: 3 workgroups per CU (at most 168 VGPRs: three waves per SIMD)
+#ifndef JFA_FWD_MFMA16_BLOCKS
+#define JFA_FWD_MFMA16_BLOCKS 3
+#endif
+template <typename T, int D> struct FwdMfma16 {
+  static constexpr bool value = JFA_FWD_MFMA16 != 0 && sizeof(T) == 2 && D <= 64;
+};
+
+constexpr int pad_tr16(int rowb) { return (rowb / 32) % 2 == 1 ? rowb : rowb + 32; }
+
+template <int D>
+struct FwdTiles16 {
+  static constexpr int BM = 128, BN = 64, THREADS = 256, ROWB = D * 2;
+  static constexpr int KS = pad_nat(ROWB), VS = pad_tr16(ROWB);
+  static constexpr int KTILE = BN * KS, VTILE = BN * VS, STAGE = KTILE + VTILE;
+  static constexpr int CPR = ROWB / 16, CPT = BN * CPR / THREADS;
+  static constexpr int BIAS_OFF = 2 * STAGE;
+  static constexpr int LDS = BIAS_OFF + 1040;
+  static_assert((BN * CPR) % THREADS == 0, "tile pieces divide the workgroup");
+};
+
+__device__ __forceinline__ void mma16(f32x4& c, const bf16x8& a, const bf16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Combined over the four 16-lane rows of the wave (every lane gets the result).
+__device__ __forceinline__ float quarter_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return half_max(fmaxf(__int_as_float(r[0]), __int_as_float(r[1])));
+}
+__device__ __forceinline__ float quarter_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  const float y = __int_as_float(r[0]) + __int_as_float(r[1]);
+  return y + other_half(y);
+}
+// V^T operand of a 16x16x32 product: lane l holds column d = dbase + l%16 of
+// key rows kbase + 4(l/16) + 0..3 (k-slots 0..3) and kbase + 16 + 4(l/16) +
+// 0..3 (k-slots 4..7) of a padded-row tile: two transposing reads, each
+// 16-lane row of the wave reading a 4-row x 16-column block.
+template <int S>
+__device__ __forceinline__ bf16x8 ptfrag16(const lds_t* tile, int kbase, int dbase, int lane) {
+  const int row = kbase + 4 * (lane >> 4) + ((lane & 15) >> 2);
+  const int b = (dbase + (lane & 3) * 4) * 2;
+  s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + row * S + b));
+  s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + (row + 16) * S + b));
+  const bf16x4 x4 = __builtin_bit_cast(bf16x4, x), y4 = __builtin_bit_cast(bf16x4, y);
+  return (bf16x8){x4[0], x4[1], x4[2], x4[3], y4[0], y4[1], y4[2], y4[3]};
+}
+
+template <int D, bool BIAS>
+__global__ __launch_bounds__(256, JFA_FWD_MFMA16_BLOCKS) void jfa_fwd_m16_kernel(FwdArgs a) {
+  using T = bf16;
+  using C = FwdTiles16<D>;
+  constexpr int BM = C::BM, BN = C::BN, ES = 2;
+  static_assert(BM == FwdRows<T, D>::value, "tile shape published to the planner");
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ QueueCursor qcur;
+  lds_t* lds = (lds_t*)smem;
+  __attribute__((address_space(3))) float* bias_lds = (__attribute__((address_space(3))) float*)(lds + C::BIAS_OFF);
+
+  const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.H;
+  const uint32_t gstride = (uint32_t)H * C::ROWB;
+  static_assert(kShortLds <= C::LDS, "combining step fits the LDS");
+  for_short_groups(a.gfirst, a.B * H, lds, [&](int gi) { fsq_merge<T, D>(a, gi, lds); });
+  load_queues(a.hdr, &qcur);
+  TicketState tk;
+
+  for (;;) {
+    const int it = next_item(a.hdr, &qcur, tk);
+    if (it < 0) break;
+    const int4 item = a.items[it];
+    const int b = item.x, h = item.y, qt = item.z;
+    const int q0 = a.q_off[b], Lq = a.q_off[b + 1] - q0;
+    const int k0 = a.kv_off[b], Lk = a.kv_off[b + 1] - k0;
+    const int row0 = qt * BM;
+    const int n_kv = a.causal ? cdiv(min(min(row0 + BM, Lq), Lk), BN) : cdiv(Lk, BN);
+    const size_t qrow = ((size_t)q0 * H + h) * C::ROWB, krow = ((size_t)k0 * H + h) * C::ROWB;
+    const View qv = seq_view((const char*)a.q + qrow, Lq, gstride, C::ROWB);
+    const View kv = seq_view((const char*)a.k + krow, Lk, gstride, C::ROWB);
+    const View vv = seq_view((const char*)a.v + krow, Lk, gstride, C::ROWB);
+    if (BIAS) {
+      for (int i = tid; i < kBiasLen; i += C::THREADS) bias_lds[i] = a.bias[h * kBiasLen + i] * kLog2e;
+    }
+
+    const int wr0 = row0 + 32 * w;  // first query row of this wave
+    const bool wave_on = wr0 < Lq;
+    int qi[2];                      // this lane's query row in each 16-row tile
+    bf16x8 qf[2][D / 32];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      qi[t] = wr0 + 16 * t + l16;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk)
+        qf[t][kk] = gfrag(qv, (uint32_t)qi[t] * gstride + (32 * kk + 8 * g4) * ES, (T*)0).v;
+    }
+
+    i32x4 kr[C::CPT], vr[C::CPT];
+    auto gload = [&](int j) {
+#pragma unroll
+      for (int c = 0; c < C::CPT; ++c) {
+        const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
+        const uint32_t off = (uint32_t)(j * BN + row) * gstride + col * 16;
+        kr[c] = ld16(kv, off);
+        vr[c] = ld16(vv, off);
+      }
+    };
+    auto swrite = [&](int s) {
+#pragma unroll
+      for (int c = 0; c < C::CPT; ++c) {
+        const int x = tid + C::THREADS * c, row = x / C::CPR, col = x % C::CPR;
+        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + row * C::KS + col * 16) = kr[c];
+        *(__attribute__((address_space(3))) i32x4*)(lds + s * C::STAGE + C::KTILE + row * C::VS + col * 16) = vr[c];
+      }
+    };
+    if (n_kv > 0) {
+      gload(0);
+      swrite(0);
+    }
+    wait_vmem();
+    __syncthreads();
+
+    f32x4 o[D / 16][2];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) o[dt][t] = (f32x4){};
+    float m[2] = {kNegInit, kNegInit}, l[2] = {0.f, 0.f}, lb[2] = {0.f, 0.f};
+    float l_pre[2] = {0.f, 0.f}, lb_pre[2] = {0.f, 0.f};
+    int last_tile = -1;
+    bool last_masked = false;
+
+    for (int j = 0; j < n_kv; ++j) {
+      const int s = j & 1;
+      if (j + 1 < n_kv) gload(j + 1);
+      const int key0 = j * BN;
+      const bool active = wave_on && (!a.causal || key0 <= wr0 + 31);
+      if (active) {
+        const bool masked = (a.causal && (key0 + BN - 1 > wr0)) || kFwdMaskMode == 2 ||
+                            (kFwdMaskMode == 1 && key0 + BN > Lk);
+        const bool cmask = kFwdMaskMode == 0 || a.causal;
+        last_tile = j;
+        last_masked = masked;
+        const lds_t* kt = lds + s * C::STAGE;
+        const lds_t* vt = kt + C::KTILE;
+        f32x4 sc[BN / 16][2];
+        prio_mfma();
+#pragma unroll
+        for (int ktile = 0; ktile < BN / 16; ++ktile) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) sc[ktile][t] = (f32x4){};
+#pragma unroll
+          for (int kk = 0; kk < D / 32; ++kk) {
+            const bf16x8 kf = prfrag<C::KS>(kt, 16 * ktile + l16, 32 * kk + 8 * g4, (T*)0).v;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) mma16(sc[ktile][t], kf, qf[t][kk]);
+          }
+        }
+        prio_valu();
+        const bool plain = !BIAS && !masked;
+        float mx[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float x_max = -INFINITY;
+          if (plain) {
+#pragma unroll
+            for (int ktile = 0; ktile < BN / 16; ++ktile)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) x_max = fmaxf(x_max, sc[ktile][t][i]);
+            mx[t] = quarter_max(x_max) * a.scale2;
+          } else {
+#pragma unroll
+            for (int ktile = 0; ktile < BN / 16; ++ktile) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int kj = key0 + 16 * ktile + 4 * g4 + i;
+                float x = sc[ktile][t][i] * a.scale2;
+                if (BIAS) x += bias_lds[min(max(qi[t] - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+                if (masked && ((cmask && kj > qi[t]) || kj >= Lk)) x = -INFINITY;
+                sc[ktile][t][i] = x;
+                x_max = fmaxf(x_max, x);
+              }
+            }
+            mx[t] = quarter_max(x_max);
+          }
+        }
+        // running max with slack, as the library's kernel
+        const bool grow0 = mx[0] > m[0] + kRescaleSlack, grow1 = mx[1] > m[1] + kRescaleSlack;
+        if (__any(grow0 || grow1)) {
+          const bool grow[2] = {grow0, grow1};
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const float mn = grow[t] ? mx[t] : m[t];
+            const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);
+            m[t] = mn;
+            l[t] *= alpha;
+            lb[t] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) o[dt][t] *= alpha;
+          }
+        }
+        if (j + 1 == n_kv) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            l_pre[t] = l[t];
+            lb_pre[t] = lb[t];
+          }
+        }
+        if (plain) {  // raw dot products: the scale is folded into the exponent
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const float nm = -m[t];
+#pragma unroll
+            for (int ktile = 0; ktile < BN / 16; ++ktile) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ktile][t][i], a.scale2, nm));
+                sc[ktile][t][i] = p;
+                l[t] += p;
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int ktile = 0; ktile < BN / 16; ++ktile) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float p = __builtin_amdgcn_exp2f(sc[ktile][t][i] - m[t]);
+                sc[ktile][t][i] = p;
+                l[t] += p;
+              }
+            }
+          }
+        }
+        prio_mfma();
+#pragma unroll
+        for (int ks = 0; ks < BN / 32; ++ks) {
+          bf16x8 pf[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pf[t][e] = (bf16)sc[2 * ks][t][e];
+              pf[t][4 + e] = (bf16)sc[2 * ks + 1][t][e];
+            }
+            Frag<T> f;
+            f.v = pf[t];
+            lb[t] = frag_sum(f, lb[t]);
+          }
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) {
+            const bf16x8 vf = ptfrag16<C::VS>(vt, 32 * ks, 16 * dt, lane);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) mma16(o[dt][t], vf, pf[t]);
+          }
+        }
+        prio_valu();
+      }
+      if (j + 1 < n_kv) swrite((j + 1) & 1);
+      __syncthreads();
+    }
+
+    // Epilogue, per query tile: the four rows' partial sums combined, the pad
+    // terms removed (cancellation guard as in the library's kernel), O and lse
+    // stored.
+    const View ov = seq_view((char*)a.out + qrow, Lq, gstride, C::ROWB);
+    const View lv = seq_view(a.lse + (size_t)q0 * H + h, Lq, (uint32_t)H * 4, 4);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float lt = quarter_sum(l[t]);
+      float lbt = quarter_sum(lb[t]);
+      if (wave_on && last_tile >= 0 && !last_masked) {
+        const int pad1 = (last_tile + 1) * BN;
+        if (pad1 > Lk) {
+          float pads, pads_b;
+          if (!BIAS) {
+            const float pe = __builtin_amdgcn_exp2f(-m[t]);
+            pads = (float)(pad1 - Lk) * pe;
+            pads_b = (float)(pad1 - Lk) * as_operand(pe, (T*)0);
+          } else {
+            float sub = 0.f, subb = 0.f;
+            for (int kj = Lk + g4; kj < pad1; kj += 4) {
+              const float pe =
+                  __builtin_amdgcn_exp2f(bias_lds[min(max(qi[t] - kj, -kBiasRadius), kBiasRadius) + kBiasRadius] - m[t]);
+              sub += pe;
+              subb += as_operand(pe, (T*)0);
+            }
+            pads = quarter_sum(sub);
+            pads_b = quarter_sum(subb);
+          }
+          const float full = lt;
+          lt -= pads;
+          lbt -= pads_b;
+          const bool cancel = !(lt > full * 0x1p-12f);
+          if (__any(cancel)) {
+            const lds_t* kt = lds + (last_tile & 1) * C::STAGE;
+            const int key0 = last_tile * BN;
+            float sv = 0.f, svb = 0.f;
+#pragma unroll 1
+            for (int r = g4; r < BN; r += 4) {
+              const int kj = key0 + r;
+              if (kj >= Lk) break;
+              float dot = 0.f;
+#pragma unroll 1
+              for (int c = 0; c < C::CPR; ++c) {
+                const i32x4 kq = *(const __attribute__((address_space(3))) i32x4*)(kt + r * C::KS + c * 16);
+                const i32x4 qq = ld16(qv, (uint32_t)qi[t] * gstride + c * 16);
+                const bf16x8 k8 = __builtin_bit_cast(bf16x8, kq), q8 = __builtin_bit_cast(bf16x8, qq);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot += (float)k8[e] * (float)q8[e];
+              }
+              float x = dot * a.scale2;
+              if (BIAS) x += bias_lds[min(max(qi[t] - kj, -kBiasRadius), kBiasRadius) + kBiasRadius];
+              const float pe = __builtin_amdgcn_exp2f(x - m[t]);
+              sv += pe;
+              svb += as_operand(pe, (T*)0);
+            }
+            const float fixed = quarter_sum(l_pre[t]) + quarter_sum(sv);
+            const float fixedb = quarter_sum(lb_pre[t]) + quarter_sum(svb);
+            if (cancel) {
+              lt = fixed;
+              lbt = fixedb;
+            }
+          }
+        }
+      }
+      if (wave_on) {
+        const float inv = lbt > 0.f ? 1.0f / lbt : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const int d = 16 * dt + 4 * g4;
+          store4(ov, (uint32_t)qi[t] * gstride + d * ES, o[dt][t][0] * inv, o[dt][t][1] * inv, o[dt][t][2] * inv,
+                 o[dt][t][3] * inv, (T*)0);
+        }
+        if (g4 == 0) {
+          const float lse = lt > 0.f ? (m[t] + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+          st4f(lv, (uint32_t)qi[t] * H * 4, lse);
+        }
+      }
+    }
+    if constexpr (!kSchedPersistent) break;
+  }
+}
+
 template <typename T, int D, bool PADDED = false>
 static hipError_t launch_fwd_t(const FwdArgs& a, bool bias, long max_items, int num_cus, hipStream_t st) {
   constexpr bool PP = FwdPingPong<T, D>::value && !PADDED;
   constexpr bool R64 = FwdRows64<T, D>::value && !PADDED;
+  constexpr bool M16 = FwdMfma16<T, D>::value && !PADDED;
   constexpr int threads = PP ? 512 : 256;
   void (*kern)(FwdArgs);
-  if constexpr (R64)
+  if constexpr (M16)
+    kern = bias ? jfa_fwd_m16_kernel<D, true> : jfa_fwd_m16_kernel<D, false>;
+  else if constexpr (R64)
     kern = bias ? jfa_fwd_r64_kernel<D, true> : jfa_fwd_r64_kernel<D, false>;
   else if constexpr (PP)
     kern = bias ? jfa_fwd_pp_kernel<D, true> : jfa_fwd_pp_kernel<D, false>;

@@ -20,6 +20,8 @@ read ahead. The others are the same sources compiled with other choices:
     pp       D = 128 two-group kernel: 8 waves, 256 rows per item, the two
              waves of each SIMD in opposite matrix / softmax phases
     pp64     the two-group kernel for D = 64 as well
+    m16      bf16 D <= 64 with 16x16x32 matrix products (two 16-row query
+             tiles per wave) in place of 32x32x16
 
     python -m variable_length_attention_jfa_amd.tile_study --build
     python -m variable_length_attention_jfa_amd.tile_study --variant V --workload W
@@ -50,6 +52,7 @@ VARIANTS = {
               ("JFA_FWD_WIDE_BN=32", "JFA_FWD_WIDE_DMA=1", "JFA_FWD_WIDE_BLOCKS=3")),
     "pp": ("D = 128 two-group kernel (8 waves, 256 rows)", ("JFA_FWD_PINGPONG=1",)),
     "pp64": ("two-group kernel for D = 64 and 128", ("JFA_FWD_PINGPONG=1", "JFA_FWD_PINGPONG_NARROW=1")),
+    "m16": ("16x16x32 matrix products (bf16 D <= 64)", ("JFA_FWD_MFMA16=1",)),
 }
 
 
