@@ -92,24 +92,29 @@ __device__ __forceinline__ int snake(int g, int nq) {
   return r < nq ? r : 2 * nq - 1 - r;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active):
+// DPP shifts by 1, 2, 4 and 8 lanes inside each 16-lane row, then the sum at
+// the end of row 0 carried into row 1, of row 2 into row 3, and of rows 0-1
+// (lane 31) into rows 2 and 3. Lanes a shift leaves without a source add 0.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return x;
+}
+
 // Exclusive scan over the workgroup; returns the prefix, *total gets the sum.
+// Called by every thread of the workgroup.
 __device__ int block_exclusive_scan(int v, int* total, int* wsum) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  const int x = wave_inclusive_scan(v);
   if (lane == 63) wsum[w] = x;
   __syncthreads();
-  if (threadIdx.x < 64) {
-    int s = threadIdx.x < kPlanWaves ? wsum[threadIdx.x] : 0;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(s, d);
-      if (lane >= d) s += y;
-    }
+  if (threadIdx.x < 64) {  // wave 0, whole: the waves' totals
+    const int s = wave_inclusive_scan(threadIdx.x < kPlanWaves ? wsum[threadIdx.x] : 0);
     if (threadIdx.x < kPlanWaves) wsum[kPlanWaves + threadIdx.x] = s;  // inclusive wave prefix
   }
   __syncthreads();
@@ -180,6 +185,7 @@ __device__ __forceinline__ void plan_pass(const PlanArgs& a, int pi, char* dyn) 
     const unsigned long long mine = tid < P ? key[tid] : 0ull;
     int rank = 0;
     if (tid < P)
+#pragma unroll 8
       for (int i = 0; i < P; ++i) rank += key[i] < mine;
     __syncthreads();
     if (tid < P) key[rank] = mine;
